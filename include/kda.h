@@ -1,0 +1,144 @@
+/*
+ * kda.h -- C ABI of libkda.so, the MI355X (gfx950) Kimi Delta Attention mixer core.
+ *
+ * The operation (nnterp Kimi-Linear encyclopedia page, Notes, section on KDA decaying
+ * each key channel, and the family-module docstring of section 04): per head, a state
+ * S of [key_dim, value_dim] is carried across tokens.  Each token
+ *     1. L2-normalises its key and query (the kernel applies the norm) and scales the
+ *        query by 1/sqrt(key_dim),
+ *     2. decays every key channel i of S by exp(g[i])   (g: natural-log decay, <= 0),
+ *     3. applies the delta rule  S += beta * k (v - S^T k)^T,
+ *     4. reads  o = S^T q  from the updated state.
+ * The kernels take (query, key, value, g=, beta=, initial_state=) and return the head
+ * outputs and the last state; initial_state is absent at the start of a prompt
+ * (same page, section 02, state_input / state_output rows).  The head outputs then
+ * pass a sigmoid-gated RMSNorm with one [head_dim] weight (Kimi-K3 atlas,
+ * gate-project page: o_norm code and Parameters table).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major buffers owned by
+ *    the caller; the library never allocates, frees or retains device memory and keeps
+ *    no state between calls (calls are thread-safe).  Pointers to tensors with a
+ *    feature axis (q, k, v, g, states, o, gate, y, weights) must be 16-byte aligned;
+ *    beta and cu_seqlens need 4-byte alignment, mask none.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default
+ *    stream).  Arguments are validated on the host before anything is launched; a
+ *    non-OK status means nothing was enqueued and no output was touched.  Faults
+ *    inside a kernel surface at the caller's next synchronisation.
+ *  - dtype codes: KDA_F32 = IEEE fp32, KDA_BF16 = bfloat16 (outputs rounded to
+ *    nearest-even).  The recurrent state is always fp32.
+ *  - Precondition (not checked, documented): every g lies in [-5, 0], the decay lower
+ *    bound of the Kimi-K3 configuration (Kimi-K3 atlas, config.json,
+ *    linear_attn_config.gate_lower_bound).  The bf16 chunked kernel factors
+ *    within-chunk decays with 16-token reference points and stays finite for
+ *    g >= -5.4; the other kernels accept any g <= 0.
+ *  - Padded tokens (mask == 0), and tokens of a packed batch, must hold finite values.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,         /* a required pointer is NULL                                   */
+  KDA_ERR_SHAPE = 2,        /* a size is out of range or inconsistent                       */
+  KDA_ERR_DTYPE = 3,        /* unknown dtype code                                           */
+  KDA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned                             */
+  KDA_ERR_CONFLICT = 5,     /* mutually exclusive arguments given together                  */
+  KDA_ERR_UNSUPPORTED = 6,  /* a valid combination this build has no kernel for             */
+  KDA_ERR_HIP = 7           /* the HIP runtime reported an error at launch                  */
+} kda_status_t;
+
+/* Problem description shared by the prefill and recurrent entry points. */
+typedef struct {
+  int32_t B;             /* batch rows; 1 when cu_seqlens packs the sequences              */
+  int32_t T;             /* tokens per row (packed total with cu_seqlens)                  */
+  int32_t H;             /* heads                                                          */
+  int32_t dk;            /* key_dim   (16, 32, 64 or 128)                                  */
+  int32_t dv;            /* value_dim (== dk in this build)                                */
+  int32_t num_seqs;      /* sequences: len(cu_seqlens)-1 with cu_seqlens, else ignored (=B) */
+  int32_t chunk;         /* prefill chunk length: 0 = default; 64 (bf16 MFMA path) or 16   */
+  float scale;           /* query scale; 0 = 1/sqrt(dk)                                    */
+  int32_t use_qk_l2norm; /* 1: q, k are L2-normalised in the kernel (x / sqrt(sum x^2 + 1e-6)) */
+  int32_t in_dtype;      /* kda_dtype_t of q, k, v and gate                                */
+  int32_t out_dtype;     /* kda_dtype_t of o and y                                         */
+  float norm_eps;        /* gated-RMSNorm epsilon                                          */
+} kda_params_t;
+
+/*
+ * kda_chunk_prefill -- the prompt kernel: runs the recurrence over whole sequences,
+ * carrying the state from one chunk of tokens to the next without storing it per token
+ * (nnterp Kimi-Linear page, Notes, "Loading": 64-token chunks).  Results equal the
+ * token-by-token recurrence up to rounding.
+ *
+ *   q, k          [B, T, H, dk]   in_dtype
+ *   v             [B, T, H, dv]   in_dtype
+ *   g             [B, T, H, dk]   fp32 log decays (<= 0)
+ *   beta          [B, T, H]       fp32 write strengths in (0, 1), already sigmoided
+ *   initial_state [N, H, dk, dv]  fp32, or NULL for a zero state (start of a prompt)
+ *   cu_seqlens    [N + 1]         int32 device array of packed sequence offsets
+ *                                 (cu_seqlens[0] = 0, non-decreasing, last <= T), or NULL;
+ *                                 requires B == 1 and p->num_seqs = N
+ *   mask          [B, T]          uint8, 1 = token, 0 = padding (skipped: state unchanged,
+ *                                 output 0), or NULL; not together with cu_seqlens
+ *   o             [B, T, H, dv]   out_dtype head outputs (before the gated norm)
+ *   final_state   [N, H, dk, dv]  fp32; may be the same buffer as initial_state
+ *   gate          [B, T, H, dv]   in_dtype, norm_weight [dv] fp32, y [B, T, H, dv]
+ *                                 out_dtype: the gated norm y = w * o / rms(o) *
+ *                                 sigmoid(gate) per head; all three set or all NULL
+ * N = B without cu_seqlens.  Tokens of a packed batch outside [0, cu_seqlens[N]) are
+ * not written.
+ */
+kda_status_t kda_chunk_prefill(const kda_params_t *p,
+                               const void *q, const void *k, const void *v,
+                               const float *g, const float *beta,
+                               const float *initial_state,
+                               const int32_t *cu_seqlens, const uint8_t *mask,
+                               void *o, float *final_state,
+                               const void *gate, const float *norm_weight, void *y,
+                               void *stream);
+
+/*
+ * kda_recurrent_step -- the decode kernel: the token-by-token form, for one new token
+ * per row (T = 1) or a few tokens (T >= 1, applied in order).  The state is read and
+ * written in place: state [B, H, dk, dv] fp32 holds S before the call and S after the
+ * last token on return.  Other arguments as for kda_chunk_prefill (no cu_seqlens).
+ */
+kda_status_t kda_recurrent_step(const kda_params_t *p,
+                                const void *q, const void *k, const void *v,
+                                const float *g, const float *beta,
+                                float *state, const uint8_t *mask,
+                                void *o,
+                                const void *gate, const float *norm_weight, void *y,
+                                void *stream);
+
+/*
+ * kda_gated_rmsnorm -- y = w * x / sqrt(mean(x^2) + eps) * sigmoid(gate) over each row
+ * of `width` features (one head).  x and gate: [rows, width] in in_dtype; weight:
+ * [width] fp32 shared by every row; y: [rows, width] out_dtype.  width must be a power
+ * of two in [8, 512].  y may alias x.
+ */
+kda_status_t kda_gated_rmsnorm(const void *x, const void *gate, const float *weight, void *y,
+                               int64_t rows, int32_t width, float eps,
+                               int32_t in_dtype, int32_t out_dtype, void *stream);
+
+/* Text of a status code (static storage). */
+const char *kda_status_string(kda_status_t s);
+/* Detail of the last non-OK status returned on this thread (thread-local storage). */
+const char *kda_last_error(void);
+/* Library version string, e.g. "kda-mi355x 0.1.0 gfx950". */
+const char *kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

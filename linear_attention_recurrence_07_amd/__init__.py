@@ -1,0 +1,286 @@
+"""Kimi Delta Attention (KDA) mixer core for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over libkda.so (see include/kda.h).  It only marshals arguments:
+torch tensors supply device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  If libkda.so is missing, importing
+works but every call raises; there is no CPU fallback.
+
+    o, final_state = chunk_prefill(q, k, v, g, beta, initial_state=None)
+    o, final_state, y = chunk_prefill(..., gate=gate, norm_weight=w)      # fused gated norm
+    o = recurrent_step(q, k, v, g, beta, state)                            # state updated in place
+    y = gated_rmsnorm(x, gate, w)
+
+The call mirrors the kernels on the nnterp Kimi-Linear page (section 04): queries,
+keys, values [B, T, H, d], g= per-key-channel log decays [B, T, H, dk] (fp32, <= 0),
+beta= write strengths [B, T, H], initial_state= [N, H, dk, dv] or None; it returns the
+head outputs and the last state.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["chunk_prefill", "recurrent_step", "gated_rmsnorm", "library_path", "load_library",
+           "KdaError", "version"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_ALIGN",
+           5: "KDA_ERR_CONFLICT", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_HIP"}
+
+
+class KdaError(RuntimeError):
+    """A non-OK status from libkda.so."""
+
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class KdaParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("use_qk_l2norm", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("norm_eps", ctypes.c_float)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libkda.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it first "
+                           "(python -c 'import __graft_entry__ as e; e.build()')")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.kda_chunk_prefill.restype = ctypes.c_int
+    lib.kda_chunk_prefill.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 14
+    lib.kda_recurrent_step.restype = ctypes.c_int
+    lib.kda_recurrent_step.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 12
+    lib.kda_gated_rmsnorm.restype = ctypes.c_int
+    lib.kda_gated_rmsnorm.argtypes = [P, P, P, P, i64, i32, f32, i32, i32, P]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load_library().kda_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise KdaError(status, load_library().kda_last_error().decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return KDA_BF16
+    if t == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t}: use bfloat16 or float32")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, device) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _params(B, T, H, dk, dv, *, num_seqs=0, chunk=0, scale=None, use_qk_l2norm=True,
+            in_dtype=KDA_BF16, out_dtype=KDA_BF16, norm_eps=1e-6) -> KdaParams:
+    return KdaParams(B, T, H, dk, dv, num_seqs, chunk, 0.0 if scale is None else float(scale),
+                     1 if use_qk_l2norm else 0, in_dtype, out_dtype, float(norm_eps))
+
+
+def _check_cu_seqlens(cu: torch.Tensor, T: int) -> None:
+    c = cu.tolist()
+    if len(c) < 2 or c[0] != 0 or c[-1] > T or any(b < a for a, b in zip(c, c[1:])):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at or before T")
+
+
+def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None, *,
+                  cu_seqlens: Optional[torch.Tensor] = None,
+                  attention_mask: Optional[torch.Tensor] = None,
+                  gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+                  norm_eps: float = 1e-6, scale: Optional[float] = None,
+                  use_qk_l2norm_in_kernel: bool = True, chunk: int = 0,
+                  output_dtype: Optional[torch.dtype] = None,
+                  out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                  y: Optional[torch.Tensor] = None):
+    """Chunked prefill.  Returns (o, final_state), or (o, final_state, y) with the fused
+    sigmoid-gated RMSNorm when gate and norm_weight are given.
+
+    cu_seqlens ([N+1] int32; a CPU tensor is validated then copied to the GPU) packs N
+    sequences into B = 1; attention_mask ([B, T], nonzero = token) marks padding.
+    """
+    lib = load_library()
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    in_dt = q.dtype
+    out_dt = output_dtype or in_dt
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, dev)
+        if t.dtype != in_dt:
+            raise TypeError(f"{name} dtype {t.dtype} differs from q's {in_dt}")
+    if k.shape != q.shape or v.shape[:3] != (B, T, H):
+        raise ValueError("q, k must be [B,T,H,dk] and v [B,T,H,dv]")
+    _dev(g, "g", dev)
+    _dev(beta, "beta", dev)
+    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("g and beta must be float32")
+    if g.shape != (B, T, H, dk) or beta.shape != (B, T, H):
+        raise ValueError("g must be [B,T,H,dk] and beta [B,T,H]")
+    cu_dev = None
+    if cu_seqlens is not None:
+        if cu_seqlens.device.type == "cpu":
+            _check_cu_seqlens(cu_seqlens, T)
+            cu_dev = cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
+        else:
+            cu_dev = _dev(cu_seqlens, "cu_seqlens", dev)
+            if cu_dev.dtype != torch.int32:
+                raise TypeError("cu_seqlens must be int32")
+        N = cu_dev.numel() - 1
+    else:
+        N = B
+    mask_dev = None
+    if attention_mask is not None:
+        if attention_mask.shape != (B, T):
+            raise ValueError("attention_mask must be [B, T]")
+        mask_dev = (attention_mask != 0).to(device=dev, dtype=torch.uint8).contiguous()
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", dev)
+        if initial_state.dtype != torch.float32 or initial_state.shape != (N, H, dk, dv):
+            raise ValueError(f"initial_state must be float32 [{N},{H},{dk},{dv}]")
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
+    _dev(o, "out", dev)
+    fs = final_state if final_state is not None else torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _dev(fs, "final_state", dev)
+    norm = gate is not None or norm_weight is not None
+    if norm:
+        if gate is None or norm_weight is None:
+            raise ValueError("the gated norm needs both gate and norm_weight")
+        _dev(gate, "gate", dev)
+        _dev(norm_weight, "norm_weight", dev)
+        if gate.dtype != in_dt or gate.shape != (B, T, H, dv):
+            raise ValueError("gate must match v's shape and q's dtype")
+        if norm_weight.dtype != torch.float32 or norm_weight.shape != (dv,):
+            raise ValueError("norm_weight must be float32 [dv]")
+        y = y if y is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
+        _dev(y, "y", dev)
+    else:
+        y = None
+    p = _params(B, T, H, dk, dv, num_seqs=N if cu_dev is not None else 0, chunk=chunk, scale=scale,
+                use_qk_l2norm=use_qk_l2norm_in_kernel, in_dtype=_dtype_code(in_dt),
+                out_dtype=_dtype_code(out_dt), norm_eps=norm_eps)
+    _check(lib.kda_chunk_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(initial_state), _ptr(cu_dev), _ptr(mask_dev), _ptr(o), _ptr(fs),
+                                 _ptr(gate), _ptr(norm_weight), _ptr(y), _stream(dev)))
+    return (o, fs) if y is None else (o, fs, y)
+
+
+def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                   beta: torch.Tensor, state: torch.Tensor, *,
+                   attention_mask: Optional[torch.Tensor] = None,
+                   gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+                   norm_eps: float = 1e-6, scale: Optional[float] = None,
+                   use_qk_l2norm_in_kernel: bool = True, output_dtype: Optional[torch.dtype] = None,
+                   out: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None):
+    """Token-by-token step(s): advances `state` ([B,H,dk,dv] fp32) in place over the T
+    tokens of q/k/v and returns o (and y with the gated norm)."""
+    lib = load_library()
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    in_dt = q.dtype
+    out_dt = output_dtype or in_dt
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, dev)
+        if t.dtype != in_dt:
+            raise TypeError(f"{name} dtype {t.dtype} differs from q's {in_dt}")
+    if k.shape != q.shape or v.shape[:3] != (B, T, H):
+        raise ValueError("q, k must be [B,T,H,dk] and v [B,T,H,dv]")
+    _dev(g, "g", dev)
+    _dev(beta, "beta", dev)
+    if g.dtype != torch.float32 or beta.dtype != torch.float32 or g.shape != (B, T, H, dk) or beta.shape != (B, T, H):
+        raise ValueError("g must be float32 [B,T,H,dk] and beta float32 [B,T,H]")
+    _dev(state, "state", dev)
+    if state.dtype != torch.float32 or state.shape != (B, H, dk, dv):
+        raise ValueError("state must be float32 [B,H,dk,dv]")
+    mask_dev = None
+    if attention_mask is not None:
+        if attention_mask.shape != (B, T):
+            raise ValueError("attention_mask must be [B, T]")
+        mask_dev = (attention_mask != 0).to(device=dev, dtype=torch.uint8).contiguous()
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
+    _dev(o, "out", dev)
+    norm = gate is not None or norm_weight is not None
+    if norm:
+        if gate is None or norm_weight is None:
+            raise ValueError("the gated norm needs both gate and norm_weight")
+        _dev(gate, "gate", dev)
+        _dev(norm_weight, "norm_weight", dev)
+        if gate.dtype != in_dt or gate.shape != (B, T, H, dv) or norm_weight.dtype != torch.float32:
+            raise ValueError("gate must match v (q's dtype); norm_weight float32 [dv]")
+        y = y if y is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
+        _dev(y, "y", dev)
+    else:
+        y = None
+    p = _params(B, T, H, dk, dv, scale=scale, use_qk_l2norm=use_qk_l2norm_in_kernel,
+                in_dtype=_dtype_code(in_dt), out_dtype=_dtype_code(out_dt), norm_eps=norm_eps)
+    _check(lib.kda_recurrent_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(state), _ptr(mask_dev), _ptr(o), _ptr(gate), _ptr(norm_weight),
+                                  _ptr(y), _stream(dev)))
+    return o if y is None else (o, y)
+
+
+def gated_rmsnorm(x: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *,
+                  output_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None):
+    """y = weight * x / sqrt(mean(x^2) + eps) * sigmoid(gate) over the last axis."""
+    lib = load_library()
+    dev = x.device
+    _dev(x, "x", dev)
+    _dev(gate, "gate", dev)
+    _dev(weight, "weight", dev)
+    if gate.shape != x.shape or gate.dtype != x.dtype:
+        raise ValueError("gate must match x in shape and dtype")
+    width = x.shape[-1]
+    if weight.dtype != torch.float32 or weight.shape != (width,):
+        raise ValueError("weight must be float32 [width]")
+    y = out if out is not None else torch.empty(x.shape, dtype=output_dtype or x.dtype, device=dev)
+    _dev(y, "out", dev)
+    rows = x.numel() // width if width else 0
+    _check(lib.kda_gated_rmsnorm(_ptr(x), _ptr(gate), _ptr(weight), _ptr(y), rows, width, float(eps),
+                                 _dtype_code(x.dtype), _dtype_code(y.dtype), _stream(dev)))
+    return y

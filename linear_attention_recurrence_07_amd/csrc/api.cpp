@@ -1,0 +1,217 @@
+// C ABI of libkda.so: host-side validation and dispatch to the HIP kernels.
+// Every check runs before anything is enqueued, so a non-OK status leaves all outputs
+// untouched.  See include/kda.h for the contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kda_status_t fail(kda_status_t s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+// Tensors with a feature axis are read and written in 16-byte vectors; per-token
+// scalars (beta, mask, cu_seqlens) only need their element alignment.
+kda_status_t check_ptr(const void *p, const char *name, bool required, unsigned align = 16) {
+  if (p == nullptr) {
+    if (required) return fail(KDA_ERR_NULL, "%s is NULL", name);
+    return KDA_OK;
+  }
+  if ((reinterpret_cast<uintptr_t>(p) & (align - 1u)) != 0)
+    return fail(KDA_ERR_ALIGN, "%s is not %u-byte aligned", name, align);
+  return KDA_OK;
+}
+
+#define KDA_TRY(expr)                      \
+  do {                                     \
+    const kda_status_t s_ = (expr);        \
+    if (s_ != KDA_OK) return s_;           \
+  } while (0)
+
+bool valid_dtype(int32_t d) { return d == KDA_F32 || d == KDA_BF16; }
+
+// Shared validation of the problem description.
+kda_status_t check_params(const kda_params_t *p, bool prefill) {
+  if (p == nullptr) return fail(KDA_ERR_NULL, "params is NULL");
+  if (p->B <= 0 || p->T < 0 || p->H <= 0 || p->dk <= 0 || p->dv <= 0)
+    return fail(KDA_ERR_SHAPE, "bad sizes B=%d T=%d H=%d dk=%d dv=%d", p->B, p->T, p->H, p->dk, p->dv);
+  if (!valid_dtype(p->in_dtype) || !valid_dtype(p->out_dtype))
+    return fail(KDA_ERR_DTYPE, "unknown dtype code in=%d out=%d", p->in_dtype, p->out_dtype);
+  if (!(p->scale >= 0.f) || !std::isfinite(p->scale)) return fail(KDA_ERR_SHAPE, "scale must be finite and >= 0");
+  if (!(p->norm_eps >= 0.f) || !std::isfinite(p->norm_eps)) return fail(KDA_ERR_SHAPE, "norm_eps must be finite and >= 0");
+  if (p->use_qk_l2norm != 0 && p->use_qk_l2norm != 1) return fail(KDA_ERR_SHAPE, "use_qk_l2norm must be 0 or 1");
+  if (prefill && p->chunk != 0 && p->chunk != 16 && p->chunk != 64)
+    return fail(KDA_ERR_UNSUPPORTED, "chunk %d not supported (0, 16 or 64)", p->chunk);
+  // Element counts must stay addressable with 32-bit token indices times heads.
+  const double toks = static_cast<double>(p->B) * p->T * p->H;
+  if (toks * p->dk > 9.0e18 || static_cast<double>(p->B) * p->T > 2147483647.0)
+    return fail(KDA_ERR_SHAPE, "problem too large");
+  return KDA_OK;
+}
+
+kda::Args make_args(const kda_params_t *p) {
+  kda::Args a{};
+  a.B = p->B;
+  a.T = p->T;
+  a.H = p->H;
+  a.dk = p->dk;
+  a.dv = p->dv;
+  a.N = p->B;
+  a.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt(static_cast<float>(p->dk));
+  a.eps = p->norm_eps;
+  a.use_l2 = p->use_qk_l2norm;
+  a.in_bf16 = p->in_dtype == KDA_BF16;
+  a.out_bf16 = p->out_dtype == KDA_BF16;
+  return a;
+}
+
+kda_status_t check_norm(const void *gate, const float *w, void *y, int dv) {
+  const int set = (gate != nullptr) + (w != nullptr) + (y != nullptr);
+  if (set != 0 && set != 3) return fail(KDA_ERR_CONFLICT, "gate, norm_weight and y must be all set or all NULL");
+  if (set == 3) {
+    KDA_TRY(check_ptr(gate, "gate", true));
+    KDA_TRY(check_ptr(w, "norm_weight", true));
+    KDA_TRY(check_ptr(y, "y", true));
+    if (dv < 8 || dv > 512 || (dv & (dv - 1)) != 0)
+      return fail(KDA_ERR_UNSUPPORTED, "gated norm width %d must be a power of two in [8, 512]", dv);
+  }
+  return KDA_OK;
+}
+
+kda_status_t hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *initial_state,
+                               const int32_t *cu_seqlens, const uint8_t *mask, void *o,
+                               float *final_state, const void *gate, const float *norm_weight,
+                               void *y, void *stream) {
+  KDA_TRY(check_params(p, true));
+  KDA_TRY(check_ptr(q, "q", true));
+  KDA_TRY(check_ptr(k, "k", true));
+  KDA_TRY(check_ptr(v, "v", true));
+  KDA_TRY(check_ptr(g, "g", true));
+  KDA_TRY(check_ptr(beta, "beta", true, 4));
+  KDA_TRY(check_ptr(o, "o", true));
+  KDA_TRY(check_ptr(final_state, "final_state", true));
+  KDA_TRY(check_ptr(initial_state, "initial_state", false));
+  KDA_TRY(check_ptr(cu_seqlens, "cu_seqlens", false, 4));
+  KDA_TRY(check_ptr(mask, "mask", false, 1));
+  KDA_TRY(check_norm(gate, norm_weight, y, p->dv));
+  if (cu_seqlens && mask) return fail(KDA_ERR_CONFLICT, "give cu_seqlens or mask, not both");
+  if (cu_seqlens && p->B != 1) return fail(KDA_ERR_CONFLICT, "cu_seqlens needs B == 1 (packed batch)");
+  if (cu_seqlens && p->num_seqs <= 0) return fail(KDA_ERR_SHAPE, "num_seqs must be > 0 with cu_seqlens");
+  kda::Args a = make_args(p);
+  a.N = cu_seqlens ? p->num_seqs : p->B;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.init = initial_state; a.state = final_state;
+  a.cu = cu_seqlens; a.mask = mask; a.o = o;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool norm = y != nullptr;
+  const int chunk = p->chunk;
+  const bool mfma = kda::prefill_mfma_supports(p->dk, p->dv, a.in_bf16) && (chunk == 0 || chunk == 64);
+  if (!mfma) {
+    if (!kda::prefill_valu_supports(p->dk, p->dv))
+      return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dk=%d dv=%d", p->dk, p->dv);
+    if (chunk == 64)
+      return fail(KDA_ERR_UNSUPPORTED, "chunk 64 needs bf16 inputs with dk = dv = 128");
+  }
+  if (mfma) {
+    KDA_TRY(hip_status(kda::launch_prefill_mfma(a, st), "prefill (MFMA)"));
+    if (norm) {
+      const int64_t rows = static_cast<int64_t>(p->B) * p->T * p->H;
+      KDA_TRY(hip_status(kda::launch_gated_rmsnorm(o, gate, norm_weight, y, rows, p->dv, p->norm_eps,
+                                                   a.out_bf16, a.in_bf16, a.out_bf16, st),
+                         "gated norm"));
+    }
+  } else {
+    a.gate = gate; a.norm_w = norm_weight; a.y = y;
+    KDA_TRY(hip_status(kda::launch_prefill_valu(a, st), "prefill (VALU)"));
+  }
+  return KDA_OK;
+}
+
+kda_status_t kda_recurrent_step(const kda_params_t *p, const void *q, const void *k, const void *v,
+                                const float *g, const float *beta, float *state,
+                                const uint8_t *mask, void *o, const void *gate,
+                                const float *norm_weight, void *y, void *stream) {
+  KDA_TRY(check_params(p, false));
+  KDA_TRY(check_ptr(q, "q", true));
+  KDA_TRY(check_ptr(k, "k", true));
+  KDA_TRY(check_ptr(v, "v", true));
+  KDA_TRY(check_ptr(g, "g", true));
+  KDA_TRY(check_ptr(beta, "beta", true, 4));
+  KDA_TRY(check_ptr(state, "state", true));
+  KDA_TRY(check_ptr(o, "o", true));
+  KDA_TRY(check_ptr(mask, "mask", false, 1));
+  KDA_TRY(check_norm(gate, norm_weight, y, p->dv));
+  if (!kda::recurrent_supports(p->dk, p->dv))
+    return fail(KDA_ERR_UNSUPPORTED, "no recurrent kernel for dk=%d dv=%d", p->dk, p->dv);
+  if (p->T == 0) return KDA_OK;
+  kda::Args a = make_args(p);
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.state = state; a.mask = mask; a.o = o;
+  a.gate = gate; a.norm_w = norm_weight; a.y = y;
+  KDA_TRY(hip_status(kda::launch_recurrent(a, static_cast<hipStream_t>(stream)), "recurrent step"));
+  return KDA_OK;
+}
+
+kda_status_t kda_gated_rmsnorm(const void *x, const void *gate, const float *weight, void *y,
+                               int64_t rows, int32_t width, float eps, int32_t in_dtype,
+                               int32_t out_dtype, void *stream) {
+  KDA_TRY(check_ptr(x, "x", true));
+  KDA_TRY(check_ptr(gate, "gate", true));
+  KDA_TRY(check_ptr(weight, "weight", true));
+  KDA_TRY(check_ptr(y, "y", true));
+  if (rows < 0) return fail(KDA_ERR_SHAPE, "rows must be >= 0");
+  if (width < 8 || width > 512 || (width & (width - 1)) != 0)
+    return fail(KDA_ERR_UNSUPPORTED, "width %d must be a power of two in [8, 512]", width);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(KDA_ERR_DTYPE, "unknown dtype code in=%d out=%d", in_dtype, out_dtype);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(KDA_ERR_SHAPE, "eps must be finite and >= 0");
+  if (rows / 256 > 2147483647LL) return fail(KDA_ERR_SHAPE, "too many rows");
+  const int bf = in_dtype == KDA_BF16;
+  KDA_TRY(hip_status(kda::launch_gated_rmsnorm(x, gate, weight, y, rows, width, eps, bf, bf,
+                                               out_dtype == KDA_BF16, static_cast<hipStream_t>(stream)),
+                     "gated norm"));
+  return KDA_OK;
+}
+
+const char *kda_status_string(kda_status_t s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL";
+    case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE";
+    case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE";
+    case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN";
+    case KDA_ERR_CONFLICT: return "KDA_ERR_CONFLICT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+const char *kda_last_error(void) { return g_last_error; }
+
+const char *kda_version(void) { return "kda-mi355x 0.1.0 gfx950"; }
+
+}  // extern "C"

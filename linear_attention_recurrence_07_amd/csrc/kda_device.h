@@ -1,0 +1,89 @@
+// Device helpers shared by the KDA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kL2Eps = 1e-6f;   // in-kernel q/k L2 norm: x / sqrt(sum x^2 + 1e-6)
+
+// ------------------------------------------------------------------ bf16 <-> fp32
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ------------------------------------------------------------------ typed element access
+// Inputs are either fp32 or raw bf16 bits (uint16_t); outputs likewise.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float *p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float *p, size_t i, float v) { p[i] = v; }
+  // four consecutive elements (16-byte aligned)
+  __device__ __forceinline__ static float4 load4(const float *p, size_t i) {
+    return *reinterpret_cast<const float4 *>(p + i);
+  }
+  __device__ __forceinline__ static void store4(float *p, size_t i, float4 v) {
+    *reinterpret_cast<float4 *>(p + i) = v;
+  }
+};
+template <> struct Elem<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t *p, size_t i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store(uint16_t *p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+  // four consecutive elements (8-byte aligned)
+  __device__ __forceinline__ static float4 load4(const uint16_t *p, size_t i) {
+    uint2 w = *reinterpret_cast<const uint2 *>(p + i);
+    return make_float4(lo_bf16(w.x), hi_bf16(w.x), lo_bf16(w.y), hi_bf16(w.y));
+  }
+  __device__ __forceinline__ static void store4(uint16_t *p, size_t i, float4 v) {
+    *reinterpret_cast<uint2 *>(p + i) = pack_bf16x4(v.x, v.y, v.z, v.w);
+  }
+};
+
+// ------------------------------------------------------------------ synchronisation
+// Work-group barrier that orders LDS only.  A plain __syncthreads() also waits for
+// every outstanding global load, which would stall register prefetches.
+__device__ __forceinline__ void sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// Make this wave's LDS writes visible to the rest of the same wave.
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Sum over the lanes of a wave whose lane ids differ only in the bits of MASK
+// (MASK = 31: over 32 consecutive lanes; MASK = 32: over the two half-waves).
+template <int MASK>
+__device__ __forceinline__ float lane_sum(float x) {
+#pragma unroll
+  for (int b = 1; b < 64; b <<= 1)
+    if (MASK & b) x += __shfl_xor(x, b, 64);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+}  // namespace kda

@@ -1,0 +1,41 @@
+// Host-side launchers of the KDA kernels (internal to libkda.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+
+namespace kda {
+
+// Arguments of one prefill or recurrent call after host validation.
+struct Args {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  const float *init;          // prefill: initial state or null
+  float *state;               // recurrent: in/out state; prefill: final state
+  const int32_t *cu;          // packed offsets or null
+  const uint8_t *mask;        // padding mask or null
+  void *o;
+  const void *gate;
+  const float *norm_w;
+  void *y;
+  int B, T, H, dk, dv, N;
+  float scale, eps;
+  int use_l2;
+  int in_bf16, out_bf16;
+};
+
+hipError_t launch_recurrent(const Args &a, hipStream_t s);
+hipError_t launch_prefill_valu(const Args &a, hipStream_t s);
+hipError_t launch_prefill_mfma(const Args &a, hipStream_t s);
+hipError_t launch_gated_rmsnorm(const void *x, const void *gate, const float *w, void *y,
+                                int64_t rows, int width, float eps, int x_bf16, int gate_bf16,
+                                int out_bf16, hipStream_t s);
+
+// Shape support of each kernel family.
+bool recurrent_supports(int dk, int dv);
+bool prefill_valu_supports(int dk, int dv);
+bool prefill_mfma_supports(int dk, int dv, int in_bf16);
+
+}  // namespace kda

@@ -1,0 +1,207 @@
+// Token-by-token KDA step (the decode kernel).
+//
+// Per head the state S[dk][dv] (fp32) is read once, advanced over the call's tokens
+// and written back in place.  For each token (nnterp Kimi-Linear page, Notes, section
+// on KDA decaying each key channel; section 04 docstring):
+//     S' = diag(exp(g)) S                    decay every key channel first
+//     r  = S'^T k,  u = beta (v - r)         delta-rule correction
+//     S  = S' + k u^T
+//     o  = S^T q = S'^T q + u (k . q)        one pass: both reductions read S'
+// with k, q L2-normalised and q scaled by 1/sqrt(dk).
+//
+// Layout: one work-group per (batch row, head) slab.  Thread (cg, rg) owns the four
+// value columns 4cg..4cg+3 of key rows rg, rg+RG, rg+2RG, ... so a wave's float4 loads
+// cover whole 512-byte state rows (coalesced) and the slab lives in registers.  The two
+// column reductions (S'^T k, S'^T q) run over lanes with cross-lane adds, then over
+// waves through LDS.  This kernel is HBM-bound: at B=64, H=96, d=128 it moves 805 MB
+// of state per step and does 0.86 flop per byte.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+template <int D, int RPT, typename TIn, typename TOut, bool NORM>
+__global__ void __launch_bounds__((D / RPT) * (D / 4))
+recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
+                 const float *__restrict__ g, const float *__restrict__ beta,
+                 float *__restrict__ state, const uint8_t *__restrict__ mask,
+                 TOut *__restrict__ o, const TIn *__restrict__ gate,
+                 const float *__restrict__ norm_w, TOut *__restrict__ y,
+                 int T, int H, float scale, int use_l2, float eps) {
+  constexpr int CG = D / 4;          // column groups (float4 each)
+  constexpr int RG = D / RPT;        // row groups
+  constexpr int NT = RG * CG;
+  constexpr int NW = NT / 64;
+  static_assert(NT % 64 == 0 && 64 % CG == 0, "thread layout");
+  constexpr int RED_MASK = 63 & ~(CG - 1);   // lanes sharing a column group within a wave
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cg = tid % CG, rg = tid / CG;
+  const int slab = blockIdx.x;
+  const int b = slab / H, h = slab % H;
+  float *S = state + static_cast<size_t>(slab) * D * D;
+
+  __shared__ float s_k[D], s_q[D], s_e[D];
+  __shared__ float s_red[NW][2][D];
+  __shared__ float s_scal[4];
+
+  float4 s[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m)
+    s[m] = *reinterpret_cast<const float4 *>(S + static_cast<size_t>(rg + RG * m) * D + 4 * cg);
+
+  for (int t = 0; t < T; ++t) {
+    const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
+    if (wave == 0) {
+      constexpr int EPL = (D + 63) / 64;
+      float kk[EPL], qq[EPL], ee[EPL];
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        kk[j] = qq[j] = 0.f;
+        ee[j] = 1.f;
+        if (e < D) {
+          kk[j] = Elem<TIn>::load(k, tok * D + e);
+          qq[j] = Elem<TIn>::load(q, tok * D + e);
+          ee[j] = fast_exp2(g[tok * D + e] * kLog2e);
+          sk += kk[j] * kk[j];
+          sq += qq[j] * qq[j];
+        }
+      }
+      sk = lane_sum<63>(sk);
+      sq = lane_sum<63>(sq);
+      const float kn = use_l2 ? rsqrtf(sk + kL2Eps) : 1.f;
+      const float qn = (use_l2 ? rsqrtf(sq + kL2Eps) : 1.f) * scale;
+      float kq = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        if (e < D) {
+          s_k[e] = kk[j] * kn;
+          s_q[e] = qq[j] * qn;
+          s_e[e] = ee[j];
+          kq += (kk[j] * kn) * (qq[j] * qn);
+        }
+      }
+      kq = lane_sum<63>(kq);
+      if (lane == 0) {
+        s_scal[0] = kq;
+        s_scal[1] = beta[tok];
+        s_scal[2] = (mask == nullptr || mask[static_cast<size_t>(b) * T + t] != 0) ? 1.f : 0.f;
+      }
+    }
+    sync_lds();
+    const bool valid = s_scal[2] != 0.f;
+    if (valid) {
+      float4 r = make_float4(0.f, 0.f, 0.f, 0.f), p = r;
+#pragma unroll
+      for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RG * m;
+        const float a = s_e[i], kv = s_k[i], qv = s_q[i];
+        s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;
+        r.x += kv * s[m].x; r.y += kv * s[m].y; r.z += kv * s[m].z; r.w += kv * s[m].w;
+        p.x += qv * s[m].x; p.y += qv * s[m].y; p.z += qv * s[m].z; p.w += qv * s[m].w;
+      }
+      r.x = lane_sum<RED_MASK>(r.x); r.y = lane_sum<RED_MASK>(r.y);
+      r.z = lane_sum<RED_MASK>(r.z); r.w = lane_sum<RED_MASK>(r.w);
+      p.x = lane_sum<RED_MASK>(p.x); p.y = lane_sum<RED_MASK>(p.y);
+      p.z = lane_sum<RED_MASK>(p.z); p.w = lane_sum<RED_MASK>(p.w);
+      if (lane < CG) {
+        *reinterpret_cast<float4 *>(&s_red[wave][0][4 * cg]) = r;
+        *reinterpret_cast<float4 *>(&s_red[wave][1][4 * cg]) = p;
+      }
+    }
+    sync_lds();
+    float4 out = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (valid) {
+      float4 rr = *reinterpret_cast<const float4 *>(&s_red[0][0][4 * cg]);
+      float4 pp = *reinterpret_cast<const float4 *>(&s_red[0][1][4 * cg]);
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        const float4 r2 = *reinterpret_cast<const float4 *>(&s_red[w][0][4 * cg]);
+        const float4 p2 = *reinterpret_cast<const float4 *>(&s_red[w][1][4 * cg]);
+        rr.x += r2.x; rr.y += r2.y; rr.z += r2.z; rr.w += r2.w;
+        pp.x += p2.x; pp.y += p2.y; pp.z += p2.z; pp.w += p2.w;
+      }
+      const float bt = s_scal[1], kq = s_scal[0];
+      const float4 vv = Elem<TIn>::load4(v, tok * D + 4 * cg);
+      float4 u;
+      u.x = bt * (vv.x - rr.x); u.y = bt * (vv.y - rr.y);
+      u.z = bt * (vv.z - rr.z); u.w = bt * (vv.w - rr.w);
+      out.x = pp.x + u.x * kq; out.y = pp.y + u.y * kq;
+      out.z = pp.z + u.z * kq; out.w = pp.w + u.w * kq;
+#pragma unroll
+      for (int m = 0; m < RPT; ++m) {
+        const float kv = s_k[rg + RG * m];
+        s[m].x += kv * u.x; s[m].y += kv * u.y; s[m].z += kv * u.z; s[m].w += kv * u.w;
+      }
+    }
+    if (rg == 0) {   // the first CG threads (wave 0) hold one full output row
+      Elem<TOut>::store4(o, tok * D + 4 * cg, out);
+      if constexpr (NORM) {
+        float ss = out.x * out.x + out.y * out.y + out.z * out.z + out.w * out.w;
+        ss = lane_sum<CG - 1>(ss);
+        const float rn = rsqrtf(ss / D + eps);
+        const float4 gt = Elem<TIn>::load4(gate, tok * D + 4 * cg);
+        const float4 w = *reinterpret_cast<const float4 *>(norm_w + 4 * cg);
+        float4 yy;
+        yy.x = w.x * out.x * rn * sigmoidf_(gt.x);
+        yy.y = w.y * out.y * rn * sigmoidf_(gt.y);
+        yy.z = w.z * out.z * rn * sigmoidf_(gt.z);
+        yy.w = w.w * out.w * rn * sigmoidf_(gt.w);
+        Elem<TOut>::store4(y, tok * D + 4 * cg, yy);
+      }
+    }
+    sync_lds();   // s_k / s_q / s_e / s_red are rewritten by the next token
+  }
+
+#pragma unroll
+  for (int m = 0; m < RPT; ++m)
+    *reinterpret_cast<float4 *>(S + static_cast<size_t>(rg + RG * m) * D + 4 * cg) = s[m];
+}
+
+template <int D, int RPT, typename TIn, typename TOut>
+hipError_t launch_typed(const Args &a, hipStream_t st) {
+  constexpr int NT = (D / RPT) * (D / 4);
+  const dim3 grid(static_cast<unsigned>(a.B) * a.H), block(NT);
+  const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k),
+            *v = static_cast<const TIn *>(a.v), *gate = static_cast<const TIn *>(a.gate);
+  TOut *o = static_cast<TOut *>(a.o), *y = static_cast<TOut *>(a.y);
+  if (a.y)
+    hipLaunchKernelGGL((recurrent_kernel<D, RPT, TIn, TOut, true>), grid, block, 0, st, q, k, v,
+                       a.g, a.beta, a.state, a.mask, o, gate, a.norm_w, y, a.T, a.H, a.scale,
+                       a.use_l2, a.eps);
+  else
+    hipLaunchKernelGGL((recurrent_kernel<D, RPT, TIn, TOut, false>), grid, block, 0, st, q, k, v,
+                       a.g, a.beta, a.state, a.mask, o, gate, a.norm_w, y, a.T, a.H, a.scale,
+                       a.use_l2, a.eps);
+  return hipGetLastError();
+}
+
+template <int D, int RPT>
+hipError_t launch_d(const Args &a, hipStream_t st) {
+  if (a.in_bf16 && a.out_bf16) return launch_typed<D, RPT, uint16_t, uint16_t>(a, st);
+  if (a.in_bf16) return launch_typed<D, RPT, uint16_t, float>(a, st);
+  if (a.out_bf16) return launch_typed<D, RPT, float, uint16_t>(a, st);
+  return launch_typed<D, RPT, float, float>(a, st);
+}
+
+}  // namespace
+
+bool recurrent_supports(int dk, int dv) {
+  return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);
+}
+
+hipError_t launch_recurrent(const Args &a, hipStream_t st) {
+  switch (a.dk) {
+    case 16: return launch_d<16, 1>(a, st);
+    case 32: return launch_d<32, 4>(a, st);
+    case 64: return launch_d<64, 8>(a, st);
+    case 128: return launch_d<128, 16>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kda

@@ -1,0 +1,132 @@
+"""CPU checks of the C ABI: the library builds and loads, exports every function that
+include/kda.h declares, its struct layout matches the Python binding, and host-side
+validation returns the documented status codes without launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_attention_recurrence_07_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = _declared_functions()
+    for n in ("kda_chunk_prefill", "kda_recurrent_step", "kda_gated_rmsnorm",
+              "kda_status_string", "kda_last_error", "kda_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = K.load_library()
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", K.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\S+)", out))
+    for n in _declared_functions():
+        assert n in exported, n
+
+
+def test_params_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(f'''#include <stdio.h>
+#include <stddef.h>
+#include "{HEADER}"
+int main(void) {{
+  printf("%zu", sizeof(kda_params_t));
+#define F(x) printf(" %zu", offsetof(kda_params_t, x));
+  F(B) F(T) F(H) F(dk) F(dv) F(num_seqs) F(chunk) F(scale) F(use_qk_l2norm) F(in_dtype) F(out_dtype) F(norm_eps)
+  return 0;
+}}''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-o", str(exe), str(src)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(K.KdaParams)] + [getattr(K.KdaParams, f).offset for f, _ in K.KdaParams._fields_]
+    assert got == want
+
+
+def _p(**kw):
+    base = dict(B=1, T=64, H=2, dk=128, dv=128)
+    base.update({k: v for k, v in kw.items() if k in base})
+    rest = {k: v for k, v in kw.items() if k not in base}
+    return K._params(base["B"], base["T"], base["H"], base["dk"], base["dv"], **rest)
+
+
+A = ctypes.c_void_p(1 << 20)          # a 16-byte-aligned stand-in address; never dereferenced
+MIS = ctypes.c_void_p((1 << 20) + 4)  # misaligned
+
+
+def _prefill(p, **ptrs):
+    lib = K.load_library()
+    names = ["q", "k", "v", "g", "beta", "init", "cu", "mask", "o", "fs", "gate", "w", "y"]
+    default = dict(q=A, k=A, v=A, g=A, beta=A, init=None, cu=None, mask=None, o=A, fs=A,
+                   gate=None, w=None, y=None)
+    default.update(ptrs)
+    return lib.kda_chunk_prefill(None if p is None else ctypes.byref(p),
+                                 *[default[n] for n in names], None)
+
+
+def test_prefill_validation_codes():
+    assert _prefill(None) == 1
+    assert _prefill(_p(), q=None) == 1
+    assert _prefill(_p(), o=None) == 1
+    assert _prefill(_p(B=0)) == 2
+    assert _prefill(_p(T=-1)) == 2
+    assert _prefill(_p(in_dtype=7)) == 3
+    assert _prefill(_p(), k=MIS) == 4
+    assert _prefill(_p(B=1, num_seqs=1), cu=A, mask=A) == 5
+    assert _prefill(_p(B=2, num_seqs=2), cu=A) == 5
+    assert _prefill(_p(), gate=A) == 5                       # gate without weight and y
+    assert _prefill(_p(chunk=32)) == 6
+    assert _prefill(_p(dk=96, dv=96)) == 6
+    assert _prefill(_p(dk=16, dv=16, chunk=64)) == 6         # 64-token chunks only on the MFMA path
+    assert _prefill(_p(in_dtype=0, chunk=64)) == 6
+    assert _prefill(_p(scale=float("nan"))) == 2
+
+
+def test_recurrent_and_norm_validation_codes():
+    lib = K.load_library()
+    names = ["q", "k", "v", "g", "beta", "state", "mask", "o", "gate", "w", "y"]
+
+    def rec(p, **ptrs):
+        d = dict(q=A, k=A, v=A, g=A, beta=A, state=A, mask=None, o=A, gate=None, w=None, y=None)
+        d.update(ptrs)
+        return lib.kda_recurrent_step(ctypes.byref(p), *[d[n] for n in names], None)
+
+    assert rec(_p(), state=None) == 1
+    assert rec(_p(dk=128, dv=64)) == 6
+    assert rec(_p(), y=A) == 5
+    assert rec(_p(), g=MIS) == 4
+    assert rec(_p(T=0)) == 0                                  # nothing to do, nothing launched
+    norm = lib.kda_gated_rmsnorm
+    assert norm(A, A, A, A, 10, 100, 1e-6, 1, 1, None) == 6
+    assert norm(A, A, A, A, -1, 128, 1e-6, 1, 1, None) == 2
+    assert norm(None, A, A, A, 10, 128, 1e-6, 1, 1, None) == 1
+    assert norm(A, A, A, A, 10, 128, 1e-6, 5, 1, None) == 3
+    assert norm(A, A, A, A, 10, 128, -1.0, 1, 1, None) == 2
+    assert norm(A, A, A, A, 0, 128, 1e-6, 1, 1, None) == 0   # zero rows: no launch
+
+
+def test_status_strings_and_version():
+    lib = K.load_library()
+    for code, name in K._STATUS.items():
+        assert lib.kda_status_string(code).decode() == name
+    assert "gfx950" in K.version()
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    t = torch.zeros((1, 4, 2, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        K.chunk_prefill(t, t, t, t.float(), torch.zeros((1, 4, 2)))

@@ -1,0 +1,280 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded
+inputs.  Bar: max|GPU - oracle| / rms(oracle) <= 2e-2 for bf16 q/k/v with an fp32 state,
+<= 1e-4 for the all-fp32 path, separately for head outputs, gated-norm outputs and states.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gen import inputs as gi
+from oracle import kda_ref as R
+from tests import kda_testutil as U
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not U.gpu_available():
+        pytest.fail("GPU tests need an MI355X; run them with -m gpu on a GPU host")
+    import linear_attention_recurrence_07_amd as kda
+    kda.load_library()
+
+
+def _check_prefill(x, *, tol, heads=None, chunk=0, tag=""):
+    U.log(f"prefill {x.name}{tag}: B={x.B} T={x.T} H={x.H} d={x.dk} chunk={chunk}")
+    o, fs, y = U.run_prefill(x, DEV, chunk=chunk, heads=heads)
+    U.log(f"oracle {x.name}{tag}: heads={'all' if heads is None else heads}")
+    ro, rfs, ry = U.oracle(x, heads=heads)
+    valid = U.valid_token_mask(x)
+    U.assert_close(f"{x.name}{tag} o", o[valid], ro[valid], tol)
+    U.assert_close(f"{x.name}{tag} final_state", fs, rfs, tol)
+    if ry is not None:
+        U.assert_close(f"{x.name}{tag} y", y[valid], ry[valid], tol)
+    return o, fs, y
+
+
+# ------------------------------------------------------------------ config 1: tiny, all fp32
+def test_tiny_fp32_prefill():
+    _check_prefill(gi.tiny(), tol=U.F32_TOL)
+
+
+def test_tiny_fp32_recurrent_steps():
+    import linear_attention_recurrence_07_amd as kda
+    x = gi.tiny()
+    d = U.device_inputs(x, DEV)
+    ro, rfs, ry = U.oracle(x)
+    U.log("tiny fp32 recurrent: one call over all 64 tokens")
+    state = torch.zeros((1, 2, 16, 16), dtype=torch.float32, device=DEV)
+    o, y = kda.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state,
+                              gate=d["gate"], norm_weight=d["norm_weight"], norm_eps=x.norm_eps)
+    U.assert_close("tiny recurrent(T=64) o", U.to_numpy64(o), ro, U.F32_TOL)
+    U.assert_close("tiny recurrent(T=64) y", U.to_numpy64(y), ry, U.F32_TOL)
+    U.assert_close("tiny recurrent(T=64) state", U.to_numpy64(state), rfs, U.F32_TOL)
+    U.log("tiny fp32 recurrent: 64 calls of one token")
+    state.zero_()
+    outs = []
+    for t in range(x.T):
+        sl = slice(t, t + 1)
+        outs.append(kda.recurrent_step(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
+                                       d["v"][:, sl].contiguous(), d["g"][:, sl].contiguous(),
+                                       d["beta"][:, sl].contiguous(), state))
+    U.assert_close("tiny recurrent(64 x T=1) o", U.to_numpy64(torch.cat(outs, 1)), ro, U.F32_TOL)
+    U.assert_close("tiny recurrent(64 x T=1) state", U.to_numpy64(state), rfs, U.F32_TOL)
+
+
+# ------------------------------------------------------------------ gated norm
+@pytest.mark.parametrize("dtype,width", [("f32", 16), ("f32", 128), ("bf16", 128), ("bf16", 64)])
+def test_gated_rmsnorm(dtype, width):
+    import linear_attention_recurrence_07_amd as kda
+    rng = np.random.default_rng(3)
+    rows = 1000
+    x = rng.standard_normal((rows, width)).astype(np.float32) * 3.0
+    gate = rng.standard_normal((rows, width)).astype(np.float32) * 2.0
+    w = (1.0 + 0.1 * rng.standard_normal(width)).astype(np.float32)
+    if dtype == "bf16":
+        x, gate = gi.f32_to_bf16_bits(x), gi.f32_to_bf16_bits(gate)
+    U.log(f"gated_rmsnorm {dtype} width={width}")
+    y = kda.gated_rmsnorm(U.to_torch(x, dtype, DEV), U.to_torch(gate, dtype, DEV),
+                          torch.from_numpy(w).to(DEV), 1e-6)
+    ref = R.gated_rmsnorm(gi.to_f64(x, dtype), gi.to_f64(gate, dtype), w, 1e-6)
+    U.assert_close(f"gated_rmsnorm {dtype}/{width}", U.to_numpy64(y), ref,
+                   U.F32_TOL if dtype == "f32" else U.BF16_TOL)
+
+
+# ------------------------------------------------------------------ MFMA prefill, small shapes
+@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 200])
+@pytest.mark.parametrize("with_init,norm", [(False, False), (True, True)])
+def test_mfma_prefill_small(T, with_init, norm):
+    x = gi.make_inputs(f"mfma_T{T}", B=2, T=T, H=3, dk=128, dv=128, in_dtype=gi.BF16, seed=T,
+                       initial_state_std=0.02 if with_init else None, norm=norm)
+    _check_prefill(x, tol=U.BF16_TOL)
+
+
+@pytest.mark.parametrize("g_lo,g_hi", [(-5.0, -3.0), (-0.05, 0.0), (-5.0, 0.0)])
+def test_mfma_prefill_decay_ranges(g_lo, g_hi):
+    x = gi.make_inputs(f"mfma_g[{g_lo},{g_hi})", B=1, T=300, H=4, dk=128, dv=128, in_dtype=gi.BF16,
+                       seed=7, g_range=(g_lo, g_hi), initial_state_std=0.02, norm=True)
+    _check_prefill(x, tol=U.BF16_TOL)
+
+
+@pytest.mark.parametrize("chunk", [0, 16])
+def test_bf16_outputs_are_rounded_fp32_outputs(chunk):
+    """bf16 head outputs are the round-to-nearest-even of the fp32 ones, bit for bit; the
+    final state does not depend on the output dtype."""
+    x = gi.make_inputs("bf16out", B=1, T=130, H=2, dk=128, dv=128, in_dtype=gi.BF16, seed=5,
+                       initial_state_std=0.02)
+    U.log(f"prefill bf16 vs fp32 outputs, chunk={chunk}")
+    import linear_attention_recurrence_07_amd as kda
+    d = U.device_inputs(x, DEV)
+    o32, s32 = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                                 chunk=chunk, output_dtype=torch.float32)
+    o16, s16 = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                                 chunk=chunk, output_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(s16, s32)
+
+
+def test_recurrent_bf16_outputs_are_rounded_fp32_outputs():
+    import linear_attention_recurrence_07_amd as kda
+    x = gi.make_inputs("rec_bf16out", B=3, T=5, H=4, dk=128, dv=128, in_dtype=gi.BF16, seed=6,
+                       initial_state_std=0.5)
+    d = U.device_inputs(x, DEV)
+    s1, s2 = d["initial_state"].clone(), d["initial_state"].clone()
+    o32 = kda.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], s1, output_dtype=torch.float32)
+    o16 = kda.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], s2)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(s1, s2)
+
+
+def test_valu_prefill_bf16_chunk16():
+    x = gi.make_inputs("valu_bf16_c16", B=1, T=77, H=2, dk=128, dv=128, in_dtype=gi.BF16, seed=9,
+                       initial_state_std=0.02, norm=True)
+    _check_prefill(x, tol=U.BF16_TOL, chunk=16, tag=" (chunk 16)")
+
+
+@pytest.mark.parametrize("d", [32, 64])
+def test_valu_prefill_fp32_other_sizes(d):
+    x = gi.make_inputs(f"valu_f32_d{d}", B=2, T=45, H=3, dk=d, dv=d, chunk=16, in_dtype=gi.F32,
+                       seed=d, initial_state_std=0.1, norm=True)
+    _check_prefill(x, tol=U.F32_TOL)
+
+
+# ------------------------------------------------------------------ varlen and padding
+def test_varlen_packed_and_padded_small():
+    lengths = (100, 0, 37, 64, 129, 1)
+    x = gi.varlen_packed(lengths, H=3, d=128)
+    _check_prefill(x, tol=U.BF16_TOL, tag=" packed")
+    for left in (False, True):
+        p = gi.padded_from_packed(x, left=left)
+        _check_prefill(p, tol=U.BF16_TOL, tag=" left-padded" if left else " right-padded")
+
+
+def test_packed_tail_untouched():
+    """Tokens of a packed batch past cu_seqlens[-1] are not written."""
+    import linear_attention_recurrence_07_amd as kda
+    x = gi.make_inputs("tail", B=1, T=150, H=2, dk=128, dv=128, in_dtype=gi.BF16, seed=11,
+                       cu_seqlens=[0, 70, 120], num_seqs=2)
+    d = U.device_inputs(x, DEV)
+    o = torch.full((1, 150, 2, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"], out=o)
+    torch.cuda.synchronize()
+    assert torch.all(o[0, 120:] == 7.0)
+
+
+# ------------------------------------------------------------------ state plumbing
+def test_prefill_then_decode_equals_long_prefill():
+    """prefill(0:T1) -> state -> recurrent steps (T1:T) equals the oracle over 0:T."""
+    import linear_attention_recurrence_07_amd as kda
+    x = gi.make_inputs("split", B=2, T=140, H=3, dk=128, dv=128, in_dtype=gi.BF16, seed=13,
+                       initial_state_std=0.02)
+    d = U.device_inputs(x, DEV)
+    ro, rfs, _ = U.oracle(x)
+    T1 = 131
+    U.log("split: prefill 0:131 then 9 single-token steps")
+    o1, st = kda.chunk_prefill(d["q"][:, :T1].contiguous(), d["k"][:, :T1].contiguous(),
+                               d["v"][:, :T1].contiguous(), d["g"][:, :T1].contiguous(),
+                               d["beta"][:, :T1].contiguous(), d["initial_state"],
+                               output_dtype=torch.float32)
+    outs = [o1]
+    for t in range(T1, x.T):
+        sl = slice(t, t + 1)
+        outs.append(kda.recurrent_step(d["q"][:, sl].contiguous(), d["k"][:, sl].contiguous(),
+                                       d["v"][:, sl].contiguous(), d["g"][:, sl].contiguous(),
+                                       d["beta"][:, sl].contiguous(), st, output_dtype=torch.float32))
+    torch.cuda.synchronize()
+    U.assert_close("split o", U.to_numpy64(torch.cat(outs, 1)), ro, U.BF16_TOL)
+    U.assert_close("split state", U.to_numpy64(st), rfs, U.BF16_TOL)
+
+
+def test_final_state_may_alias_initial_state():
+    import linear_attention_recurrence_07_amd as kda
+    x = gi.make_inputs("alias", B=1, T=90, H=2, dk=128, dv=128, in_dtype=gi.BF16, seed=17,
+                       initial_state_std=0.02)
+    d = U.device_inputs(x, DEV)
+    ro, rfs, _ = U.oracle(x)
+    st = d["initial_state"].clone()
+    kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], st, final_state=st)
+    torch.cuda.synchronize()
+    U.assert_close("alias state", U.to_numpy64(st), rfs, U.BF16_TOL)
+
+
+def test_no_write_no_decay_keeps_state_exactly():
+    """beta = 0 and g = 0: every kernel must return the initial state bit for bit."""
+    import linear_attention_recurrence_07_amd as kda
+    x = gi.make_inputs("identity", B=1, T=100, H=2, dk=128, dv=128, in_dtype=gi.BF16, seed=19,
+                       initial_state_std=0.5)
+    d = U.device_inputs(x, DEV)
+    z_g, z_b = torch.zeros_like(d["g"]), torch.zeros_like(d["beta"])
+    _, fs = kda.chunk_prefill(d["q"], d["k"], d["v"], z_g, z_b, d["initial_state"])
+    st = d["initial_state"].clone()
+    kda.recurrent_step(d["q"], d["k"], d["v"], z_g, z_b, st)
+    torch.cuda.synchronize()
+    assert torch.equal(st, d["initial_state"])
+    # the MFMA path carries the state in fp32 accumulators; its only change is exp(0) = 1
+    assert torch.equal(fs, d["initial_state"])
+
+
+def test_deterministic():
+    x = gi.make_inputs("det", B=1, T=256, H=4, dk=128, dv=128, in_dtype=gi.BF16, seed=23,
+                       initial_state_std=0.02, norm=True)
+    a = U.run_prefill(x, DEV)
+    b = U.run_prefill(x, DEV)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+# ------------------------------------------------------------------ full-size configs
+def test_config2_prefill_T2048_all_heads():
+    _check_prefill(gi.prefill(T=2048), tol=U.BF16_TOL)
+
+
+def test_config3_varlen_full():
+    x = gi.varlen_packed()
+    heads = [0, 13, 31, 47, 48, 64, 80, 95]
+    o, fs, y = _check_prefill(x, tol=U.BF16_TOL, heads=heads, tag=" packed")
+    p = gi.padded_from_packed(x)
+    U.log("config 3 right-padded [4, 8192] layout against the packed run (all heads)")
+    po, pfs, py = U.run_prefill(p, DEV)
+    qo, qfs, qy = U.run_prefill(x, DEV)
+    cu = x.cu_seqlens
+    for n in range(len(cu) - 1):
+        ln = cu[n + 1] - cu[n]
+        U.assert_close(f"padded vs packed o seq{n}", po[n, :ln], qo[0, cu[n]:cu[n + 1]], 1e-6)
+        U.assert_close(f"padded vs packed y seq{n}", py[n, :ln], qy[0, cu[n]:cu[n + 1]], 1e-6)
+    U.assert_close("padded vs packed state", pfs, qfs, 1e-6)
+
+
+def test_config4_decode_B64():
+    import linear_attention_recurrence_07_amd as kda
+    from oracle import cref
+    B, H, D, P = 64, 96, 128, 1000
+    U.log("config 4: oracle state over 1000 prompt tokens for 64 rows")
+    state = np.empty((B, H, D, D), np.float32)
+    for r in range(B):
+        pr = gi.decode_prompt(r, P)
+        _, fs = cref.recurrence(pr.q, pr.k, pr.v, pr.g, pr.beta, in_dtype=pr.in_dtype)
+        state[r] = fs[0].astype(np.float32)
+    x = gi.decode_step(B)
+    d = U.device_inputs(x, DEV)
+    st = torch.from_numpy(state).to(DEV)
+    U.log("config 4: one decode step on the GPU")
+    o, y = kda.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st, gate=d["gate"],
+                              norm_weight=d["norm_weight"], norm_eps=x.norm_eps,
+                              output_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rfs = cref.recurrence(x.q, x.k, x.v, x.g, x.beta, state, in_dtype=x.in_dtype)
+    ry = R.gated_rmsnorm(ro, x.f64("gate"), x.norm_weight, x.norm_eps)
+    U.assert_close("decode o", U.to_numpy64(o), ro, U.BF16_TOL)
+    U.assert_close("decode y", U.to_numpy64(y), ry, U.BF16_TOL)
+    U.assert_close("decode state", U.to_numpy64(st), rfs, U.BF16_TOL)
+
+
+def test_config5_long_context_sampled_heads():
+    x = gi.long_context()
+    heads = [0, 47, 48, 95]
+    _check_prefill(x, tol=U.BF16_TOL, heads=heads)
