@@ -109,7 +109,7 @@ def make_decode_inputs(seed: int = 0):
     return state, step
 
 
-def cpu_baseline(seed: int = 0, tokens: int = 2048):
+def cpu_baseline(seed: int = 0, tokens: int = T_PREFILL):
     """The fp64 oracle (C, OpenMP over heads) on the first `tokens` tokens of the same
     prompt, all 96 heads, timed on this host's cores."""
     from gen import inputs as gi
@@ -133,7 +133,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this build runs on one GPU "

@@ -7,18 +7,25 @@
 // incoming state, G the running sum of g over the chunk (per key channel), k and q
 // normalised (q also scaled by 1/sqrt(dk)):
 //     A[s][j]   = beta_s sum_c k_sc k_jc exp(G_sc - G_jc)         (j < s)
-//     U         = (I + A)^-1 (beta V - (beta k exp(G)) S0)
+//     U         = (I + A)^-1 diag(beta) (V - (k exp(G)) S0)
 //     Bqk[r][s] = sum_c q_rc k_sc exp(G_rc - G_sc)                 (s <= r)
 //     O         = (q exp(G)) S0 + Bqk U
 //     S_next    = diag(exp(G_last)) S0 + (k exp(G_last - G))^T U
 // This is the token-by-token recurrence regrouped; it equals it up to rounding.
 //
 // Work decomposition.  Value columns are independent in the recurrence, so a work-group
-// owns one (sequence, head, 64-column tile); its four waves each own 16 value columns and
-// hold their 128 x 16 slice of the fp32 state in accumulator registers for the whole
-// sequence.  The key-side work of a chunk (decay factors, A, Bqk, the inverses of the two
-// diagonal 16x16 blocks of I + A) is shared by the waves through LDS.  The next chunk's
-// inputs are loaded into registers while the current chunk computes.
+// owns one (sequence, head, 64-column tile) with four waves, one per SIMD.  Every step
+// each wave does two independent jobs, one chunk apart, handed over through
+// double-buffered LDS:
+//   producer work on chunk c: load (registers, one chunk ahead), normalise q/k, form the
+//     per-channel decay factors and every MFMA operand of the chunk, and the key-side
+//     products A, Bqk and the inverses of the two diagonal 16x16 blocks of I + A;
+//   consumer work on chunk c-1: the wave owns 16 value columns, keeps its 128 x 16 slice
+//     of the fp32 state in accumulator registers for the whole sequence, and runs the
+//     state products (X -> U -> O, state carry) on MFMA.
+// Producer work is mostly vector-ALU and consumer work mostly matrix-core; placing both in
+// the same straight-line code lets the MFMA pipeline run under the vector work.  Three
+// work-group barriers separate the sub-phases of a step.
 //
 // Decay factoring.  exp(G_s - G_j) is split into a row and a column factor around a
 // reference point: the boundary before block 1 for the off-diagonal block (both factors
@@ -53,44 +60,52 @@ constexpr int DVT = 64;           // value columns per work-group
 constexpr int NTILE = DV / DVT;   // work-groups per (sequence, head)
 constexpr int NW = DVT / 16;      // waves; each owns 16 value columns
 constexpr int NT = NW * 64;       // 256 threads
-constexpr int TPG = 4;            // tokens per thread in the elementwise phase
+constexpr int TPG = 4;            // tokens per producer thread
 constexpr int NG = C / TPG;       // 8 token groups, four per sub-block
-static_assert(NT == 256 && NG == 8, "the elementwise mapping assumes 256 threads");
+static_assert(NW == 4 && NG == 8, "the thread mappings assume these sizes");
 
 // LDS row strides in elements.
-constexpr int LDK = DK + 8;       // [token][channel], 272-byte rows
-constexpr int LDT = C + 8;        // [channel][token]
+constexpr int LDS_ = DK + 4;      // fp16 [token][channel] state operands, 8-byte reads
+constexpr int LDK = DK + 8;       // [token][channel] key-side operands, 16-byte reads
 constexpr int LDV = DVT + 8;      // value tile (bf16)
 constexpr int LDB = C + 8;        // 32x32 Bqk
 constexpr int LDN = SB + 8;       // 16x16 -A(1,0)
-constexpr int LDA = SB * SB + 8;  // fp32 16x16 diagonal blocks of A
+constexpr int LDA = SB * SB + 8;  // fp32 16x16 diagonal blocks of A, transposed
 constexpr int LDO = DVT + 4;      // fp32 output staging
+// (k exp(G_last - G))^T: channel rows of 32 tokens, with 4 extra elements after every
+// 4 rows so the producers' transposed 8-byte writes spread over the banks.
+__device__ __forceinline__ int ket_row(int ch) { return ch * C + (ch >> 2) * 4; }
+constexpr int KET_SIZE = DK * C + (DK / 4) * 4;
 
+// Data handed from the producer work on chunk c to the consumer work on it, one step later.
+struct Hand {
+  uint16_t kb[C * LDS_];       // fp16 k exp(G)       (beta applied by the consumer)
+  uint16_t qt[C * LDS_];       // fp16 q exp(G)
+  uint16_t ket[KET_SIZE];      // fp16 (k exp(G_last - G))^T
+  uint16_t vt[C * LDV];        // bf16 value tile
+  uint16_t bq[C * LDB];        // fp16 Bqk, zero above the diagonal blocks
+  uint16_t na[SB * LDN];       // fp16 -A(1,0)
+  uint16_t td[2 * SB * SB];    // fp16 (I + A_aa)^-1, row-major per block
+  float beta[C];
+  float ec[DK];                // decay over the whole chunk
+};
 struct Smem {
-  // operands of the state products (fp16)
-  uint16_t kb[C * LDK];        // beta k exp(G)
-  uint16_t qt[C * LDK];        // q exp(G)
-  uint16_t ket[DK * LDT];      // (k exp(G_last - G))^T
-  // operands of the key-side products
-  uint16_t rkd[C * LDK];       // bf16 k exp(G - G_mid(block))         (also O staging)
+  Hand hand[2];
+  // producer-internal (key-side operands)
+  uint16_t rkd[C * LDK];       // bf16 k exp(G - G_mid(block))
   uint16_t rqd_hi[C * LDK];    // bf16 q exp(G - G_mid(block)), hi part
   uint16_t rqd_lo[C * LDK];    //                                  lo part
   uint16_t ckd_hi[C * LDK];    // bf16 k exp(G_mid(block) - G), hi part
   uint16_t ckd_lo[C * LDK];    //                                  lo part
-  uint16_t rk1[SB * LDK];      // fp16 k exp(G - G_15) for block-1 tokens
-  uint16_t rq1[SB * LDK];      // fp16 q exp(G - G_15) for block-1 tokens
-  uint16_t ck0[SB * LDK];      // fp16 k exp(G_15 - G) for block-0 tokens
-  uint16_t vt[C * LDV];        // value tile (bf16)
-  uint16_t bq[C * LDB];        // fp16 Bqk, zero above the diagonal blocks
-  uint16_t na[SB * LDN];       // fp16 -A(1,0)
-  uint16_t td[2 * SB * SB];    // fp16 (I + A_aa)^-1, row-major per block
-  float adiag[2 * LDA];        // A_aa (strictly lower), fp32
-  float beta[C];
+  uint16_t rk1[C * LDK];       // fp16 k exp(G - G_15)   (rows of block 1 are used)
+  uint16_t rq1[C * LDK];       // fp16 q exp(G - G_15)   (rows of block 1 are used)
+  uint16_t ck0[C * LDK];       // fp16 k exp(G_15 - G)   (rows of block 0 are used)
+  float at[2 * LDA];           // A_aa transposed: at[a][j][s] = A[16a+s][16a+j]
   float gtot[NG * DK];         // decay product over each 4-token group
-  float ec[DK];                // decay over the whole chunk
+  // consumer side
+  float ost[C * LDO];          // fp32 output staging
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
-static_assert(C * LDO * 4 <= C * LDK * 2 * 3, "O staging fits in rkd..rqd_lo");
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ f16x8 as_f16x8(uint4 u) { return __builtin_bit_cast(f16x8, u); }
@@ -98,7 +113,9 @@ __device__ __forceinline__ f16x4 as_f16x4(uint2 u) { return __builtin_bit_cast(f
 __device__ __forceinline__ uint2 lds_u2(const uint16_t *p) { return *reinterpret_cast<const uint2 *>(p); }
 __device__ __forceinline__ uint4 lds_u4(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ uint4 join(uint2 a, uint2 b) { return make_uint4(a.x, a.y, b.x, b.y); }
-
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   const f16x2 h = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
   return __builtin_bit_cast(uint32_t, h);
@@ -108,26 +125,15 @@ __device__ __forceinline__ uint2 pack_f16x4(float a, float b, float c, float d) 
 }
 // x = hi + lo with both parts fp16 (about 22 significant bits together).
 __device__ __forceinline__ void split_f16x4(f32x4 x, uint2 &hi, uint2 &lo) {
-  float h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const _Float16 hh = static_cast<_Float16>(x[i]);
-    h[i] = static_cast<float>(hh);
-    l[i] = x[i] - h[i];
-  }
-  hi = pack_f16x4(h[0], h[1], h[2], h[3]);
-  lo = pack_f16x4(l[0], l[1], l[2], l[3]);
+  hi = pack_f16x4(x[0], x[1], x[2], x[3]);
+  const f16x4 h = as_f16x4(hi);
+  lo = pack_f16x4(x[0] - static_cast<float>(h[0]), x[1] - static_cast<float>(h[1]),
+                  x[2] - static_cast<float>(h[2]), x[3] - static_cast<float>(h[3]));
 }
 // x = hi + lo with both parts bf16 (about 16 significant bits together).
 __device__ __forceinline__ void split_bf16x4(const float *x, uint2 &hi, uint2 &lo) {
-  float h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = bf16_to_f32(f32_to_bf16(x[i]));
-    l[i] = x[i] - h[i];
-  }
-  hi = pack_bf16x4(h[0], h[1], h[2], h[3]);
-  lo = pack_bf16x4(l[0], l[1], l[2], l[3]);
+  hi = pack_bf16x4(x[0], x[1], x[2], x[3]);
+  lo = pack_bf16x4(x[0] - lo_bf16(hi.x), x[1] - hi_bf16(hi.x), x[2] - lo_bf16(hi.y), x[3] - hi_bf16(hi.y));
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
@@ -141,7 +147,6 @@ __device__ __forceinline__ f32x4 mfma_f16k16(uint2 a, uint2 b, f32x4 c) {
 }
 
 // Key-side 16x16 blocks.  Result layout: acc[i] = block[4*lg + i][l16].
-// Diagonal block of A (bf16 factors around the block's mid token).
 __device__ __forceinline__ f32x4 a_diag(const Smem &sm, int a, int l16, int lg) {
   const uint16_t *rp = sm.rkd + (SB * a + l16) * LDK + 8 * lg;
   const uint16_t *cp = sm.ckd_hi + (SB * a + l16) * LDK + 8 * lg;
@@ -150,7 +155,6 @@ __device__ __forceinline__ f32x4 a_diag(const Smem &sm, int a, int l16, int lg) 
   for (int s = 0; s < DK / 32; ++s) acc = mfma_bf16(lds_u4(rp + 32 * s), lds_u4(cp + 32 * s), acc);
   return acc;
 }
-// Diagonal block of Bqk: hi/lo-split bf16 factors, three products per K step.
 __device__ __forceinline__ f32x4 bqk_diag(const Smem &sm, int a, int l16, int lg) {
   const int ro = (SB * a + l16) * LDK + 8 * lg;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -164,7 +168,6 @@ __device__ __forceinline__ f32x4 bqk_diag(const Smem &sm, int a, int l16, int lg
   }
   return acc;
 }
-// Block (1,0) of A (rows rk1) or of Bqk (rows rq1): fp16 factors around token 15.
 __device__ __forceinline__ f32x4 off_block(const uint16_t *rows, const Smem &sm, int l16, int lg) {
   const uint16_t *rp = rows + l16 * LDK + 8 * lg;
   const uint16_t *cp = sm.ck0 + l16 * LDK + 8 * lg;
@@ -181,7 +184,7 @@ struct Raw {   // one chunk's inputs for one thread, as loaded
   uint4 v;
 };
 
-template <typename TOut, bool HAS_INIT>
+template <typename TOut, bool HAS_INIT, bool HAS_MASK>
 __global__ void __launch_bounds__(NT, 1)
 prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                     const uint16_t *__restrict__ v, const float *__restrict__ g,
@@ -189,7 +192,8 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
                     const int32_t *__restrict__ cu, const uint8_t *__restrict__ mask,
                     TOut *__restrict__ o, int T, int H, int units, float scale, int use_l2) {
   __shared__ Smem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: branches stay scalar
   const int l16 = lane & 15, lg = lane >> 4;
 
   // Work-groups are dealt to the 8 XCDs round-robin; give both column tiles of one
@@ -210,55 +214,64 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
     t_end = T;
   }
   const int col0 = tile * DVT;
-  const int wcol = 16 * wave + l16;            // this lane's value column within the tile
   const size_t slab = (static_cast<size_t>(n) * H + h) * DK * DV;
-
-  // State tile t (key channels 16t..16t+15): Sacc[t][i] = S[16t + 4*lg + i][col0 + wcol].
-  f32x4 Sacc[DK / 16];
-#pragma unroll
-  for (int t = 0; t < DK / 16; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      Sacc[t][i] = HAS_INIT ? init[slab + static_cast<size_t>(16 * t + 4 * lg + i) * DV + col0 + wcol] : 0.f;
-
-  for (int e = tid; e < C * LDB; e += NT) sm.bq[e] = 0;   // the block above the diagonal stays zero
-
-  const int cg = tid & 31, tg = tid >> 5;       // elementwise mapping: 4 channels x 4 tokens
-  const int blk = tg >> 2;
   const int nchunks = (t_end - t_begin + C - 1) / C;
+  const size_t tok_stride = static_cast<size_t>(H) * DK;      // elements between tokens (q, k, g)
+  const size_t row0 = static_cast<size_t>(b) * T;             // first token row of this batch row
 
-  auto token_valid = [&](int t) {
-    return t < t_end && (mask == nullptr || mask[static_cast<size_t>(b) * T + t] != 0);
-  };
-  auto load_raw = [&](int c0, Raw &r) {
+  for (int e = tid; e < C * LDB; e += NT) sm.hand[0].bq[e] = sm.hand[1].bq[e] = 0;
+
+  // ---------------------------------------------------------------- producer state
+  const int cg = tid & 31, tg = tid >> 5;         // 4 channels x 4 tokens per thread
+  const int blk = tg >> 2;                        // wave-uniform sub-block of this thread
+  Raw raw;
+  // Loads are unconditional (clamped to the sequence's last token) and masked with
+  // selects, so the steady-state loop stays one basic block per sub-phase.
+  auto load_raw = [&](int c0) {
 #pragma unroll
     for (int j = 0; j < TPG; ++j) {
       const int t = c0 + TPG * tg + j;
-      const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
-      if (token_valid(t)) {
-        r.k[j] = *reinterpret_cast<const uint2 *>(k + tok * DK + 4 * cg);
-        r.q[j] = *reinterpret_cast<const uint2 *>(q + tok * DK + 4 * cg);
-        r.g[j] = *reinterpret_cast<const float4 *>(g + tok * DK + 4 * cg);
-        r.beta[j] = beta[tok];
-      } else {   // padding and tokens past the sequence act as no-ops
-        r.k[j] = r.q[j] = make_uint2(0, 0);
-        r.g[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        r.beta[j] = 0.f;
-      }
+      const int tc = min(t, t_end - 1);
+      bool valid = t < t_end;
+      if constexpr (HAS_MASK) valid = valid && mask[row0 + tc] != 0;
+      const size_t off = (row0 + tc) * tok_stride + static_cast<size_t>(h) * DK + 4 * cg;
+      const uint2 kk = *reinterpret_cast<const uint2 *>(k + off);
+      const uint2 qq = *reinterpret_cast<const uint2 *>(q + off);
+      const float4 gg = *reinterpret_cast<const float4 *>(g + off);
+      const float bb = beta[(row0 + tc) * H + h];
+      // padding and tokens past the sequence act as no-ops
+      raw.k[j] = valid ? kk : make_uint2(0, 0);
+      raw.q[j] = valid ? qq : make_uint2(0, 0);
+      raw.g[j] = valid ? gg : make_float4(0.f, 0.f, 0.f, 0.f);
+      raw.beta[j] = valid ? bb : 0.f;
     }
+    // value tile (32 tokens x 64 columns): token tid/8, 8 columns per thread
     const int t = c0 + (tid >> 3);
-    r.v = make_uint4(0, 0, 0, 0);
-    if (token_valid(t))
-      r.v = *reinterpret_cast<const uint4 *>(v + ((static_cast<size_t>(b) * T + t) * H + h) * DV + col0 + (tid & 7) * 8);
+    const int tc = min(t, t_end - 1);
+    bool valid = t < t_end;
+    if constexpr (HAS_MASK) valid = valid && mask[row0 + tc] != 0;
+    const uint4 vv = *reinterpret_cast<const uint4 *>(v + ((row0 + tc) * H + h) * DV + col0 + (tid & 7) * 8);
+    raw.v = valid ? vv : make_uint4(0, 0, 0, 0);
   };
+  float kx[TPG][4], qx[TPG][4], fw[TPG][4], bw[TPG][4];
 
-  Raw raw;
-  if (nchunks > 0) load_raw(t_begin, raw);
+  // ---------------------------------------------------------------- consumer state
+  const int wcol = 16 * wave + l16;              // this lane's value column in the tile
+  f32x4 Sacc[DK / 16];                           // Sacc[t][i] = S[16t + 4lg + i][col0 + wcol]
+#pragma unroll
+  for (int t = 0; t < DK / 16; ++t) Sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (HAS_INIT) {
+#pragma unroll
+    for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Sacc[t][i] = init[slab + static_cast<size_t>(16 * t + 4 * lg + i) * DV + col0 + wcol];
+  }
+  uint4 Uh = make_uint4(0, 0, 0, 0), Ul = Uh;
 
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
-    const int c0 = t_begin + chunk * C;
-    // ------------------------------------------------------------ phase L: elementwise
-    float kx[TPG][4], qx[TPG][4], fw[TPG][4], bw[TPG][4], bx[TPG];
+  // ================================================================ producer, sub-phase 1
+  // Unpack chunk c0's inputs, start loading chunk c_next, normalise q/k, decay factors.
+  auto prod1 = [&](Hand &hp, int c_next) {
 #pragma unroll
     for (int j = 0; j < TPG; ++j) {
       kx[j][0] = lo_bf16(raw.k[j].x); kx[j][1] = hi_bf16(raw.k[j].x);
@@ -266,12 +279,11 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
       qx[j][0] = lo_bf16(raw.q[j].x); qx[j][1] = hi_bf16(raw.q[j].x);
       qx[j][2] = lo_bf16(raw.q[j].y); qx[j][3] = hi_bf16(raw.q[j].y);
       fw[j][0] = raw.g[j].x; fw[j][1] = raw.g[j].y; fw[j][2] = raw.g[j].z; fw[j][3] = raw.g[j].w;
-      bx[j] = raw.beta[j];
+      hp.beta[TPG * tg + j] = raw.beta[j];          // the same value from all 32 lanes
     }
-    *reinterpret_cast<uint4 *>(sm.vt + (tid >> 3) * LDV + (tid & 7) * 8) = raw.v;
-    if (chunk + 1 < nchunks) load_raw(c0 + C, raw);    // prefetch the next chunk
-
-    // q/k L2 norms over the 128 channels (32 lanes x 4 channels).
+    *reinterpret_cast<uint4 *>(hp.vt + (tid >> 3) * LDV + (tid & 7) * 8) = raw.v;
+    load_raw(c_next);
+    // q/k L2 norms over the 128 channels (32 lanes x 4 channels)
 #pragma unroll
     for (int j = 0; j < TPG; ++j) {
       float sk = kx[j][0] * kx[j][0] + kx[j][1] * kx[j][1] + kx[j][2] * kx[j][2] + kx[j][3] * kx[j][3];
@@ -286,8 +298,7 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
         qx[j][c] *= qn;
       }
     }
-    // Per-token decay factors and running products over the thread's 4 tokens:
-    // fw[j] = prod_{i<=j} e_i (inclusive), bw[j] = prod_{j<i<4} e_i (exclusive).
+    // fw[j] = prod_{i<=j} e_i (inclusive), bw[j] = prod_{j<i<4} e_i (exclusive)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float e[TPG];
@@ -308,126 +319,113 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
     }
     *reinterpret_cast<float4 *>(sm.gtot + tg * DK + 4 * cg) =
         make_float4(fw[TPG - 1][0], fw[TPG - 1][1], fw[TPG - 1][2], fw[TPG - 1][3]);
-    if (cg == 0) {
+  };
+
+  // ================================================================ producer, sub-phase 2
+  // Combine the group decay products and write every MFMA operand of the chunk.
+  auto prod2 = [&](Hand &hp) {
+    float gt[NG][4];
 #pragma unroll
-      for (int j = 0; j < TPG; ++j) sm.beta[TPG * tg + j] = bx[j];
+    for (int m = 0; m < NG; ++m) {
+      const float4 x = *reinterpret_cast<const float4 *>(sm.gtot + m * DK + 4 * cg);
+      gt[m][0] = x.x; gt[m][1] = x.y; gt[m][2] = x.z; gt[m][3] = x.w;
     }
-    sync_lds();
-    {
-      float gt[NG][4];
+    const int gi = tg & 3;                         // group within the sub-block
+    float e3m[4], e4m[4], fkb[4], fke[4], ih1[4], ih2[4], ec[4];
 #pragma unroll
-      for (int m = 0; m < NG; ++m) {
-        const float4 x = *reinterpret_cast<const float4 *>(sm.gtot + m * DK + 4 * cg);
-        gt[m][0] = x.x; gt[m][1] = x.y; gt[m][2] = x.z; gt[m][3] = x.w;
-      }
-      float e3m[4], e4m[4], est[4], eend[4], ih1[4], ih2[4];
+    for (int c = 0; c < 4; ++c) {
+      // this block's group products, selected with constant register indices
+      const float b0 = blk ? gt[4][c] : gt[0][c], b1 = blk ? gt[5][c] : gt[1][c];
+      const float b2 = blk ? gt[6][c] : gt[2][c], b3 = blk ? gt[7][c] : gt[3][c];
+      const float p01 = b0 * b1, p23 = b2 * b3;
+      e3m[c] = gi == 0 ? 1.f : gi == 1 ? b0 : gi == 2 ? p01 : p01 * b2;     // block start -> group
+      e4m[c] = gi == 3 ? 1.f : gi == 2 ? b3 : gi == 1 ? p23 : b1 * p23;     // group -> block end
+      ih1[c] = __builtin_amdgcn_rcpf(p01);        // block start -> 8th token
+      ih2[c] = __builtin_amdgcn_rcpf(p23);        // 8th token -> block end
+      const float d0 = (gt[0][c] * gt[1][c]) * (gt[2][c] * gt[3][c]);     // decay over block 0
+      const float d1 = (gt[4][c] * gt[5][c]) * (gt[6][c] * gt[7][c]);     // decay over block 1
+      fkb[c] = blk ? d0 : 1.f;      // exp(G_r) = fkb * exp(G_r - G_block_start)
+      fke[c] = blk ? 1.f : d1;      // exp(G_last - G_r) = fke * exp(G_block_end - G_r)
+      ec[c] = d0 * d1;
+    }
+#pragma unroll
+    for (int j = 0; j < TPG; ++j) {
+      const int r = TPG * tg + j;
+      float k3[4], q3[4], k4[4], rkd[4], rqd[4], ckd[4], kb[4], qt[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        float a3 = 1.f, a4 = 1.f, s0 = 1.f, s1 = 1.f;
-#pragma unroll
-        for (int m = 0; m < NG; ++m) {
-          if ((m >> 2) == blk && m < tg) a3 *= gt[m][c];          // block start -> this group
-          if ((m >> 2) == blk && m > tg) a4 *= gt[m][c];          // this group -> block end
-          if ((m >> 2) < blk) s0 *= gt[m][c];                     // chunk start -> block start
-          if ((m >> 2) > blk) s1 *= gt[m][c];                     // block end -> chunk end
-        }
-        e3m[c] = a3; e4m[c] = a4; est[c] = s0; eend[c] = s1;
-        ih1[c] = 1.f / (gt[4 * blk][c] * gt[4 * blk + 1][c]);   // block start -> mid token
-        ih2[c] = 1.f / (gt[4 * blk + 2][c] * gt[4 * blk + 3][c]);
+        const float e3 = e3m[c] * fw[j][c];       // exp(G_r - G_block_start)
+        const float e4 = bw[j][c] * e4m[c];       // exp(G_block_end - G_r)
+        k3[c] = kx[j][c] * e3;
+        q3[c] = qx[j][c] * e3;
+        k4[c] = kx[j][c] * e4;
+        rkd[c] = k3[c] * ih1[c];                  // k exp(G_r - G_mid)
+        rqd[c] = q3[c] * ih1[c];
+        ckd[c] = k4[c] * ih2[c];                  // k exp(G_mid - G_r)
+        kb[c] = k3[c] * fkb[c];
+        qt[c] = q3[c] * fkb[c];
+        kx[j][c] = k4[c] * fke[c];                // k exp(G_last - G_r), for the transpose
       }
-#pragma unroll
-      for (int j = 0; j < TPG; ++j) {
-        const int r = TPG * tg + j;
-        float kb[4], qt[4], rkd[4], rqd[4], ckd[4], k3[4], q3[4], k4[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float e3 = e3m[c] * fw[j][c];     // exp(G_r - G_block_start)
-          const float e4 = bw[j][c] * e4m[c];     // exp(G_block_end - G_r)
-          k3[c] = kx[j][c] * e3;
-          q3[c] = qx[j][c] * e3;
-          k4[c] = kx[j][c] * e4;
-          kb[c] = bx[j] * est[c] * k3[c];
-          qt[c] = est[c] * q3[c];
-          rkd[c] = k3[c] * ih1[c];                // k exp(G_r - G_mid)
-          rqd[c] = q3[c] * ih1[c];
-          ckd[c] = k4[c] * ih2[c];                // k exp(G_mid - G_r)
-          kx[j][c] = k4[c] * eend[c];             // k exp(G_last - G_r), for the transpose
-        }
-        const int o4 = r * LDK + 4 * cg;
-        *reinterpret_cast<uint2 *>(sm.kb + o4) = pack_f16x4(kb[0], kb[1], kb[2], kb[3]);
-        *reinterpret_cast<uint2 *>(sm.qt + o4) = pack_f16x4(qt[0], qt[1], qt[2], qt[3]);
-        *reinterpret_cast<uint2 *>(sm.rkd + o4) = pack_bf16x4(rkd[0], rkd[1], rkd[2], rkd[3]);
-        uint2 hi, lo;
-        split_bf16x4(rqd, hi, lo);
-        *reinterpret_cast<uint2 *>(sm.rqd_hi + o4) = hi;
-        *reinterpret_cast<uint2 *>(sm.rqd_lo + o4) = lo;
-        split_bf16x4(ckd, hi, lo);
-        *reinterpret_cast<uint2 *>(sm.ckd_hi + o4) = hi;
-        *reinterpret_cast<uint2 *>(sm.ckd_lo + o4) = lo;
-        if (blk == 1) {
-          const int o1 = (r - SB) * LDK + 4 * cg;
-          *reinterpret_cast<uint2 *>(sm.rk1 + o1) = pack_f16x4(k3[0], k3[1], k3[2], k3[3]);
-          *reinterpret_cast<uint2 *>(sm.rq1 + o1) = pack_f16x4(q3[0], q3[1], q3[2], q3[3]);
-        } else {
-          *reinterpret_cast<uint2 *>(sm.ck0 + o4) = pack_f16x4(k4[0], k4[1], k4[2], k4[3]);
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint2 *>(sm.ket + (4 * cg + c) * LDT + TPG * tg) =
-            pack_f16x4(kx[0][c], kx[1][c], kx[2][c], kx[3][c]);
-      if (tg == 0) {
-        float ec[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          ec[c] = 1.f;
-#pragma unroll
-          for (int m = 0; m < NG; ++m) ec[c] *= gt[m][c];
-        }
-        *reinterpret_cast<float4 *>(sm.ec + 4 * cg) = make_float4(ec[0], ec[1], ec[2], ec[3]);
-      }
+      *reinterpret_cast<uint2 *>(hp.kb + r * LDS_ + 4 * cg) = pack_f16x4(kb[0], kb[1], kb[2], kb[3]);
+      *reinterpret_cast<uint2 *>(hp.qt + r * LDS_ + 4 * cg) = pack_f16x4(qt[0], qt[1], qt[2], qt[3]);
+      const int o4 = r * LDK + 4 * cg;
+      *reinterpret_cast<uint2 *>(sm.rkd + o4) = pack_bf16x4(rkd[0], rkd[1], rkd[2], rkd[3]);
+      uint2 hi, lo;
+      split_bf16x4(rqd, hi, lo);
+      *reinterpret_cast<uint2 *>(sm.rqd_hi + o4) = hi;
+      *reinterpret_cast<uint2 *>(sm.rqd_lo + o4) = lo;
+      split_bf16x4(ckd, hi, lo);
+      *reinterpret_cast<uint2 *>(sm.ckd_hi + o4) = hi;
+      *reinterpret_cast<uint2 *>(sm.ckd_lo + o4) = lo;
+      // off-diagonal factors around token 15 (rows of block 1 / columns of block 0 are read)
+      *reinterpret_cast<uint2 *>(sm.rk1 + o4) = pack_f16x4(k3[0], k3[1], k3[2], k3[3]);
+      *reinterpret_cast<uint2 *>(sm.rq1 + o4) = pack_f16x4(q3[0], q3[1], q3[2], q3[3]);
+      *reinterpret_cast<uint2 *>(sm.ck0 + o4) = pack_f16x4(k4[0], k4[1], k4[2], k4[3]);
     }
-    sync_lds();
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<uint2 *>(hp.ket + ket_row(4 * cg + c) + TPG * tg) =
+          pack_f16x4(kx[0][c], kx[1][c], kx[2][c], kx[3][c]);
+    *reinterpret_cast<float4 *>(hp.ec + 4 * cg) = make_float4(ec[0], ec[1], ec[2], ec[3]);
+  };
 
-    // ------------------------------------------------------------ phase K: key-side products
+  // ================================================================ producer, sub-phase 3
+  // Key-side products: A and Bqk blocks, the inverses of the diagonal blocks of I + A.
+  auto prod3 = [&](Hand &hp) {
     if (wave == 0) {
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const f32x4 acc = a_diag(sm, a, l16, lg);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int sl = 4 * lg + i;
-          sm.adiag[a * LDA + sl * SB + l16] = (l16 < sl) ? sm.beta[SB * a + sl] * acc[i] : 0.f;
-        }
+        float4 w;   // A[s][j] = beta_s * acc for j < s, stored transposed at at[a][j][s]
+        const float *bs = hp.beta + SB * a + 4 * lg;
+        w.x = (l16 < 4 * lg + 0) ? bs[0] * acc[0] : 0.f;
+        w.y = (l16 < 4 * lg + 1) ? bs[1] * acc[1] : 0.f;
+        w.z = (l16 < 4 * lg + 2) ? bs[2] * acc[2] : 0.f;
+        w.w = (l16 < 4 * lg + 3) ? bs[3] * acc[3] : 0.f;
+        *reinterpret_cast<float4 *>(sm.at + a * LDA + l16 * SB + 4 * lg) = w;
       }
       wave_sync_lds();
-      if (lane < 32) {   // (I + A_aa)^-1 by forward substitution: lane (block a, column c)
-        const int a = lane >> 4, c = l16;
-        float tc[SB];
+      // (I + A_aa)^-1, column c, by right-looking elimination; lanes 32-63 repeat 0-31
+      const int a = (lane >> 4) & 1, c = l16;
+      float tc[SB];
 #pragma unroll
-        for (int r = 0; r < SB; ++r) {
-          float acc = (r == c) ? 1.f : 0.f;
-          const float *arow = sm.adiag + a * LDA + r * SB;
+      for (int r = 0; r < SB; ++r) tc[r] = (r == c) ? 1.f : 0.f;
 #pragma unroll
-          for (int j = 0; j < r; ++j) acc -= arow[j] * tc[j];
-          tc[r] = acc;
-        }
+      for (int j = 0; j < SB - 1; ++j) {
+        const float *col = sm.at + a * LDA + j * SB;   // A[.][j]
 #pragma unroll
-        for (int r = 0; r < SB; ++r) {
-          const _Float16 hv = static_cast<_Float16>(tc[r]);
-          sm.td[(a * SB + r) * SB + c] = __builtin_bit_cast(uint16_t, hv);
-        }
+        for (int r = j + 1; r < SB; ++r) tc[r] -= col[r] * tc[j];
       }
+#pragma unroll
+      for (int r = 0; r < SB; ++r) hp.td[(a * SB + r) * SB + c] = f16_bits(tc[r]);
     } else if (wave == 1) {
-      const f32x4 accA = off_block(sm.rk1, sm, l16, lg);
-      const f32x4 accB = off_block(sm.rq1, sm, l16, lg);
+      const f32x4 accA = off_block(sm.rk1 + SB * LDK, sm, l16, lg);
+      const f32x4 accB = off_block(sm.rq1 + SB * LDK, sm, l16, lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int sl = 4 * lg + i;
-        const _Float16 na = static_cast<_Float16>(-sm.beta[SB + sl] * accA[i]);
-        const _Float16 bq = static_cast<_Float16>(accB[i]);
-        sm.na[sl * LDN + l16] = __builtin_bit_cast(uint16_t, na);
-        sm.bq[(SB + sl) * LDB + l16] = __builtin_bit_cast(uint16_t, bq);
+        hp.na[sl * LDN + l16] = f16_bits(-hp.beta[SB + sl] * accA[i]);
+        hp.bq[(SB + sl) * LDB + l16] = f16_bits(accB[i]);
       }
     } else {
       const int a = wave - 2;
@@ -435,103 +433,139 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int sl = 4 * lg + i;
-        const _Float16 bq = static_cast<_Float16>(l16 <= sl ? acc[i] : 0.f);
-        sm.bq[(SB * a + sl) * LDB + SB * a + l16] = __builtin_bit_cast(uint16_t, bq);
+        hp.bq[(SB * a + sl) * LDB + SB * a + l16] = f16_bits(l16 <= sl ? acc[i] : 0.f);
       }
     }
-    sync_lds();
+  };
 
-    // ------------------------------------------------------------ phase S: state products
-    // S0 as fp16 B operands; K-step s covers channels {32s + 4lg + 0..3, 32s + 16 + 4lg + 0..3}.
+  // ================================================================ consumer, sub-phase 1
+  // X = beta (V - (k exp(G)) S0);  U0 = T00 X0;  U1 = T11 (X1 - A10 U0).
+  auto cons1 = [&](const Hand &hc) {
+    uint4 Sh[DK / 32];   // S0 (fp16); K step s covers channels {32s+4lg+0..3, 32s+16+4lg+0..3}
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+      const f32x4 a = Sacc[2 * s], bb = Sacc[2 * s + 1];
+      Sh[s] = join(pack_f16x4(a[0], a[1], a[2], a[3]), pack_f16x4(bb[0], bb[1], bb[2], bb[3]));
+    }
+    f32x4 X[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t *ap = hc.kb + (SB * m + l16) * LDS_ + 4 * lg;
+#pragma unroll
+      for (int s = 0; s < DK / 32; ++s) acc = mfma_f16(join(lds_u2(ap + 32 * s), lds_u2(ap + 32 * s + 16)), Sh[s], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = SB * m + 4 * lg + i;
+        X[m][i] = hc.beta[r] * (bf16_to_f32(hc.vt[r * LDV + wcol]) - acc[i]);
+      }
+    }
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    uint2 u0h, u0l, u1h, u1l, xh, xl;
+    split_f16x4(X[0], xh, xl);
+    const uint2 t0 = lds_u2(hc.td + l16 * SB + 4 * lg);
+    f32x4 U0 = mfma_f16k16(t0, xl, zero);
+    U0 = mfma_f16k16(t0, xh, U0);
+    split_f16x4(U0, u0h, u0l);
+    const uint2 nav = lds_u2(hc.na + l16 * LDN + 4 * lg);
+    f32x4 acc = X[1];
+    acc = mfma_f16k16(nav, u0l, acc);
+    acc = mfma_f16k16(nav, u0h, acc);
+    split_f16x4(acc, xh, xl);
+    const uint2 t1 = lds_u2(hc.td + (SB + l16) * SB + 4 * lg);
+    f32x4 U1 = mfma_f16k16(t1, xl, zero);
+    U1 = mfma_f16k16(t1, xh, U1);
+    split_f16x4(U1, u1h, u1l);
+    Uh = join(u0h, u1h);   // tokens {4lg+0..3, 16+4lg+0..3} as K=32 B operands
+    Ul = join(u0l, u1l);
+  };
+
+  // ================================================================ consumer, sub-phase 2
+  // O = (q exp(G)) S0 + Bqk U into the staging buffer; then the state carry.
+  auto cons2 = [&](const Hand &hc) {
     uint4 Sh[DK / 32];
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s) {
       const f32x4 a = Sacc[2 * s], bb = Sacc[2 * s + 1];
       Sh[s] = join(pack_f16x4(a[0], a[1], a[2], a[3]), pack_f16x4(bb[0], bb[1], bb[2], bb[3]));
     }
-    // X_m = beta V - (beta k exp(G)) S0 for the two sub-blocks
-    f32x4 X[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t *ap = sm.kb + (SB * m + l16) * LDK + 4 * lg;
+      const uint16_t *ap = hc.qt + (SB * m + l16) * LDS_ + 4 * lg;
 #pragma unroll
       for (int s = 0; s < DK / 32; ++s) acc = mfma_f16(join(lds_u2(ap + 32 * s), lds_u2(ap + 32 * s + 16)), Sh[s], acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = SB * m + 4 * lg + i;
-        X[m][i] = sm.beta[r] * bf16_to_f32(sm.vt[r * LDV + wcol]) - acc[i];
-      }
-    }
-    // U0 = T00 X0;  U1 = T11 (X1 - A10 U0).  X and U enter as fp16 hi + lo.
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    uint2 u0h, u0l, u1h, u1l, xh, xl;
-    f32x4 U0, U1;
-    {
-      split_f16x4(X[0], xh, xl);
-      const uint2 t0 = lds_u2(sm.td + l16 * SB + 4 * lg);
-      U0 = mfma_f16k16(t0, xl, zero);
-      U0 = mfma_f16k16(t0, xh, U0);
-      split_f16x4(U0, u0h, u0l);
-      const uint2 nav = lds_u2(sm.na + l16 * LDN + 4 * lg);
-      f32x4 acc = X[1];
-      acc = mfma_f16k16(nav, u0l, acc);
-      acc = mfma_f16k16(nav, u0h, acc);
-      split_f16x4(acc, xh, xl);
-      const uint2 t1 = lds_u2(sm.td + (SB + l16) * SB + 4 * lg);
-      U1 = mfma_f16k16(t1, xl, zero);
-      U1 = mfma_f16k16(t1, xh, U1);
-      split_f16x4(U1, u1h, u1l);
-    }
-    // Token pair {4lg + 0..3, 16 + 4lg + 0..3} of U as K=32 B operands.
-    const uint4 Uh = join(u0h, u1h), Ul = join(u0l, u1l);
-
-    // O_m = (q exp(G)) S0 + Bqk U, staged (fp32) in the rkd region for coalesced stores.
-    float *ost = reinterpret_cast<float *>(sm.rkd);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t *ap = sm.qt + (SB * m + l16) * LDK + 4 * lg;
-#pragma unroll
-      for (int s = 0; s < DK / 32; ++s) acc = mfma_f16(join(lds_u2(ap + 32 * s), lds_u2(ap + 32 * s + 16)), Sh[s], acc);
-      const uint16_t *bp = sm.bq + (SB * m + l16) * LDB + 4 * lg;
+      const uint16_t *bp = hc.bq + (SB * m + l16) * LDB + 4 * lg;
       const uint4 bqv = join(lds_u2(bp), lds_u2(bp + 16));
       acc = mfma_f16(bqv, Ul, acc);
       acc = mfma_f16(bqv, Uh, acc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ost[(SB * m + 4 * lg + i) * LDO + wcol] = acc[i];
+      for (int i = 0; i < 4; ++i) sm.ost[(SB * m + 4 * lg + i) * LDO + wcol] = acc[i];
     }
-    // S_next = diag(exp(G_last)) S0 + (k exp(G_last - G))^T U
 #pragma unroll
     for (int t = 0; t < DK / 16; ++t) {
-      const float4 ec = *reinterpret_cast<const float4 *>(sm.ec + 16 * t + 4 * lg);
-      Sacc[t][0] *= ec.x; Sacc[t][1] *= ec.y; Sacc[t][2] *= ec.z; Sacc[t][3] *= ec.w;
-      const uint16_t *ap = sm.ket + (16 * t + l16) * LDT + 4 * lg;
+      const float4 e = *reinterpret_cast<const float4 *>(hc.ec + 16 * t + 4 * lg);
+      Sacc[t][0] *= e.x; Sacc[t][1] *= e.y; Sacc[t][2] *= e.z; Sacc[t][3] *= e.w;
+      const uint16_t *ap = hc.ket + ket_row(16 * t + l16) + 4 * lg;
       const uint4 kv = join(lds_u2(ap), lds_u2(ap + 16));
       Sacc[t] = mfma_f16(kv, Ul, Sacc[t]);
       Sacc[t] = mfma_f16(kv, Uh, Sacc[t]);
     }
-    sync_lds();
-    {   // coalesced output rows: token tid/8, 8 columns per thread
-      const int r = tid >> 3, c8 = (tid & 7) * 8;
-      const int t = c0 + r;
-      if (t < t_end) {
-        TOut *op = o + ((static_cast<size_t>(b) * T + t) * H + h) * DV + col0 + c8;
-        const float *sp = ost + r * LDO + c8;
-        const float4 x0 = reinterpret_cast<const float4 *>(sp)[0];
-        const float4 x1 = reinterpret_cast<const float4 *>(sp)[1];
-        if constexpr (sizeof(TOut) == 2) {
-          uint4 w;
-          w.x = pack_bf16x2(x0.x, x0.y); w.y = pack_bf16x2(x0.z, x0.w);
-          w.z = pack_bf16x2(x1.x, x1.y); w.w = pack_bf16x2(x1.z, x1.w);
-          *reinterpret_cast<uint4 *>(op) = w;
-        } else {
-          reinterpret_cast<float4 *>(op)[0] = x0;
-          reinterpret_cast<float4 *>(op)[1] = x1;
-        }
+  };
+
+  // ================================================================ consumer, sub-phase 3
+  // Coalesced output rows of the chunk starting at c0: token tid/8, 8 columns per thread.
+  auto cons3 = [&](int c0) {
+    const int r = tid >> 3, c8 = (tid & 7) * 8;
+    const int t = c0 + r;
+    if (t < t_end) {
+      TOut *op = o + ((row0 + t) * H + h) * DV + col0 + c8;
+      const float *sp = sm.ost + r * LDO + c8;
+      const float4 x0 = reinterpret_cast<const float4 *>(sp)[0];
+      const float4 x1 = reinterpret_cast<const float4 *>(sp)[1];
+      if constexpr (sizeof(TOut) == 2) {
+        uint4 w;
+        w.x = pack_bf16x2(x0.x, x0.y); w.y = pack_bf16x2(x0.z, x0.w);
+        w.z = pack_bf16x2(x1.x, x1.y); w.w = pack_bf16x2(x1.z, x1.w);
+        *reinterpret_cast<uint4 *>(op) = w;
+      } else {
+        reinterpret_cast<float4 *>(op)[0] = x0;
+        reinterpret_cast<float4 *>(op)[1] = x1;
       }
     }
+  };
+
+  if (nchunks > 0) {
+    load_raw(t_begin);
+    // step 0: producer work only
+    prod1(sm.hand[0], t_begin + min(1, nchunks - 1) * C);
     sync_lds();
+    prod2(sm.hand[0]);
+    sync_lds();
+    prod3(sm.hand[0]);
+    sync_lds();
+    // steady state: producer work on chunk `step`, consumer work on chunk `step - 1`
+    for (int step = 1; step < nchunks; ++step) {
+      Hand &hp = sm.hand[step & 1];
+      const Hand &hc = sm.hand[(step + 1) & 1];
+      const int c0 = t_begin + step * C;
+      prod1(hp, t_begin + min(step + 1, nchunks - 1) * C);
+      cons1(hc);
+      sync_lds();
+      prod2(hp);
+      cons2(hc);
+      sync_lds();
+      prod3(hp);
+      cons3(c0 - C);
+      sync_lds();
+    }
+    // last step: consumer work only
+    const Hand &hc = sm.hand[(nchunks + 1) & 1];
+    cons1(hc);
+    sync_lds();
+    cons2(hc);
+    sync_lds();
+    cons3(t_begin + (nchunks - 1) * C);
   }
 
 #pragma unroll
@@ -541,20 +575,25 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
       fin[slab + static_cast<size_t>(16 * t + 4 * lg + i) * DV + col0 + wcol] = Sacc[t][i];
 }
 
-template <typename TOut>
-hipError_t launch_typed(const Args &a, hipStream_t st) {
+template <typename TOut, bool HAS_INIT>
+hipError_t launch_init(const Args &a, hipStream_t st) {
   const int units = a.N * a.H;
   const unsigned grid = static_cast<unsigned>((units + 7) / 8) * 8 * NTILE;
   const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k),
                  *v = static_cast<const uint16_t *>(a.v);
   TOut *o = static_cast<TOut *>(a.o);
-  if (a.init)
-    hipLaunchKernelGGL((prefill_mfma_kernel<TOut, true>), dim3(grid), dim3(NT), 0, st, q, k, v, a.g,
-                       a.beta, a.init, a.state, a.cu, a.mask, o, a.T, a.H, units, a.scale, a.use_l2);
+  if (a.mask)
+    hipLaunchKernelGGL((prefill_mfma_kernel<TOut, HAS_INIT, true>), dim3(grid), dim3(NT), 0, st, q, k,
+                       v, a.g, a.beta, a.init, a.state, a.cu, a.mask, o, a.T, a.H, units, a.scale, a.use_l2);
   else
-    hipLaunchKernelGGL((prefill_mfma_kernel<TOut, false>), dim3(grid), dim3(NT), 0, st, q, k, v, a.g,
-                       a.beta, a.init, a.state, a.cu, a.mask, o, a.T, a.H, units, a.scale, a.use_l2);
+    hipLaunchKernelGGL((prefill_mfma_kernel<TOut, HAS_INIT, false>), dim3(grid), dim3(NT), 0, st, q, k,
+                       v, a.g, a.beta, a.init, a.state, a.cu, a.mask, o, a.T, a.H, units, a.scale, a.use_l2);
   return hipGetLastError();
+}
+
+template <typename TOut>
+hipError_t launch_typed(const Args &a, hipStream_t st) {
+  return a.init ? launch_init<TOut, true>(a, st) : launch_init<TOut, false>(a, st);
 }
 
 }  // namespace

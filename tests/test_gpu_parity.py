@@ -256,6 +256,8 @@ def test_config4_decode_B64():
     U.log("config 4: oracle state over 1000 prompt tokens for 64 rows")
     state = np.empty((B, H, D, D), np.float32)
     for r in range(B):
+        if r % 16 == 0:
+            U.log(f"config 4: prompt rows {r}..{min(r + 16, B) - 1}")
         pr = gi.decode_prompt(r, P)
         _, fs = cref.recurrence(pr.q, pr.k, pr.v, pr.g, pr.beta, in_dtype=pr.in_dtype)
         state[r] = fs[0].astype(np.float32)
