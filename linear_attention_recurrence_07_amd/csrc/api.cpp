@@ -128,7 +128,8 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const bool norm = y != nullptr;
   const int chunk = p->chunk;
-  const bool mfma = kda::prefill_mfma_supports(p->dk, p->dv, a.in_bf16) && (chunk == 0 || chunk == 64);
+  const bool mfma = kda::prefill_mfma_supports(p->dk, p->dv, a.in_bf16) && (chunk == 0 || chunk == 64) &&
+                    kda::prefill_mfma_fits(p->T, p->H);
   if (!mfma) {
     if (!kda::prefill_valu_supports(p->dk, p->dv))
       return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dk=%d dv=%d", p->dk, p->dv);

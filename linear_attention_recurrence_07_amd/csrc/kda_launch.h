@@ -37,5 +37,6 @@ hipError_t launch_gated_rmsnorm(const void *x, const void *gate, const float *w,
 bool recurrent_supports(int dk, int dv);
 bool prefill_valu_supports(int dk, int dv);
 bool prefill_mfma_supports(int dk, int dv, int in_bf16);
+bool prefill_mfma_fits(long long T, long long H);
 
 }  // namespace kda

@@ -14,17 +14,16 @@
 // This is the token-by-token recurrence regrouped; it equals it up to rounding.
 //
 // Work decomposition.  Value columns are independent in the recurrence, so a work-group
-// owns one (sequence, head, 64-column tile) with four waves, one per SIMD.  Every step
-// each wave does two independent jobs, one chunk apart, handed over through
-// double-buffered LDS:
-//   producer work on chunk c: load (registers, one chunk ahead), normalise q/k, form the
-//     per-channel decay factors and every MFMA operand of the chunk, and the key-side
-//     products A, Bqk and the inverses of the two diagonal 16x16 blocks of I + A;
-//   consumer work on chunk c-1: the wave owns 16 value columns, keeps its 128 x 16 slice
-//     of the fp32 state in accumulator registers for the whole sequence, and runs the
-//     state products (X -> U -> O, state carry) on MFMA.
-// Producer work is mostly vector-ALU and consumer work mostly matrix-core; placing both in
-// the same straight-line code lets the MFMA pipeline run under the vector work.  Three
+// owns one (sequence, head, 64-column tile), with eight waves, two per SIMD.  Every step
+// handles two chunks, one apart, handed over through double-buffered LDS:
+//   producer work on chunk c (all eight waves, 4 tokens x 2 channels per thread): unpack
+//     the inputs loaded one chunk ahead, normalise q/k, form the per-channel decay factors
+//     and every MFMA operand; then (waves 4-7) the key-side products A, Bqk and the
+//     inverses of the two diagonal 16x16 blocks of I + A;
+//   consumer work on chunk c-1 (waves 0-3): each wave owns 16 value columns, keeps its
+//     128 x 16 slice of the fp32 state in accumulator registers for the whole sequence,
+//     and runs the state products (X -> U -> O, state carry) on MFMA.
+// Two waves per SIMD hide each other's LDS, MFMA and barrier latencies.  Three
 // work-group barriers separate the sub-phases of a step.
 //
 // Decay factoring.  exp(G_s - G_j) is split into a row and a column factor around a
@@ -58,11 +57,11 @@ constexpr int C = 32;             // tokens per chunk
 constexpr int SB = 16;            // tokens per sub-block
 constexpr int DVT = 64;           // value columns per work-group
 constexpr int NTILE = DV / DVT;   // work-groups per (sequence, head)
-constexpr int NW = DVT / 16;      // waves; each owns 16 value columns
-constexpr int NT = NW * 64;       // 256 threads
-constexpr int TPG = 4;            // tokens per producer thread
-constexpr int NG = C / TPG;       // 8 token groups, four per sub-block
-static_assert(NW == 4 && NG == 8, "the thread mappings assume these sizes");
+constexpr int NCW = DVT / 16;     // consumer waves; each owns 16 value columns
+constexpr int NW = 8;             // waves per work-group
+constexpr int NT = NW * 64;       // 512 threads
+constexpr int TPW = C / NW;       // tokens per producer wave (4)
+static_assert(NCW == 4 && TPW == 4, "the thread mappings assume these sizes");
 
 // LDS row strides in elements.
 constexpr int LDS_ = DK + 4;      // fp16 [token][channel] state operands, 8-byte reads
@@ -73,9 +72,9 @@ constexpr int LDN = SB + 8;       // 16x16 -A(1,0)
 constexpr int LDA = SB * SB + 8;  // fp32 16x16 diagonal blocks of A, transposed
 constexpr int LDO = DVT + 4;      // fp32 output staging
 // (k exp(G_last - G))^T: channel rows of 32 tokens, with 4 extra elements after every
-// 4 rows so the producers' transposed 8-byte writes spread over the banks.
-__device__ __forceinline__ int ket_row(int ch) { return ch * C + (ch >> 2) * 4; }
-constexpr int KET_SIZE = DK * C + (DK / 4) * 4;
+// 2 rows so the transposed 8-byte writes spread over the banks.
+__device__ __forceinline__ int ket_row(int ch) { return ch * C + (ch >> 1) * 4; }
+constexpr int KET_SIZE = DK * C + (DK / 2) * 4;
 
 // Data handed from the producer work on chunk c to the consumer work on it, one step later.
 struct Hand {
@@ -91,7 +90,7 @@ struct Hand {
 };
 struct Smem {
   Hand hand[2];
-  // producer-internal (key-side operands)
+  // key-side operands (producer)
   uint16_t rkd[C * LDK];       // bf16 k exp(G - G_mid(block))
   uint16_t rqd_hi[C * LDK];    // bf16 q exp(G - G_mid(block)), hi part
   uint16_t rqd_lo[C * LDK];    //                                  lo part
@@ -101,7 +100,7 @@ struct Smem {
   uint16_t rq1[C * LDK];       // fp16 q exp(G - G_15)   (rows of block 1 are used)
   uint16_t ck0[C * LDK];       // fp16 k exp(G_15 - G)   (rows of block 0 are used)
   float at[2 * LDA];           // A_aa transposed: at[a][j][s] = A[16a+s][16a+j]
-  float gtot[NG * DK];         // decay product over each 4-token group
+  float gtot[NW * DK];         // decay product over each 4-token group
   // consumer side
   float ost[C * LDO];          // fp32 output staging
 };
@@ -130,10 +129,29 @@ __device__ __forceinline__ void split_f16x4(f32x4 x, uint2 &hi, uint2 &lo) {
   lo = pack_f16x4(x[0] - static_cast<float>(h[0]), x[1] - static_cast<float>(h[1]),
                   x[2] - static_cast<float>(h[2]), x[3] - static_cast<float>(h[3]));
 }
-// x = hi + lo with both parts bf16 (about 16 significant bits together).
-__device__ __forceinline__ void split_bf16x4(const float *x, uint2 &hi, uint2 &lo) {
-  hi = pack_bf16x4(x[0], x[1], x[2], x[3]);
-  lo = pack_bf16x4(x[0] - lo_bf16(hi.x), x[1] - hi_bf16(hi.x), x[2] - lo_bf16(hi.y), x[3] - hi_bf16(hi.y));
+// (a, b) = hi + lo with both parts bf16 (about 16 significant bits together).
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - lo_bf16(hi), b - hi_bf16(hi));
+}
+
+// Sum over the 64 lanes of a wave: DPP adds within rows of 16, a swizzle across the two
+// rows of each half, a lane swap across the halves.
+__device__ __forceinline__ float wave_sum(float x) {
+  const int r8 = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false);  // row_ror:8
+  x += __builtin_bit_cast(float, r8);
+  const int r4 = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false);  // row_ror:4
+  x += __builtin_bit_cast(float, r4);
+  const int q2 = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
+  x += __builtin_bit_cast(float, q2);
+  const int q1 = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+  x += __builtin_bit_cast(float, q1);
+  x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));    // lane ^ 16
+  // the swap leaves lanes 32..63 of x in element 1's lanes 0..31 and lanes 0..31 in element 0's lanes 32..63
+  const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                                    false, false);
+  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return x + __builtin_bit_cast(float, lane < 32 ? sw[1] : sw[0]);
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
@@ -178,10 +196,10 @@ __device__ __forceinline__ f32x4 off_block(const uint16_t *rows, const Smem &sm,
 }
 
 struct Raw {   // one chunk's inputs for one thread, as loaded
-  uint2 k[TPG], q[TPG];
-  float4 g[TPG];
-  float beta[TPG];
-  uint4 v;
+  uint32_t k[TPW], q[TPW];     // 2 bf16 channels per token
+  float2 g[TPW];
+  float beta[TPW];
+  uint2 v;                     // 4 bf16 values of the value tile
 };
 
 template <typename TOut, bool HAS_INIT, bool HAS_MASK>
@@ -216,51 +234,58 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
   const int col0 = tile * DVT;
   const size_t slab = (static_cast<size_t>(n) * H + h) * DK * DV;
   const int nchunks = (t_end - t_begin + C - 1) / C;
-  const size_t tok_stride = static_cast<size_t>(H) * DK;      // elements between tokens (q, k, g)
-  const size_t row0 = static_cast<size_t>(b) * T;             // first token row of this batch row
+  const int tok_stride = H * DK;                               // elements between tokens (q, k, g)
+  const size_t row0 = static_cast<size_t>(b) * T;              // first token row of this batch row
+  const uint16_t *kp = k + row0 * tok_stride + h * DK + 2 * lane;
+  const uint16_t *qp = q + row0 * tok_stride + h * DK + 2 * lane;
+  const float *gp = g + row0 * tok_stride + h * DK + 2 * lane;
+  const float *bp = beta + row0 * H + h;
+  const uint16_t *vp = v + row0 * H * DV + h * DV + col0 + (tid & 15) * 4;
+  const uint8_t *mp = HAS_MASK ? mask + row0 : nullptr;
 
   for (int e = tid; e < C * LDB; e += NT) sm.hand[0].bq[e] = sm.hand[1].bq[e] = 0;
 
   // ---------------------------------------------------------------- producer state
-  const int cg = tid & 31, tg = tid >> 5;         // 4 channels x 4 tokens per thread
-  const int blk = tg >> 2;                        // wave-uniform sub-block of this thread
+  // thread: tokens 4*wave .. 4*wave+3 of the chunk, channels 2*lane, 2*lane+1
+  const int blk = wave >> 2;                     // sub-block of this wave's tokens
+  const int gi = wave & 3;                       // group within the sub-block
   Raw raw;
   // Loads are unconditional (clamped to the sequence's last token) and masked with
   // selects, so the steady-state loop stays one basic block per sub-phase.
   auto load_raw = [&](int c0) {
 #pragma unroll
-    for (int j = 0; j < TPG; ++j) {
-      const int t = c0 + TPG * tg + j;
+    for (int j = 0; j < TPW; ++j) {
+      const int t = c0 + TPW * wave + j;
       const int tc = min(t, t_end - 1);
       bool valid = t < t_end;
-      if constexpr (HAS_MASK) valid = valid && mask[row0 + tc] != 0;
-      const size_t off = (row0 + tc) * tok_stride + static_cast<size_t>(h) * DK + 4 * cg;
-      const uint2 kk = *reinterpret_cast<const uint2 *>(k + off);
-      const uint2 qq = *reinterpret_cast<const uint2 *>(q + off);
-      const float4 gg = *reinterpret_cast<const float4 *>(g + off);
-      const float bb = beta[(row0 + tc) * H + h];
+      if constexpr (HAS_MASK) valid = valid && mp[tc] != 0;
+      const int off = tc * tok_stride;
+      const uint32_t kk = *reinterpret_cast<const uint32_t *>(kp + off);
+      const uint32_t qq = *reinterpret_cast<const uint32_t *>(qp + off);
+      const float2 gg = *reinterpret_cast<const float2 *>(gp + off);
+      const float bb = bp[tc * H];
       // padding and tokens past the sequence act as no-ops
-      raw.k[j] = valid ? kk : make_uint2(0, 0);
-      raw.q[j] = valid ? qq : make_uint2(0, 0);
-      raw.g[j] = valid ? gg : make_float4(0.f, 0.f, 0.f, 0.f);
+      raw.k[j] = valid ? kk : 0u;
+      raw.q[j] = valid ? qq : 0u;
+      raw.g[j] = valid ? gg : make_float2(0.f, 0.f);
       raw.beta[j] = valid ? bb : 0.f;
     }
-    // value tile (32 tokens x 64 columns): token tid/8, 8 columns per thread
-    const int t = c0 + (tid >> 3);
+    // value tile (32 tokens x 64 columns): token tid/16, 4 columns per thread
+    const int t = c0 + (tid >> 4);
     const int tc = min(t, t_end - 1);
     bool valid = t < t_end;
-    if constexpr (HAS_MASK) valid = valid && mask[row0 + tc] != 0;
-    const uint4 vv = *reinterpret_cast<const uint4 *>(v + ((row0 + tc) * H + h) * DV + col0 + (tid & 7) * 8);
-    raw.v = valid ? vv : make_uint4(0, 0, 0, 0);
+    if constexpr (HAS_MASK) valid = valid && mp[tc] != 0;
+    const uint2 vv = *reinterpret_cast<const uint2 *>(vp + static_cast<size_t>(tc) * H * DV);
+    raw.v = valid ? vv : make_uint2(0, 0);
   };
-  float kx[TPG][4], qx[TPG][4], fw[TPG][4], bw[TPG][4];
+  float kx[TPW][2], qx[TPW][2], fw[TPW][2], bw[TPW][2];
 
-  // ---------------------------------------------------------------- consumer state
-  const int wcol = 16 * wave + l16;              // this lane's value column in the tile
+  // ---------------------------------------------------------------- consumer state (waves 0-3)
+  const int wcol = 16 * (wave & 3) + l16;        // this lane's value column in the tile
   f32x4 Sacc[DK / 16];                           // Sacc[t][i] = S[16t + 4lg + i][col0 + wcol]
 #pragma unroll
   for (int t = 0; t < DK / 16; ++t) Sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (HAS_INIT) {
+  if (HAS_INIT && wave < NCW) {
 #pragma unroll
     for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
@@ -270,70 +295,61 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
   uint4 Uh = make_uint4(0, 0, 0, 0), Ul = Uh;
 
   // ================================================================ producer, sub-phase 1
-  // Unpack chunk c0's inputs, start loading chunk c_next, normalise q/k, decay factors.
+  // Unpack the chunk's inputs, start loading chunk c_next, normalise q/k, decay factors.
   auto prod1 = [&](Hand &hp, int c_next) {
 #pragma unroll
-    for (int j = 0; j < TPG; ++j) {
-      kx[j][0] = lo_bf16(raw.k[j].x); kx[j][1] = hi_bf16(raw.k[j].x);
-      kx[j][2] = lo_bf16(raw.k[j].y); kx[j][3] = hi_bf16(raw.k[j].y);
-      qx[j][0] = lo_bf16(raw.q[j].x); qx[j][1] = hi_bf16(raw.q[j].x);
-      qx[j][2] = lo_bf16(raw.q[j].y); qx[j][3] = hi_bf16(raw.q[j].y);
-      fw[j][0] = raw.g[j].x; fw[j][1] = raw.g[j].y; fw[j][2] = raw.g[j].z; fw[j][3] = raw.g[j].w;
-      hp.beta[TPG * tg + j] = raw.beta[j];          // the same value from all 32 lanes
+    for (int j = 0; j < TPW; ++j) {
+      kx[j][0] = lo_bf16(raw.k[j]); kx[j][1] = hi_bf16(raw.k[j]);
+      qx[j][0] = lo_bf16(raw.q[j]); qx[j][1] = hi_bf16(raw.q[j]);
+      fw[j][0] = raw.g[j].x; fw[j][1] = raw.g[j].y;
+      hp.beta[TPW * wave + j] = raw.beta[j];          // the same value from all lanes
     }
-    *reinterpret_cast<uint4 *>(hp.vt + (tid >> 3) * LDV + (tid & 7) * 8) = raw.v;
+    *reinterpret_cast<uint2 *>(hp.vt + (tid >> 4) * LDV + (tid & 15) * 4) = raw.v;
     load_raw(c_next);
-    // q/k L2 norms over the 128 channels (32 lanes x 4 channels)
+    // q/k L2 norms over the 128 channels (64 lanes x 2 channels)
 #pragma unroll
-    for (int j = 0; j < TPG; ++j) {
-      float sk = kx[j][0] * kx[j][0] + kx[j][1] * kx[j][1] + kx[j][2] * kx[j][2] + kx[j][3] * kx[j][3];
-      float sq = qx[j][0] * qx[j][0] + qx[j][1] * qx[j][1] + qx[j][2] * qx[j][2] + qx[j][3] * qx[j][3];
-      sk = lane_sum<31>(sk);
-      sq = lane_sum<31>(sq);
+    for (int j = 0; j < TPW; ++j) {
+      const float sk = wave_sum(kx[j][0] * kx[j][0] + kx[j][1] * kx[j][1]);
+      const float sq = wave_sum(qx[j][0] * qx[j][0] + qx[j][1] * qx[j][1]);
       const float kn = use_l2 ? rsqrtf(sk + kL2Eps) : 1.f;
       const float qn = (use_l2 ? rsqrtf(sq + kL2Eps) : 1.f) * scale;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        kx[j][c] *= kn;
-        qx[j][c] *= qn;
-      }
+      kx[j][0] *= kn; kx[j][1] *= kn;
+      qx[j][0] *= qn; qx[j][1] *= qn;
     }
     // fw[j] = prod_{i<=j} e_i (inclusive), bw[j] = prod_{j<i<4} e_i (exclusive)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float e[TPG];
+    for (int c = 0; c < 2; ++c) {
+      float e[TPW];
 #pragma unroll
-      for (int j = 0; j < TPG; ++j) e[j] = fast_exp2(fw[j][c] * kLog2e);
+      for (int j = 0; j < TPW; ++j) e[j] = fast_exp2(fw[j][c] * kLog2e);
       float run = 1.f;
 #pragma unroll
-      for (int j = 0; j < TPG; ++j) {
+      for (int j = 0; j < TPW; ++j) {
         run *= e[j];
         fw[j][c] = run;
       }
       run = 1.f;
 #pragma unroll
-      for (int j = TPG - 1; j >= 0; --j) {
+      for (int j = TPW - 1; j >= 0; --j) {
         bw[j][c] = run;
         run *= e[j];
       }
     }
-    *reinterpret_cast<float4 *>(sm.gtot + tg * DK + 4 * cg) =
-        make_float4(fw[TPG - 1][0], fw[TPG - 1][1], fw[TPG - 1][2], fw[TPG - 1][3]);
+    *reinterpret_cast<float2 *>(sm.gtot + wave * DK + 2 * lane) = make_float2(fw[TPW - 1][0], fw[TPW - 1][1]);
   };
 
   // ================================================================ producer, sub-phase 2
   // Combine the group decay products and write every MFMA operand of the chunk.
   auto prod2 = [&](Hand &hp) {
-    float gt[NG][4];
+    float gt[NW][2];
 #pragma unroll
-    for (int m = 0; m < NG; ++m) {
-      const float4 x = *reinterpret_cast<const float4 *>(sm.gtot + m * DK + 4 * cg);
-      gt[m][0] = x.x; gt[m][1] = x.y; gt[m][2] = x.z; gt[m][3] = x.w;
+    for (int m = 0; m < NW; ++m) {
+      const float2 x = *reinterpret_cast<const float2 *>(sm.gtot + m * DK + 2 * lane);
+      gt[m][0] = x.x; gt[m][1] = x.y;
     }
-    const int gi = tg & 3;                         // group within the sub-block
-    float e3m[4], e4m[4], fkb[4], fke[4], ih1[4], ih2[4], ec[4];
+    float e3m[2], e4m[2], fkb[2], fke[2], ih1[2], ih2[2], ec[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2; ++c) {
       // this block's group products, selected with constant register indices
       const float b0 = blk ? gt[4][c] : gt[0][c], b1 = blk ? gt[5][c] : gt[1][c];
       const float b2 = blk ? gt[6][c] : gt[2][c], b3 = blk ? gt[7][c] : gt[3][c];
@@ -349,11 +365,11 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
       ec[c] = d0 * d1;
     }
 #pragma unroll
-    for (int j = 0; j < TPG; ++j) {
-      const int r = TPG * tg + j;
-      float k3[4], q3[4], k4[4], rkd[4], rqd[4], ckd[4], kb[4], qt[4];
+    for (int j = 0; j < TPW; ++j) {
+      const int r = TPW * wave + j;
+      float k3[2], q3[2], k4[2], rkd[2], rqd[2], ckd[2], kb[2], qt[2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < 2; ++c) {
         const float e3 = e3m[c] * fw[j][c];       // exp(G_r - G_block_start)
         const float e4 = bw[j][c] * e4m[c];       // exp(G_block_end - G_r)
         k3[c] = kx[j][c] * e3;
@@ -366,33 +382,33 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
         qt[c] = q3[c] * fkb[c];
         kx[j][c] = k4[c] * fke[c];                // k exp(G_last - G_r), for the transpose
       }
-      *reinterpret_cast<uint2 *>(hp.kb + r * LDS_ + 4 * cg) = pack_f16x4(kb[0], kb[1], kb[2], kb[3]);
-      *reinterpret_cast<uint2 *>(hp.qt + r * LDS_ + 4 * cg) = pack_f16x4(qt[0], qt[1], qt[2], qt[3]);
-      const int o4 = r * LDK + 4 * cg;
-      *reinterpret_cast<uint2 *>(sm.rkd + o4) = pack_bf16x4(rkd[0], rkd[1], rkd[2], rkd[3]);
-      uint2 hi, lo;
-      split_bf16x4(rqd, hi, lo);
-      *reinterpret_cast<uint2 *>(sm.rqd_hi + o4) = hi;
-      *reinterpret_cast<uint2 *>(sm.rqd_lo + o4) = lo;
-      split_bf16x4(ckd, hi, lo);
-      *reinterpret_cast<uint2 *>(sm.ckd_hi + o4) = hi;
-      *reinterpret_cast<uint2 *>(sm.ckd_lo + o4) = lo;
+      *reinterpret_cast<uint32_t *>(hp.kb + r * LDS_ + 2 * lane) = pack_f16x2(kb[0], kb[1]);
+      *reinterpret_cast<uint32_t *>(hp.qt + r * LDS_ + 2 * lane) = pack_f16x2(qt[0], qt[1]);
+      const int o2 = r * LDK + 2 * lane;
+      *reinterpret_cast<uint32_t *>(sm.rkd + o2) = pack_bf16x2(rkd[0], rkd[1]);
+      uint32_t hi, lo;
+      split_bf16x2(rqd[0], rqd[1], hi, lo);
+      *reinterpret_cast<uint32_t *>(sm.rqd_hi + o2) = hi;
+      *reinterpret_cast<uint32_t *>(sm.rqd_lo + o2) = lo;
+      split_bf16x2(ckd[0], ckd[1], hi, lo);
+      *reinterpret_cast<uint32_t *>(sm.ckd_hi + o2) = hi;
+      *reinterpret_cast<uint32_t *>(sm.ckd_lo + o2) = lo;
       // off-diagonal factors around token 15 (rows of block 1 / columns of block 0 are read)
-      *reinterpret_cast<uint2 *>(sm.rk1 + o4) = pack_f16x4(k3[0], k3[1], k3[2], k3[3]);
-      *reinterpret_cast<uint2 *>(sm.rq1 + o4) = pack_f16x4(q3[0], q3[1], q3[2], q3[3]);
-      *reinterpret_cast<uint2 *>(sm.ck0 + o4) = pack_f16x4(k4[0], k4[1], k4[2], k4[3]);
+      *reinterpret_cast<uint32_t *>(sm.rk1 + o2) = pack_f16x2(k3[0], k3[1]);
+      *reinterpret_cast<uint32_t *>(sm.rq1 + o2) = pack_f16x2(q3[0], q3[1]);
+      *reinterpret_cast<uint32_t *>(sm.ck0 + o2) = pack_f16x2(k4[0], k4[1]);
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      *reinterpret_cast<uint2 *>(hp.ket + ket_row(4 * cg + c) + TPG * tg) =
+    for (int c = 0; c < 2; ++c)
+      *reinterpret_cast<uint2 *>(hp.ket + ket_row(2 * lane + c) + TPW * wave) =
           pack_f16x4(kx[0][c], kx[1][c], kx[2][c], kx[3][c]);
-    *reinterpret_cast<float4 *>(hp.ec + 4 * cg) = make_float4(ec[0], ec[1], ec[2], ec[3]);
+    if (wave == 0) *reinterpret_cast<float2 *>(hp.ec + 2 * lane) = make_float2(ec[0], ec[1]);
   };
 
   // ================================================================ producer, sub-phase 3
-  // Key-side products: A and Bqk blocks, the inverses of the diagonal blocks of I + A.
+  // Key-side products (waves 4-7): A and Bqk blocks, inverses of the diagonal blocks of I + A.
   auto prod3 = [&](Hand &hp) {
-    if (wave == 0) {
+    if (wave == 4) {
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const f32x4 acc = a_diag(sm, a, l16, lg);
@@ -418,7 +434,7 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
       }
 #pragma unroll
       for (int r = 0; r < SB; ++r) hp.td[(a * SB + r) * SB + c] = f16_bits(tc[r]);
-    } else if (wave == 1) {
+    } else if (wave == 5) {
       const f32x4 accA = off_block(sm.rk1 + SB * LDK, sm, l16, lg);
       const f32x4 accB = off_block(sm.rq1 + SB * LDK, sm, l16, lg);
 #pragma unroll
@@ -427,8 +443,8 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
         hp.na[sl * LDN + l16] = f16_bits(-hp.beta[SB + sl] * accA[i]);
         hp.bq[(SB + sl) * LDB + l16] = f16_bits(accB[i]);
       }
-    } else {
-      const int a = wave - 2;
+    } else if (wave >= 6) {
+      const int a = wave - 6;
       const f32x4 acc = bqk_diag(sm, a, l16, lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -495,8 +511,8 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
       const uint16_t *ap = hc.qt + (SB * m + l16) * LDS_ + 4 * lg;
 #pragma unroll
       for (int s = 0; s < DK / 32; ++s) acc = mfma_f16(join(lds_u2(ap + 32 * s), lds_u2(ap + 32 * s + 16)), Sh[s], acc);
-      const uint16_t *bp = hc.bq + (SB * m + l16) * LDB + 4 * lg;
-      const uint4 bqv = join(lds_u2(bp), lds_u2(bp + 16));
+      const uint16_t *bqp = hc.bq + (SB * m + l16) * LDB + 4 * lg;
+      const uint4 bqv = join(lds_u2(bqp), lds_u2(bqp + 16));
       acc = mfma_f16(bqv, Ul, acc);
       acc = mfma_f16(bqv, Uh, acc);
 #pragma unroll
@@ -514,7 +530,7 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
   };
 
   // ================================================================ consumer, sub-phase 3
-  // Coalesced output rows of the chunk starting at c0: token tid/8, 8 columns per thread.
+  // Coalesced output rows of the chunk starting at c0 (waves 0-3): token tid/8, 8 columns.
   auto cons3 = [&](int c0) {
     const int r = tid >> 3, c8 = (tid & 7) * 8;
     const int t = c0 + r;
@@ -535,6 +551,7 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
     }
   };
 
+  const bool consumer = wave < NCW;
   if (nchunks > 0) {
     load_raw(t_begin);
     // step 0: producer work only
@@ -550,29 +567,31 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
       const Hand &hc = sm.hand[(step + 1) & 1];
       const int c0 = t_begin + step * C;
       prod1(hp, t_begin + min(step + 1, nchunks - 1) * C);
-      cons1(hc);
+      if (consumer) cons1(hc);
       sync_lds();
       prod2(hp);
-      cons2(hc);
+      if (consumer) cons2(hc);
       sync_lds();
-      prod3(hp);
-      cons3(c0 - C);
+      if (consumer) cons3(c0 - C);
+      else prod3(hp);
       sync_lds();
     }
     // last step: consumer work only
     const Hand &hc = sm.hand[(nchunks + 1) & 1];
-    cons1(hc);
+    if (consumer) cons1(hc);
     sync_lds();
-    cons2(hc);
+    if (consumer) cons2(hc);
     sync_lds();
-    cons3(t_begin + (nchunks - 1) * C);
+    if (consumer) cons3(t_begin + (nchunks - 1) * C);
   }
 
+  if (consumer) {
 #pragma unroll
-  for (int t = 0; t < DK / 16; ++t)
+    for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      fin[slab + static_cast<size_t>(16 * t + 4 * lg + i) * DV + col0 + wcol] = Sacc[t][i];
+      for (int i = 0; i < 4; ++i)
+        fin[slab + static_cast<size_t>(16 * t + 4 * lg + i) * DV + col0 + wcol] = Sacc[t][i];
+  }
 }
 
 template <typename TOut, bool HAS_INIT>
@@ -599,6 +618,9 @@ hipError_t launch_typed(const Args &a, hipStream_t st) {
 }  // namespace
 
 bool prefill_mfma_supports(int dk, int dv, int in_bf16) { return in_bf16 && dk == DK && dv == DV; }
+
+// Offsets of tokens within one batch row are 32-bit: T * H * 128 must stay below 2^31.
+bool prefill_mfma_fits(long long T, long long H) { return T * H * DK < (1LL << 31); }
 
 hipError_t launch_prefill_mfma(const Args &a, hipStream_t st) {
   return a.out_bf16 ? launch_typed<uint16_t>(a, st) : launch_typed<float>(a, st);
