@@ -96,9 +96,8 @@ struct Smem {
   uint16_t rqd_lo[C * LDK];    //                                  lo part
   uint16_t ckd_hi[C * LDK];    // bf16 k exp(G_mid(block) - G), hi part
   uint16_t ckd_lo[C * LDK];    //                                  lo part
-  uint16_t rk1[C * LDK];       // fp16 k exp(G - G_15)   (rows of block 1 are used)
-  uint16_t rq1[C * LDK];       // fp16 q exp(G - G_15)   (rows of block 1 are used)
-  uint16_t ck0[C * LDK];       // fp16 k exp(G_15 - G)   (rows of block 0 are used)
+  uint16_t kof[C * LDK];       // fp16 k exp(G_15 - G) on block 0 rows, k exp(G - G_15) on block 1 rows
+  uint16_t rq1[SB * LDK];      // fp16 q exp(G - G_15) of block 1 rows
   float at[2 * LDA];           // A_aa transposed: at[a][j][s] = A[16a+s][16a+j]
   float gtot[NW * DK];         // decay product over each 4-token group
   // consumer side
@@ -135,9 +134,8 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t &hi, uin
   lo = pack_bf16x2(a - lo_bf16(hi), b - hi_bf16(hi));
 }
 
-// Sum over the 64 lanes of a wave: DPP adds within rows of 16, a swizzle across the two
-// rows of each half, a lane swap across the halves.
-__device__ __forceinline__ float wave_sum(float x) {
+// Sum over the 16 lanes of each row of a wave (DPP rotations and quad permutations).
+__device__ __forceinline__ float row_sum16(float x) {
   const int r8 = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false);  // row_ror:8
   x += __builtin_bit_cast(float, r8);
   const int r4 = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false);  // row_ror:4
@@ -145,13 +143,38 @@ __device__ __forceinline__ float wave_sum(float x) {
   const int q2 = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
   x += __builtin_bit_cast(float, q2);
   const int q1 = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
-  x += __builtin_bit_cast(float, q1);
-  x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));    // lane ^ 16
-  // the swap leaves lanes 32..63 of x in element 1's lanes 0..31 and lanes 0..31 in element 0's lanes 32..63
-  const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
-                                                    false, false);
-  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  return x + __builtin_bit_cast(float, lane < 32 ? sw[1] : sw[0]);
+  return x + __builtin_bit_cast(float, q1);
+}
+// Sum of the two outputs of a lane swap.  The empty asm keeps the optimiser from folding
+// the two outputs into one (it rewrites out0 + out1 as out0 + out0 otherwise).
+__device__ __forceinline__ float swap_sum(uint32_t r0, uint32_t r1) {
+  __asm__("" : "+v"(r1));
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+// a + b after swapping lanes 32-63 of a with lanes 0-31 of b: lanes 0-31 hold a folded
+// over the two halves of the wave, lanes 32-63 hold b folded.
+__device__ __forceinline__ float fold32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, a), __builtin_bit_cast(int, b),
+                                                   false, false);
+  return swap_sum(r[0], r[1]);
+}
+// The same with rows of 16: rows 0 and 2 hold a folded over row pairs, rows 1 and 3 b.
+__device__ __forceinline__ float fold16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, a), __builtin_bit_cast(int, b),
+                                                   false, false);
+  return swap_sum(r[0], r[1]);
+}
+// Sums over the 64 lanes of eight values at once, by halving the lane range per value
+// each swap.  On return the sum of v[m] is in every lane of row m >> 1 of x0 (m even)
+// or x1 (m odd).
+__device__ __forceinline__ void wave_sum8(const float (&v)[8], float &x0, float &x1) {
+  const float w0 = fold32(v[0], v[4]), w1 = fold32(v[1], v[5]);
+  const float w2 = fold32(v[2], v[6]), w3 = fold32(v[3], v[7]);
+  x0 = row_sum16(fold16(w0, w2));
+  x1 = row_sum16(fold16(w1, w3));
+}
+__device__ __forceinline__ float readlane(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
@@ -188,7 +211,7 @@ __device__ __forceinline__ f32x4 bqk_diag(const Smem &sm, int a, int l16, int lg
 }
 __device__ __forceinline__ f32x4 off_block(const uint16_t *rows, const Smem &sm, int l16, int lg) {
   const uint16_t *rp = rows + l16 * LDK + 8 * lg;
-  const uint16_t *cp = sm.ck0 + l16 * LDK + 8 * lg;
+  const uint16_t *cp = sm.kof + l16 * LDK + 8 * lg;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < DK / 32; ++s) acc = mfma_f16(lds_u4(rp + 32 * s), lds_u4(cp + 32 * s), acc);
@@ -306,13 +329,23 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
     }
     *reinterpret_cast<uint2 *>(hp.vt + (tid >> 4) * LDV + (tid & 15) * 4) = raw.v;
     load_raw(c_next);
-    // q/k L2 norms over the 128 channels (64 lanes x 2 channels)
+    // q/k L2 norms over the 128 channels (64 lanes x 2 channels), all eight at once
+    float ss[2 * TPW];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
-      const float sk = wave_sum(kx[j][0] * kx[j][0] + kx[j][1] * kx[j][1]);
-      const float sq = wave_sum(qx[j][0] * qx[j][0] + qx[j][1] * qx[j][1]);
-      const float kn = use_l2 ? rsqrtf(sk + kL2Eps) : 1.f;
-      const float qn = (use_l2 ? rsqrtf(sq + kL2Eps) : 1.f) * scale;
+      ss[j] = kx[j][0] * kx[j][0] + kx[j][1] * kx[j][1];
+      ss[TPW + j] = qx[j][0] * qx[j][0] + qx[j][1] * qx[j][1];
+    }
+    float x0, x1;
+    wave_sum8(ss, x0, x1);
+    // rows 0-1 of x0/x1 hold key sums, rows 2-3 query sums
+    const float qs = lane >= 32 ? scale : 1.f;
+    const float n0 = (use_l2 ? rsqrtf(x0 + kL2Eps) : 1.f) * qs;
+    const float n1 = (use_l2 ? rsqrtf(x1 + kL2Eps) : 1.f) * qs;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const float kn = readlane(j & 1 ? n1 : n0, 16 * (j >> 1));
+      const float qn = readlane(j & 1 ? n1 : n0, 32 + 16 * (j >> 1));
       kx[j][0] *= kn; kx[j][1] *= kn;
       qx[j][0] *= qn; qx[j][1] *= qn;
     }
@@ -394,9 +427,9 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
       *reinterpret_cast<uint32_t *>(sm.ckd_hi + o2) = hi;
       *reinterpret_cast<uint32_t *>(sm.ckd_lo + o2) = lo;
       // off-diagonal factors around token 15 (rows of block 1 / columns of block 0 are read)
-      *reinterpret_cast<uint32_t *>(sm.rk1 + o2) = pack_f16x2(k3[0], k3[1]);
-      *reinterpret_cast<uint32_t *>(sm.rq1 + o2) = pack_f16x2(q3[0], q3[1]);
-      *reinterpret_cast<uint32_t *>(sm.ck0 + o2) = pack_f16x2(k4[0], k4[1]);
+      *reinterpret_cast<uint32_t *>(sm.kof + o2) =
+          blk ? pack_f16x2(k3[0], k3[1]) : pack_f16x2(k4[0], k4[1]);
+      if (blk) *reinterpret_cast<uint32_t *>(sm.rq1 + o2 - SB * LDK) = pack_f16x2(q3[0], q3[1]);
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -435,8 +468,8 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
 #pragma unroll
       for (int r = 0; r < SB; ++r) hp.td[(a * SB + r) * SB + c] = f16_bits(tc[r]);
     } else if (wave == 5) {
-      const f32x4 accA = off_block(sm.rk1 + SB * LDK, sm, l16, lg);
-      const f32x4 accB = off_block(sm.rq1 + SB * LDK, sm, l16, lg);
+      const f32x4 accA = off_block(sm.kof + SB * LDK, sm, l16, lg);
+      const f32x4 accB = off_block(sm.rq1, sm, l16, lg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int sl = 4 * lg + i;
@@ -457,6 +490,7 @@ prefill_mfma_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__
   // ================================================================ consumer, sub-phase 1
   // X = beta (V - (k exp(G)) S0);  U0 = T00 X0;  U1 = T11 (X1 - A10 U0).
   auto cons1 = [&](const Hand &hc) {
+    __asm__ volatile("" ::: "memory");   // not to be speculated onto producer-only waves
     uint4 Sh[DK / 32];   // S0 (fp16); K step s covers channels {32s+4lg+0..3, 32s+16+4lg+0..3}
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s) {
