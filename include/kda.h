@@ -65,7 +65,8 @@ typedef struct {
   int32_t dk;            /* key_dim   (16, 32, 64 or 128)                                  */
   int32_t dv;            /* value_dim (== dk in this build)                                */
   int32_t num_seqs;      /* sequences: len(cu_seqlens)-1 with cu_seqlens, else ignored (=B) */
-  int32_t chunk;         /* prefill chunk length: 0 = default; 64 (bf16 MFMA path) or 16   */
+  int32_t chunk;         /* prefill chunk length: 0 = kernel's choice; 32 (bf16, d = 128: the
+                            matrix-core kernel) or 16 (the vector-ALU kernel, any dtype)    */
   float scale;           /* query scale; 0 = 1/sqrt(dk)                                    */
   int32_t use_qk_l2norm; /* 1: q, k are L2-normalised in the kernel (x / sqrt(sum x^2 + 1e-6)) */
   int32_t in_dtype;      /* kda_dtype_t of q, k, v and gate                                */
@@ -76,8 +77,9 @@ typedef struct {
 /*
  * kda_chunk_prefill -- the prompt kernel: runs the recurrence over whole sequences,
  * carrying the state from one chunk of tokens to the next without storing it per token
- * (nnterp Kimi-Linear page, Notes, "Loading": 64-token chunks).  Results equal the
- * token-by-token recurrence up to rounding.
+ * (nnterp Kimi-Linear page, Notes, "Loading", which names 64-token chunks; the chunked
+ * form is exact for any chunk length, and these kernels use 32 or 16).  Results equal
+ * the token-by-token recurrence up to rounding.
  *
  *   q, k          [B, T, H, dk]   in_dtype
  *   v             [B, T, H, dv]   in_dtype

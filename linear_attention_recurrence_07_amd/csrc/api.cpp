@@ -53,8 +53,8 @@ kda_status_t check_params(const kda_params_t *p, bool prefill) {
   if (!(p->scale >= 0.f) || !std::isfinite(p->scale)) return fail(KDA_ERR_SHAPE, "scale must be finite and >= 0");
   if (!(p->norm_eps >= 0.f) || !std::isfinite(p->norm_eps)) return fail(KDA_ERR_SHAPE, "norm_eps must be finite and >= 0");
   if (p->use_qk_l2norm != 0 && p->use_qk_l2norm != 1) return fail(KDA_ERR_SHAPE, "use_qk_l2norm must be 0 or 1");
-  if (prefill && p->chunk != 0 && p->chunk != 16 && p->chunk != 64)
-    return fail(KDA_ERR_UNSUPPORTED, "chunk %d not supported (0, 16 or 64)", p->chunk);
+  if (prefill && p->chunk != 0 && p->chunk != 16 && p->chunk != 32)
+    return fail(KDA_ERR_UNSUPPORTED, "chunk %d not supported (0, 16 or 32)", p->chunk);
   // Element counts must stay addressable with 32-bit token indices times heads.
   const double toks = static_cast<double>(p->B) * p->T * p->H;
   if (toks * p->dk > 9.0e18 || static_cast<double>(p->B) * p->T > 2147483647.0)
@@ -128,13 +128,13 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const bool norm = y != nullptr;
   const int chunk = p->chunk;
-  const bool mfma = kda::prefill_mfma_supports(p->dk, p->dv, a.in_bf16) && (chunk == 0 || chunk == 64) &&
+  const bool mfma = kda::prefill_mfma_supports(p->dk, p->dv, a.in_bf16) && (chunk == 0 || chunk == 32) &&
                     kda::prefill_mfma_fits(p->T, p->H);
   if (!mfma) {
     if (!kda::prefill_valu_supports(p->dk, p->dv))
       return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dk=%d dv=%d", p->dk, p->dv);
-    if (chunk == 64)
-      return fail(KDA_ERR_UNSUPPORTED, "chunk 64 needs bf16 inputs with dk = dv = 128");
+    if (chunk == 32)
+      return fail(KDA_ERR_UNSUPPORTED, "chunk 32 needs bf16 inputs with dk = dv = 128 and T * H * 128 < 2^31");
   }
   if (mfma) {
     KDA_TRY(hip_status(kda::launch_prefill_mfma(a, st), "prefill (MFMA)"));

@@ -88,10 +88,10 @@ def test_prefill_validation_codes():
     assert _prefill(_p(B=1, num_seqs=1), cu=A, mask=A) == 5
     assert _prefill(_p(B=2, num_seqs=2), cu=A) == 5
     assert _prefill(_p(), gate=A) == 5                       # gate without weight and y
-    assert _prefill(_p(chunk=32)) == 6
+    assert _prefill(_p(chunk=64)) == 6
     assert _prefill(_p(dk=96, dv=96)) == 6
-    assert _prefill(_p(dk=16, dv=16, chunk=64)) == 6         # 64-token chunks only on the MFMA path
-    assert _prefill(_p(in_dtype=0, chunk=64)) == 6
+    assert _prefill(_p(dk=16, dv=16, chunk=32)) == 6         # 32-token chunks only on the MFMA path
+    assert _prefill(_p(in_dtype=0, chunk=32)) == 6
     assert _prefill(_p(scale=float("nan"))) == 2
 
 
