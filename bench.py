@@ -161,13 +161,14 @@ def main():
     o = torch.empty((1, T_PREFILL, H, D), dtype=torch.bfloat16, device="cuda")
     y = torch.empty_like(o)
     fs = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty((kda.chunk_prefill_workspace_size(1, T_PREFILL, H, D, D),), dtype=torch.uint8, device="cuda")
     od = torch.empty((B_DECODE, 1, H, D), dtype=torch.bfloat16, device="cuda")
     yd = torch.empty_like(od)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        kda.chunk_prefill(P["q"], P["k"], P["v"], P["g"], P["beta"], out=o, final_state=fs)
+        kda.chunk_prefill(P["q"], P["k"], P["v"], P["g"], P["beta"], out=o, final_state=fs, workspace=ws)
         if ev is not None:
             ev[1].record()
         kda.gated_rmsnorm(o, P["gate"], P["w"], P["eps"], out=y)

@@ -18,13 +18,16 @@
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers to contiguous row-major buffers owned by
  *    the caller; the library never allocates, frees or retains device memory and keeps
- *    no state between calls (calls are thread-safe).  Pointers to tensors with a
- *    feature axis (q, k, v, g, states, o, gate, y, weights) must be 16-byte aligned;
+ *    no state between calls (calls are thread-safe).  Scratch space, where a kernel
+ *    needs it, is a caller-provided workspace whose size the library reports.
+ *    Pointers to tensors with a feature axis (q, k, v, g, states, o, gate, y, weights) must be 16-byte aligned;
  *    beta and cu_seqlens need 4-byte alignment, mask none.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default
  *    stream).  Arguments are validated on the host before anything is launched; a
- *    non-OK status means nothing was enqueued and no output was touched.  Faults
- *    inside a kernel surface at the caller's next synchronisation.
+ *    non-OK status other than KDA_ERR_HIP means nothing was enqueued and no output was
+ *    touched (KDA_ERR_HIP: a launch failed, and earlier launches of the same call may
+ *    have been enqueued).  Faults inside a kernel surface at the caller's next
+ *    synchronisation.
  *  - dtype codes: KDA_F32 = IEEE fp32, KDA_BF16 = bfloat16 (outputs rounded to
  *    nearest-even).  The recurrent state is always fp32.
  *  - Precondition (not checked, documented): every g lies in [-5, 0], the decay lower
@@ -54,7 +57,8 @@ typedef enum {
   KDA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned                             */
   KDA_ERR_CONFLICT = 5,     /* mutually exclusive arguments given together                  */
   KDA_ERR_UNSUPPORTED = 6,  /* a valid combination this build has no kernel for             */
-  KDA_ERR_HIP = 7           /* the HIP runtime reported an error at launch                  */
+  KDA_ERR_HIP = 7,          /* the HIP runtime reported an error at launch                  */
+  KDA_ERR_WORKSPACE = 8     /* the workspace is missing or smaller than required            */
 } kda_status_t;
 
 /* Problem description shared by the prefill and recurrent entry points. */
@@ -96,8 +100,16 @@ typedef struct {
  *   gate          [B, T, H, dv]   in_dtype, norm_weight [dv] fp32, y [B, T, H, dv]
  *                                 out_dtype: the gated norm y = w * o / rms(o) *
  *                                 sigmoid(gate) per head; all three set or all NULL
+ *   workspace     device scratch of at least kda_chunk_prefill_workspace_size(p,
+ *                 cu_seqlens != NULL) bytes, 16-byte aligned; may be NULL when that size
+ *                 is 0.  Its contents on entry do not matter; they are overwritten.
+ *                 Calls that overlap in time must not share a workspace.
  * N = B without cu_seqlens.  Tokens of a packed batch outside [0, cu_seqlens[N]) are
  * not written.
+ *
+ * The bf16 kernel for dk = dv = 128 runs in two launches: a preparation pass over every
+ * (sequence, head, chunk) at once, which stores each chunk's intra-chunk products in the
+ * workspace (4,352 bytes per chunk and head), then the sequential state scan.
  */
 kda_status_t kda_chunk_prefill(const kda_params_t *p,
                                const void *q, const void *k, const void *v,
@@ -106,7 +118,15 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p,
                                const int32_t *cu_seqlens, const uint8_t *mask,
                                void *o, float *final_state,
                                const void *gate, const float *norm_weight, void *y,
-                               void *stream);
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_chunk_prefill_workspace_size -- bytes of workspace kda_chunk_prefill needs for
+ * these params; `packed` is nonzero when cu_seqlens will be given (p->num_seqs set).
+ * 0 for invalid params or when the chosen kernel needs none.  With packing it is
+ * (N + ceil(T / 32)) * H * 4352 bytes, otherwise B * ceil(T / 32) * H * 4352.
+ */
+size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed);
 
 /*
  * kda_recurrent_step -- the decode kernel: the token-by-token form, for one new token

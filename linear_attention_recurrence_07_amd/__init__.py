@@ -23,7 +23,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["chunk_prefill", "recurrent_step", "gated_rmsnorm", "library_path", "load_library",
+__all__ = ["chunk_prefill", "chunk_prefill_workspace_size", "recurrent_step", "gated_rmsnorm", "library_path", "load_library",
            "KdaError", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,7 +68,9 @@ def load_library():
     lib = ctypes.CDLL(_LIB_PATH)
     P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     lib.kda_chunk_prefill.restype = ctypes.c_int
-    lib.kda_chunk_prefill.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 14
+    lib.kda_chunk_prefill.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 13 + [P, ctypes.c_size_t, P]
+    lib.kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.kda_chunk_prefill_workspace_size.argtypes = [ctypes.POINTER(KdaParams), i32]
     lib.kda_recurrent_step.restype = ctypes.c_int
     lib.kda_recurrent_step.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 12
     lib.kda_gated_rmsnorm.restype = ctypes.c_int
@@ -137,12 +139,14 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   use_qk_l2norm_in_kernel: bool = True, chunk: int = 0,
                   output_dtype: Optional[torch.dtype] = None,
                   out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-                  y: Optional[torch.Tensor] = None):
+                  y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Chunked prefill.  Returns (o, final_state), or (o, final_state, y) with the fused
     sigmoid-gated RMSNorm when gate and norm_weight are given.
 
     cu_seqlens ([N+1] int32; a CPU tensor is validated then copied to the GPU) packs N
     sequences into B = 1; attention_mask ([B, T], nonzero = token) marks padding.
+    workspace (a device tensor) is scratch of at least the library's reported size; one
+    is allocated per call when it is not given.
     """
     lib = load_library()
     dev = q.device
@@ -204,10 +208,28 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     p = _params(B, T, H, dk, dv, num_seqs=N if cu_dev is not None else 0, chunk=chunk, scale=scale,
                 use_qk_l2norm=use_qk_l2norm_in_kernel, in_dtype=_dtype_code(in_dt),
                 out_dtype=_dtype_code(out_dt), norm_eps=norm_eps)
+    need = lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), 1 if cu_dev is not None else 0)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
+    else:
+        _dev(workspace, "workspace", dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.kda_chunk_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                  _ptr(initial_state), _ptr(cu_dev), _ptr(mask_dev), _ptr(o), _ptr(fs),
-                                 _ptr(gate), _ptr(norm_weight), _ptr(y), _stream(dev)))
+                                 _ptr(gate), _ptr(norm_weight), _ptr(y), _ptr(workspace), ws_bytes,
+                                 _stream(dev)))
     return (o, fs) if y is None else (o, fs, y)
+
+
+def chunk_prefill_workspace_size(B: int, T: int, H: int, dk: int, dv: int, *,
+                                  num_seqs: Optional[int] = None, dtype: torch.dtype = torch.bfloat16,
+                                  chunk: int = 0) -> int:
+    """Bytes of workspace chunk_prefill needs; num_seqs is the sequence count when
+    cu_seqlens packs the batch (B = 1)."""
+    lib = load_library()
+    p = _params(B, T, H, dk, dv, num_seqs=num_seqs or 0, chunk=chunk, in_dtype=_dtype_code(dtype),
+                out_dtype=_dtype_code(dtype))
+    return int(lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), 1 if num_seqs is not None else 0))
 
 
 def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

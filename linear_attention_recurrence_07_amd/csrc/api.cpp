@@ -62,6 +62,18 @@ kda_status_t check_params(const kda_params_t *p, bool prefill) {
   return KDA_OK;
 }
 
+// The bf16 matrix-core prefill runs when the shape and dtype allow it and the caller did
+// not ask for the 16-token vector-ALU chunks.
+bool use_mfma_prefill(const kda_params_t *p) {
+  return kda::prefill_mfma_supports(p->dk, p->dv, p->in_dtype == KDA_BF16) &&
+         (p->chunk == 0 || p->chunk == 32) && kda::prefill_mfma_fits(p->T, p->H);
+}
+
+size_t prefill_workspace(const kda_params_t *p, bool packed) {
+  if (!use_mfma_prefill(p)) return 0;
+  return kda::chunk_prep_workspace_bytes(p->B, p->T, p->H, packed ? p->num_seqs : p->B, packed);
+}
+
 kda::Args make_args(const kda_params_t *p) {
   kda::Args a{};
   a.B = p->B;
@@ -104,7 +116,7 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
                                const float *g, const float *beta, const float *initial_state,
                                const int32_t *cu_seqlens, const uint8_t *mask, void *o,
                                float *final_state, const void *gate, const float *norm_weight,
-                               void *y, void *stream) {
+                               void *y, void *workspace, size_t workspace_bytes, void *stream) {
   KDA_TRY(check_params(p, true));
   KDA_TRY(check_ptr(q, "q", true));
   KDA_TRY(check_ptr(k, "k", true));
@@ -128,8 +140,7 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const bool norm = y != nullptr;
   const int chunk = p->chunk;
-  const bool mfma = kda::prefill_mfma_supports(p->dk, p->dv, a.in_bf16) && (chunk == 0 || chunk == 32) &&
-                    kda::prefill_mfma_fits(p->T, p->H);
+  const bool mfma = use_mfma_prefill(p);
   if (!mfma) {
     if (!kda::prefill_valu_supports(p->dk, p->dv))
       return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dk=%d dv=%d", p->dk, p->dv);
@@ -137,7 +148,13 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
       return fail(KDA_ERR_UNSUPPORTED, "chunk 32 needs bf16 inputs with dk = dv = 128 and T * H * 128 < 2^31");
   }
   if (mfma) {
-    KDA_TRY(hip_status(kda::launch_prefill_mfma(a, st), "prefill (MFMA)"));
+    const size_t need = prefill_workspace(p, cu_seqlens != nullptr);
+    if (workspace_bytes < need || (need > 0 && workspace == nullptr))
+      return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
+                  workspace == nullptr ? " (NULL)" : "");
+    KDA_TRY(check_ptr(workspace, "workspace", false));
+    KDA_TRY(hip_status(kda::launch_chunk_prep(a, workspace, st), "prefill (chunk preparation)"));
+    KDA_TRY(hip_status(kda::launch_chunk_scan(a, workspace, st), "prefill (state scan)"));
     if (norm) {
       const int64_t rows = static_cast<int64_t>(p->B) * p->T * p->H;
       KDA_TRY(hip_status(kda::launch_gated_rmsnorm(o, gate, norm_weight, y, rows, p->dv, p->norm_eps,
@@ -149,6 +166,12 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
     KDA_TRY(hip_status(kda::launch_prefill_valu(a, st), "prefill (VALU)"));
   }
   return KDA_OK;
+}
+
+size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed) {
+  if (p == nullptr || check_params(p, true) != KDA_OK) return 0;
+  if (packed && p->num_seqs <= 0) return 0;
+  return prefill_workspace(p, packed != 0);
 }
 
 kda_status_t kda_recurrent_step(const kda_params_t *p, const void *q, const void *k, const void *v,
@@ -207,6 +230,7 @@ const char *kda_status_string(kda_status_t s) {
     case KDA_ERR_CONFLICT: return "KDA_ERR_CONFLICT";
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
     case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
   }
   return "KDA_ERR_UNKNOWN";
 }

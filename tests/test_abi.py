@@ -22,8 +22,8 @@ def _declared_functions():
 
 def test_header_declares_the_three_entry_points():
     names = _declared_functions()
-    for n in ("kda_chunk_prefill", "kda_recurrent_step", "kda_gated_rmsnorm",
-              "kda_status_string", "kda_last_error", "kda_version"):
+    for n in ("kda_chunk_prefill", "kda_chunk_prefill_workspace_size", "kda_recurrent_step",
+              "kda_gated_rmsnorm", "kda_status_string", "kda_last_error", "kda_version"):
         assert n in names
 
 
@@ -67,14 +67,16 @@ A = ctypes.c_void_p(1 << 20)          # a 16-byte-aligned stand-in address; neve
 MIS = ctypes.c_void_p((1 << 20) + 4)  # misaligned
 
 
-def _prefill(p, **ptrs):
+def _prefill(p, ws=None, ws_bytes=0, **ptrs):
+    """Call kda_chunk_prefill with stand-in pointers.  Every call here must fail host
+    validation: a call that passed it would launch kernels on these addresses."""
     lib = K.load_library()
     names = ["q", "k", "v", "g", "beta", "init", "cu", "mask", "o", "fs", "gate", "w", "y"]
     default = dict(q=A, k=A, v=A, g=A, beta=A, init=None, cu=None, mask=None, o=A, fs=A,
                    gate=None, w=None, y=None)
     default.update(ptrs)
     return lib.kda_chunk_prefill(None if p is None else ctypes.byref(p),
-                                 *[default[n] for n in names], None)
+                                 *[default[n] for n in names], ws, ws_bytes, None)
 
 
 def test_prefill_validation_codes():
@@ -93,6 +95,25 @@ def test_prefill_validation_codes():
     assert _prefill(_p(dk=16, dv=16, chunk=32)) == 6         # 32-token chunks only on the MFMA path
     assert _prefill(_p(in_dtype=0, chunk=32)) == 6
     assert _prefill(_p(scale=float("nan"))) == 2
+
+
+def test_prefill_workspace_size_and_checks():
+    lib = K.load_library()
+    size = lambda p, packed=0: lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), packed)
+    rec = 4352                                             # bytes per (chunk, head)
+    assert size(_p(B=1, T=64, H=2)) == 1 * 2 * 2 * rec      # B * ceil(T/32) * H records
+    assert size(_p(B=3, T=65, H=2)) == 3 * 3 * 2 * rec
+    assert size(_p(B=1, T=64, H=2, num_seqs=3), 1) == (3 + 2) * 2 * rec   # (N + ceil(T/32)) * H
+    assert size(_p(B=1, T=64, H=2), 1) == 0                 # packed without num_seqs: invalid
+    assert size(_p(chunk=16)) == 0                          # vector-ALU kernel: no workspace
+    assert size(_p(dk=64, dv=64)) == 0
+    assert size(_p(in_dtype=0)) == 0
+    assert lib.kda_chunk_prefill_workspace_size(None, 0) == 0
+    need = size(_p())
+    assert _prefill(_p()) == 8                              # missing workspace
+    assert _prefill(_p(), ws=A, ws_bytes=need - 1) == 8     # too small
+    assert _prefill(_p(), ws=MIS, ws_bytes=need) == 4       # misaligned
+    assert lib.kda_status_string(8) == b"KDA_ERR_WORKSPACE"
 
 
 def test_recurrent_and_norm_validation_codes():
