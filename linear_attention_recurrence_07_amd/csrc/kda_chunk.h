@@ -22,21 +22,37 @@ constexpr int DV = 128;
 constexpr int C = 32;     // tokens per chunk
 constexpr int SB = 16;    // tokens per sub-block
 
-// Per (sequence, head, chunk) record in the workspace, written by the preparation kernel.
-//   bqk[r][s]  fp16  sum_c q^_rc k^_sc exp(G_rc - G_sc) for s <= r, 0 above the diagonal
-//   w[r][s]    fp16  ((I + A)^-1 diag(beta))[r][s], 0 above the diagonal
-//   kn[t]      fp32  1 / sqrt(sum k_t^2 + 1e-6)        (1 when the norm is off)
-//   qn[t]      fp32  scale / sqrt(sum q_t^2 + 1e-6)    (scale when the norm is off)
-// Padding and tokens past the end of a sequence have kn = qn = 0 (which is how the scan
-// kernel recognises them) and beta = 0, so their rows and columns of w and bqk vanish.
+// Per (sequence, head, chunk) record in the workspace, written by the preparation kernel
+// in the order the scan kernel's MFMA operands take.  A fragment is 64 lanes x 16 bytes:
+// lane L = 16 * lg + r holds row r of a 16-row tile and the 8 K indices kidx(lg, e),
+// e < 8, of a 32-wide K block (the same K permutation on both operands of a product).
+//   kb[m*4+s]  fp16  k^ exp(G)      rows = tokens 16m.., K = channels 32s..
+//   qt[m*4+s]  fp16  q^ exp(G)      same tiling (q^ includes the query scale)
+//   ket[t]     fp16  k^ exp(G_last - G), transposed: rows = channels 16t.., K = tokens
+//   bq[m]      fp16  Bqk[r][s] = sum_c q^_rc k^_sc exp(G_rc - G_sc) (s <= r), rows 16m..
+//   w1         fp16  W = (I + A)^-1 diag(beta), rows 16..31, K = all 32 tokens
+//   w00        fp16  W rows 0..15, K = tokens 0..15 (16x16x16 operand: e < 4 only)
+//   ec[c]      fp32  exp(G_last) per key channel
+//   valid      bit t set for a real token t of the chunk (not padding, not past the end)
+// Padding and tokens past the end of a sequence have zero rows in kb, qt, ket, bq, and
+// zero rows and columns in w.
 struct alignas(16) Rec {
-  uint16_t bqk[C * C];
-  uint16_t w[C * C];
-  float kn[C];
-  float qn[C];
+  uint16_t kb[8][64][8];
+  uint16_t qt[8][64][8];
+  uint16_t ket[8][64][8];
+  uint16_t bq[2][64][8];
+  uint16_t w1[64][8];
+  uint16_t w00[64][4];
+  float ec[DK];
+  uint32_t valid;
+  uint32_t pad[3];
 };
-static_assert(sizeof(Rec) == 4352, "record layout");
+static_assert(sizeof(Rec) == 28688, "record layout");
 constexpr size_t kRecBytes = sizeof(Rec);
+// K index (0..31) of slot e (0..7) of lane group lg, and the inverse.
+__host__ __device__ constexpr int kidx(int lg, int e) { return (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4); }
+__host__ __device__ constexpr int kidx_lg(int x) { return (x & 15) >> 2; }
+__host__ __device__ constexpr int kidx_e(int x) { return (x & 3) + 4 * (x >> 4); }
 
 // Record slots.  Batched rows: slot = row * ceil(T / C) + chunk.  Packed sequences:
 // slot = n + floor(start_n / C) + chunk with start_n = cu[n] clamped to [0, T], which is

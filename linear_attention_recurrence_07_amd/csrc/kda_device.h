@@ -22,8 +22,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 h = static_cast<__bf16>(f);
   return __builtin_bit_cast(uint16_t, h);
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// One packed conversion (v_cvt_pk_bf16_f32), a in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
   return make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
