@@ -109,7 +109,7 @@ typedef struct {
  *
  * The bf16 kernel for dk = dv = 128 runs in two launches: a preparation pass over every
  * (sequence, head, chunk) at once, which stores each chunk's intra-chunk products in the
- * workspace (28,688 bytes per chunk and head), then the sequential state scan.
+ * workspace (30,224 bytes per chunk and head), then the sequential state scan.
  */
 kda_status_t kda_chunk_prefill(const kda_params_t *p,
                                const void *q, const void *k, const void *v,
@@ -124,7 +124,7 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p,
  * kda_chunk_prefill_workspace_size -- bytes of workspace kda_chunk_prefill needs for
  * these params; `packed` is nonzero when cu_seqlens will be given (p->num_seqs set).
  * 0 for invalid params or when the chosen kernel needs none.  With packing it is
- * (N + ceil(T / 32)) * H * 28688 bytes, otherwise B * ceil(T / 32) * H * 28688.
+ * (N + ceil(T / 32)) * H * 30224 bytes, otherwise B * ceil(T / 32) * H * 30224.
  */
 size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed);
 

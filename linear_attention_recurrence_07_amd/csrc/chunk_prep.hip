@@ -101,11 +101,19 @@ struct Tail {
   uint16_t bq[2][64][8];
   uint16_t w1[64][8];
   uint16_t w00[64][4];
+  uint16_t w1lo[64][8];
+  uint16_t w00lo[64][4];
   float ec[DK];
   uint32_t valid;
   uint32_t pad[3];
 };
 static_assert(sizeof(Tail) == TAIL_BYTES && offsetof(Rec, bq) == 3 * 8 * 64 * 16, "record tail");
+// x = hi + lo with both parts fp16.
+__device__ __forceinline__ void split_f16(float x, uint16_t &hi, uint16_t &lo) {
+  const _Float16 h = static_cast<_Float16>(x);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = f16_bits(x - static_cast<float>(h));
+}
 // Byte offset of lane L of fragment `tile` in the padded staging layout.
 __device__ __forceinline__ int stg_off(int tile, int L) { return tile * TILEB + (L >> 4) * LGB + (L & 15) * 16; }
 
@@ -370,9 +378,11 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
       for (int m = 0; m < SB; ++m) s += a10[r][m] * tm[0][m][cc];
       pp[r][cc] = s;
     } else {
-      st.w00[16 * (cc >> 2) + r][cc & 3] = f16_bits(tm[0][r][cc] * sbeta[cc]);
+      const float w00 = tm[0][r][cc] * sbeta[cc];
+      split_f16(w00, st.w00[16 * (cc >> 2) + r][cc & 3], st.w00lo[16 * (cc >> 2) + r][cc & 3]);
       const int c1 = SB + cc;                    // W(1,1) block of rows 16..31
-      st.w1[16 * kidx_lg(c1) + r][kidx_e(c1)] = f16_bits(tm[1][r][cc] * sbeta[SB + cc]);
+      const float w11 = tm[1][r][cc] * sbeta[SB + cc];
+      split_f16(w11, st.w1[16 * kidx_lg(c1) + r][kidx_e(c1)], st.w1lo[16 * kidx_lg(c1) + r][kidx_e(c1)]);
     }
     // k^ exp(G) and q^ exp(G): token r = 4w + j, channels 2l, 2l+1 -> tile (r/16, l/16),
     // lane 16 * lg(ch) + r % 16, slots e(ch) and e(ch) + 1.
@@ -402,7 +412,7 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
       float s = 0.f;
 #pragma unroll
       for (int m = 0; m < SB; ++m) s += tm[1][r][m] * pp[m][cc];
-      st.w1[16 * kidx_lg(cc) + r][kidx_e(cc)] = f16_bits(-s * sbeta[cc]);
+      split_f16(-s * sbeta[cc], st.w1[16 * kidx_lg(cc) + r][kidx_e(cc)], st.w1lo[16 * kidx_lg(cc) + r][kidx_e(cc)]);
     } else if (tid == 256) {
       uint32_t v = 0;
       for (int t = 0; t < C; ++t) v |= static_cast<uint32_t>(vb[t] != 0) << t;

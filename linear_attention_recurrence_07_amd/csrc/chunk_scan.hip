@@ -24,9 +24,9 @@
 //     rows (norm, gate) from the other;
 //   - ends with the one work-group barrier of the step.
 //
-// Precision: fp16 operands for the state and the decayed keys/queries, V - K S0 and U
-// split into fp16 hi + lo parts, fp32 accumulation.  The fp16 state operand limits |S| to
-// well inside fp16 range.
+// Precision: fp16 operands for the state, the decayed keys/queries and V - K S0; W and U
+// as fp16 hi + lo parts; fp32 accumulation.  The fp16 state operand limits |S| to well
+// inside fp16 range.
 #include "kda_chunk.h"
 #include "kda_launch.h"
 
@@ -154,8 +154,8 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
       const f32x4 a = Sacc[2 * s], bb = Sacc[2 * s + 1];
       Sh[s] = join(pack_f16x4(a[0], a[1], a[2], a[3]), pack_f16x4(bb[0], bb[1], bb[2], bb[3]));
     }
-    // Y = V - (k^ exp(G)) S0, split into fp16 hi + lo
-    uint2 yh[2], yl[2];
+    // Y = V - (k^ exp(G)) S0 in fp16 (W carries the extra precision)
+    uint2 yf[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -170,16 +170,19 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
         const uint32_t keep = 0u - ((valid >> r) & 1u);
         yy[i] = __uint_as_float((static_cast<uint32_t>(hc.vt[r * LDV + wcol]) << 16) & keep) - acc[i];
       }
-      split_f16x4(yy, yh[m], yl[m]);
+      yf[m] = pack_f16x4(yy[0], yy[1], yy[2], yy[3]);
     }
-    // U0 = W00 Y0, U1 = W10 Y0 + W11 Y1
+    // U0 = W00 Y0, U1 = W10 Y0 + W11 Y1, with W as hi + lo parts
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const uint2 w00 = __builtin_bit_cast(uint2, reinterpret_cast<const u32x2 *>(hc.rec.w00)[lane]);
-    f32x4 U0 = mfma_f16k16(w00, yl[0], zero);
-    U0 = mfma_f16k16(w00, yh[0], U0);
+    const uint2 w00l = __builtin_bit_cast(uint2, reinterpret_cast<const u32x2 *>(hc.rec.w00lo)[lane]);
+    f32x4 U0 = mfma_f16k16(w00l, yf[0], zero);
+    U0 = mfma_f16k16(w00, yf[0], U0);
     const uint4 w1 = __builtin_bit_cast(uint4, reinterpret_cast<const u32x4 *>(hc.rec.w1)[lane]);
-    f32x4 U1 = mfma_f16(w1, join(yl[0], yl[1]), zero);
-    U1 = mfma_f16(w1, join(yh[0], yh[1]), U1);
+    const uint4 w1l = __builtin_bit_cast(uint4, reinterpret_cast<const u32x4 *>(hc.rec.w1lo)[lane]);
+    const uint4 y01 = join(yf[0], yf[1]);
+    f32x4 U1 = mfma_f16(w1l, y01, zero);
+    U1 = mfma_f16(w1, y01, U1);
     uint2 u0h, u0l, u1h, u1l;
     split_f16x4(U0, u0h, u0l);
     split_f16x4(U1, u1h, u1l);

@@ -30,8 +30,8 @@ constexpr int SB = 16;    // tokens per sub-block
 //   qt[m*4+s]  fp16  q^ exp(G)      same tiling (q^ includes the query scale)
 //   ket[t]     fp16  k^ exp(G_last - G), transposed: rows = channels 16t.., K = tokens
 //   bq[m]      fp16  Bqk[r][s] = sum_c q^_rc k^_sc exp(G_rc - G_sc) (s <= r), rows 16m..
-//   w1         fp16  W = (I + A)^-1 diag(beta), rows 16..31, K = all 32 tokens
-//   w00        fp16  W rows 0..15, K = tokens 0..15 (16x16x16 operand: e < 4 only)
+//   w1, w1lo   fp16  W = (I + A)^-1 diag(beta) as hi + lo parts, rows 16..31, K = 32 tokens
+//   w00, w00lo fp16  W rows 0..15, K = tokens 0..15 (16x16x16 operand: e < 4 only)
 //   ec[c]      fp32  exp(G_last) per key channel
 //   valid      bit t set for a real token t of the chunk (not padding, not past the end)
 // Padding and tokens past the end of a sequence have zero rows in kb, qt, ket, bq, and
@@ -43,11 +43,13 @@ struct alignas(16) Rec {
   uint16_t bq[2][64][8];
   uint16_t w1[64][8];
   uint16_t w00[64][4];
+  uint16_t w1lo[64][8];
+  uint16_t w00lo[64][4];
   float ec[DK];
   uint32_t valid;
   uint32_t pad[3];
 };
-static_assert(sizeof(Rec) == 28688, "record layout");
+static_assert(sizeof(Rec) == 30224, "record layout");
 constexpr size_t kRecBytes = sizeof(Rec);
 // K index (0..31) of slot e (0..7) of lane group lg, and the inverse.
 __host__ __device__ constexpr int kidx(int lg, int e) { return (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4); }

@@ -100,7 +100,7 @@ def test_prefill_validation_codes():
 def test_prefill_workspace_size_and_checks():
     lib = K.load_library()
     size = lambda p, packed=0: lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), packed)
-    rec = 28688                                            # bytes per (chunk, head)
+    rec = 30224                                            # bytes per (chunk, head)
     assert size(_p(B=1, T=64, H=2)) == 1 * 2 * 2 * rec      # B * ceil(T/32) * H records
     assert size(_p(B=3, T=65, H=2)) == 3 * 3 * 2 * rec
     assert size(_p(B=1, T=64, H=2, num_seqs=3), 1) == (3 + 2) * 2 * rec   # (N + ceil(T/32)) * H
