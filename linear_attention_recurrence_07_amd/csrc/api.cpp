@@ -153,9 +153,14 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
       return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
                   workspace == nullptr ? " (NULL)" : "");
     KDA_TRY(check_ptr(workspace, "workspace", false));
-    a.gate = gate; a.norm_w = norm_weight; a.y = y;
     KDA_TRY(hip_status(kda::launch_chunk_prep(a, workspace, st), "prefill (chunk preparation)"));
     KDA_TRY(hip_status(kda::launch_chunk_scan(a, workspace, st), "prefill (state scan)"));
+    if (norm) {
+      const int64_t rows = static_cast<int64_t>(p->B) * p->T * p->H;
+      KDA_TRY(hip_status(kda::launch_gated_rmsnorm(o, gate, norm_weight, y, rows, p->dv, p->norm_eps,
+                                                   a.out_bf16, a.in_bf16, a.out_bf16, st),
+                         "gated norm"));
+    }
   } else {
     a.gate = gate; a.norm_w = norm_weight; a.y = y;
     KDA_TRY(hip_status(kda::launch_prefill_valu(a, st), "prefill (VALU)"));

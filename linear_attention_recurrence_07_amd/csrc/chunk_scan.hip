@@ -1,5 +1,5 @@
 // State scan of the bf16 chunked prefill on the CDNA4 matrix cores (head size 128,
-// 32-token chunks), with the sigmoid-gated RMSNorm fused into its output stage.
+// 32-token chunks).
 //
 // The prompt kernel of the KDA recurrence carries the state from chunk to chunk (nnterp
 // Kimi-Linear page, Notes, "Loading" and the KDA paragraph; section 04 docstring).  With
@@ -8,21 +8,21 @@
 //     U      = W (V - (k^ exp(G)) S0)
 //     O      = (q^ exp(G)) S0 + Bqk U
 //     S_next = diag(exp(G_last)) S0 + (k^ exp(G_last - G))^T U
-// which is the token-by-token recurrence regrouped; it equals it up to rounding.  Then,
-// per token and head (Kimi-K3 atlas, gate-project page, o_norm):
-//     y = w * O / sqrt(mean(O^2) + eps) * sigmoid(gate)
+// which is the token-by-token recurrence regrouped; it equals it up to rounding.
 //
-// Work decomposition.  One work-group per (sequence, head) with eight waves, two per SIMD;
-// wave w owns value columns 16w..16w+15 and keeps its 128 x 16 slice of the fp32 state in
-// registers for the whole sequence.  Each step:
-//   - stores the record and value tile of chunk c+1 (loaded two steps earlier into
-//     registers) into the other half of a double-buffered LDS hand-over area, and issues
-//     the loads of chunk c+3;
-//   - runs chunk c's products on MFMA, the record's operands read straight from LDS in
-//     fragment order (16-byte reads, no bank conflicts);
-//   - writes chunk c's output tile to one of two LDS staging buffers and emits chunk c-1's
-//     rows (norm, gate) from the other;
-//   - ends with the one work-group barrier of the step.
+// Work decomposition.  Value columns are independent in the recurrence, so a work-group
+// owns one (sequence, head, 64-column tile); at 96 heads that is 192 work-groups, one per
+// CU.  Eight waves, two per SIMD:
+//   compute waves 0-3: wave w owns value columns 16w..16w+15 of the tile and keeps its
+//     128 x 16 slice of the fp32 state in registers for the whole sequence.  Each chunk's
+//     products run on MFMA with the record's operands read from LDS in fragment order
+//     (16-byte reads, no bank conflicts).
+//   helper waves 4-7: stage the record and value tile of chunk c+1 (loaded one step
+//     earlier into registers) into the other half of a double-buffered LDS hand-over
+//     area, issue the loads of chunk c+2, and write chunk c-1's output rows from the
+//     other of two output tiles, while the compute waves work on chunk c.
+// One work-group barrier per step.  The two tiles of a head get work-group ids 8 apart,
+// so they land on the same XCD and share its L2 for the record reads.
 //
 // Precision: fp16 operands for the state, the decayed keys/queries and V - K S0; W and U
 // as fp16 hi + lo parts; fp32 accumulation.  The fp16 state operand limits |S| to well
@@ -34,12 +34,17 @@ namespace kda {
 namespace {
 using namespace chunk;
 
-constexpr int NW = 8;             // waves per work-group; wave w owns columns 16w..16w+15
+constexpr int DVT = 64;           // value columns per work-group
+constexpr int NTILE = DV / DVT;   // work-groups per (sequence, head)
+constexpr int NW = 8;             // waves per work-group
 constexpr int NT = NW * 64;       // 512 threads
-constexpr int LDV = DV + 8;       // value tile row stride (bf16)
-constexpr int LDO = DV + 4;       // fp32 output staging row stride
+constexpr int NCW = DVT / 16;     // compute waves, 16 columns each
+constexpr int NHT = NT - NCW * 64;  // helper threads (256)
+constexpr int LDV = DVT + 8;      // value tile row stride (bf16)
+constexpr int LDO = DVT + 4;      // fp32 output tile row stride
 constexpr int REC_PIECES = static_cast<int>(sizeof(Rec) / 16);
-constexpr int PPT = (REC_PIECES + NT - 1) / NT;   // record pieces per thread (4)
+constexpr int PPT = (REC_PIECES + NHT - 1) / NHT;   // record pieces per helper thread (8)
+static_assert(NCW == 4 && NHT == 256, "thread mappings");
 
 struct alignas(16) Hand {
   Rec rec;
@@ -50,24 +55,24 @@ struct alignas(16) Smem {
   float ost[2][C * LDO];       // fp32 output tiles
 };
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
-static_assert(sizeof(Hand) % 16 == 0 && (LDV * 2) % 16 == 0, "16-byte LDS stores");
+static_assert(sizeof(Hand) % 16 == 0 && (LDV * 2) % 16 == 0 && (LDO * 4) % 16 == 0, "16-byte LDS access");
 
-__device__ __forceinline__ float sigmoid_fast(float x) {
-  return __builtin_amdgcn_rcpf(1.f + fast_exp2(-x * kLog2e));
-}
-
-template <typename TOut, bool HAS_INIT, bool NORM>
+template <typename TOut, bool HAS_INIT>
 __global__ void __launch_bounds__(NT, 1)
 chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, const float *init,
-                  float *fin, const int32_t *__restrict__ cu, TOut *__restrict__ o,
-                  const uint16_t *__restrict__ gate, const float *__restrict__ nw,
-                  TOut *__restrict__ y, float eps, int T, int H, int units) {
+                  float *fin, const int32_t *__restrict__ cu, TOut *__restrict__ o, int T, int H, int units) {
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: branches stay scalar
   const int l16 = lane & 15, lg = lane >> 4;
+  const bool helper = wave >= NCW;
+  const int ht = tid - NCW * 64;                               // helper thread index
 
-  const int unit = blockIdx.x;
+  // Work-groups are dealt to the 8 XCDs round-robin; the tiles of one (sequence, head)
+  // get ids 8 apart.
+  const int id = blockIdx.x;
+  const int unit = (id / (8 * NTILE)) * 8 + (id % 8);
+  const int tile = (id / 8) % NTILE;
   if (unit >= units) return;
   const int n = unit / H, h = unit % H;
   int b, t_begin, t_end;
@@ -83,70 +88,87 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     t_end = T;
     slot0 = static_cast<long long>(n) * chunks_per_row(T);
   }
+  const int col0 = tile * DVT;
   const size_t slab = (static_cast<size_t>(n) * H + h) * DK * DV;
   const int nchunks = (t_end - t_begin + C - 1) / C;
   const size_t row0 = static_cast<size_t>(b) * T;              // first token row of this batch row
-  const size_t tok_stride = static_cast<size_t>(H) * DV;       // elements between tokens (v, o, gate)
-  // this thread's 8-column piece of a token row: token tid/16, columns (tid%16)*8
-  const size_t piece = row0 * tok_stride + static_cast<size_t>(h) * DV + (tid & 15) * 8;
+  const size_t tok_stride = static_cast<size_t>(H) * DV;       // elements between tokens (v, o)
+  // Addresses: a wave-uniform base plus a 32-bit per-lane byte offset.  Within one batch
+  // row, token offsets stay below 2^32 bytes (T * H * 128 < 2^31).
+  // A helper thread's row piece: token ht/8, columns (ht%8)*8 .. +7 of the tile.
+  const int hr = ht >> 3, hc8 = (ht & 7) * 8;
+  const uint32_t piece = static_cast<uint32_t>(h * DV + col0 + hc8) * 2u;   // bytes
+  const uint32_t tok_bytes = static_cast<uint32_t>(H * DV) * 2u;
+  const uint8_t *vrow = reinterpret_cast<const uint8_t *>(v + row0 * tok_stride);
   const Rec *rp0 = ws + slot0 * H + h;                         // chunk c's record: rp0 + c * H
-  const int wcol = 16 * wave + l16;                            // this lane's value column
 
-  // ---------------------------------------------------------------- prefetch registers
-  // Two sets, so a chunk's record and values are loaded two steps before they are staged.
+  // ================================================================ helper side
   struct Pre {
     u32x4 r[PPT];
     u32x4 v;
+    uint32_t valid;            // the chunk's token flags
   };
-  Pre pre0, pre1;
-  auto load = [&](Pre &pf, int cidx) {
-    const u32x4 *rp = reinterpret_cast<const u32x4 *>(rp0 + static_cast<size_t>(cidx) * H);
+  uint32_t vzero;              // 0 in a vector register: keeps the flag load a per-lane load
+  __asm__ volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+  Pre pre;
+  auto load = [&](int cidx) {
+    const uint8_t *rp = reinterpret_cast<const uint8_t *>(rp0 + static_cast<size_t>(cidx) * H);
 #pragma unroll
-    for (int i = 0; i < PPT; ++i)
-      if (i < PPT - 1 || tid + NT * i < REC_PIECES) pf.r[i] = rp[tid + NT * i];
-    const int tv = min(t_begin + cidx * C + (tid >> 4), t_end - 1);
-    pf.v = *reinterpret_cast<const u32x4 *>(v + piece + tv * tok_stride);
-    __asm__ volatile("" ::: "memory");   // keep the loads here, ahead of their use
+    for (int i = 0; i < PPT; ++i) {
+      const uint8_t *rpi = rp + NHT * 16 * i;    // uniform base per piece row
+      if (i < PPT - 1 || ht + NHT * i < REC_PIECES)
+        pre.r[i] = *reinterpret_cast<const u32x4 *>(rpi + static_cast<uint32_t>(ht) * 16u);
+    }
+    pre.valid = *reinterpret_cast<const uint32_t *>(rp + offsetof(Rec, valid) + vzero);
+    const uint32_t tv = static_cast<uint32_t>(min(t_begin + cidx * C + hr, t_end - 1));
+    pre.v = *reinterpret_cast<const u32x4 *>(vrow + (piece + tv * tok_bytes));
+    __asm__ volatile("" ::: "memory");   // keep the loads here, a step ahead of their use
   };
-  auto stage = [&](Hand &hd, const Pre &pf) {
+  auto stage = [&](Hand &hd) {
     u32x4 *dst = reinterpret_cast<u32x4 *>(&hd.rec);
 #pragma unroll
     for (int i = 0; i < PPT; ++i)
-      if (i < PPT - 1 || tid + NT * i < REC_PIECES) dst[tid + NT * i] = pf.r[i];
-    *reinterpret_cast<u32x4 *>(hd.vt + (tid >> 4) * LDV + (tid & 15) * 8) = pf.v;
+      if (i < PPT - 1 || ht + NHT * i < REC_PIECES) dst[ht + NHT * i] = pre.r[i];
+    // values of padding and of tokens past the end are zeroed
+    const bool keep = (pre.valid >> hr) & 1u;
+    *reinterpret_cast<u32x4 *>(hd.vt + hr * LDV + hc8) = keep ? pre.v : u32x4{0u, 0u, 0u, 0u};
   };
-  auto load_gate = [&](int cidx) -> u32x4 {
-    const int tv = min(t_begin + cidx * C + (tid >> 4), t_end - 1);
-    const u32x4 gv = *reinterpret_cast<const u32x4 *>(gate + piece + tv * tok_stride);
-    __asm__ volatile("" ::: "memory");
-    return gv;
+  // Token ht/8 of chunk cidx, columns (ht%8)*8..+7 of the tile.
+  auto emit = [&](int cidx, const float *ost) {
+    const int t = t_begin + cidx * C + hr;
+    const float4 x0 = *reinterpret_cast<const float4 *>(ost + hr * LDO + hc8);
+    const float4 x1 = *reinterpret_cast<const float4 *>(ost + hr * LDO + hc8 + 4);
+    if (t < t_end) {
+      const size_t off = row0 * tok_stride + (piece + static_cast<uint32_t>(t) * tok_bytes) / 2u;
+      if constexpr (sizeof(TOut) == 2) {
+        uint4 w;
+        w.x = pack_bf16x2(x0.x, x0.y); w.y = pack_bf16x2(x0.z, x0.w);
+        w.z = pack_bf16x2(x1.x, x1.y); w.w = pack_bf16x2(x1.z, x1.w);
+        *reinterpret_cast<uint4 *>(o + off) = w;
+      } else {
+        reinterpret_cast<float4 *>(o + off)[0] = x0;
+        reinterpret_cast<float4 *>(o + off)[1] = x1;
+      }
+    }
   };
 
-  // ---------------------------------------------------------------- state
-  f32x4 Sacc[DK / 16];                           // Sacc[t][i] = S[16t + 4lg + i][wcol]
+  // ================================================================ compute side
+  f32x4 Sacc[DK / 16];                           // Sacc[t][i] = S[16t + 4lg + i][col0 + 16 wave + l16]
 #pragma unroll
   for (int t = 0; t < DK / 16; ++t) Sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (HAS_INIT) {
+  const int wcol = 16 * wave + l16;              // this lane's column in the tile
+  if (HAS_INIT && !helper) {
 #pragma unroll
     for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Sacc[t][i] = init[slab + static_cast<size_t>(16 * t + 4 * lg + i) * DV + wcol];
-  }
-  float wv[8];                                   // norm weight of this thread's 8 columns
-  if (NORM) {
-    const float4 w0 = *reinterpret_cast<const float4 *>(nw + (tid & 15) * 8);
-    const float4 w1 = *reinterpret_cast<const float4 *>(nw + (tid & 15) * 8 + 4);
-    wv[0] = w0.x; wv[1] = w0.y; wv[2] = w0.z; wv[3] = w0.w;
-    wv[4] = w1.x; wv[5] = w1.y; wv[6] = w1.z; wv[7] = w1.w;
+      for (int i = 0; i < 4; ++i) Sacc[t][i] = init[slab + static_cast<size_t>(16 * t + 4 * lg + i) * DV + col0 + wcol];
   }
 
-  // ================================================================ products of one chunk
   auto products = [&](const Hand &hc, float *ost) {
     const u32x4 *KB = reinterpret_cast<const u32x4 *>(hc.rec.kb);
     const u32x4 *QT = reinterpret_cast<const u32x4 *>(hc.rec.qt);
     const u32x4 *KE = reinterpret_cast<const u32x4 *>(hc.rec.ket);
     const u32x4 *BQ = reinterpret_cast<const u32x4 *>(hc.rec.bq);
-    const uint32_t valid = hc.rec.valid;
     // S0 as fp16 B operands; K step s covers channels {32s+4lg+0..3, 32s+16+4lg+0..3}
     uint4 Sh[DK / 32];
 #pragma unroll
@@ -164,12 +186,7 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
         acc = mfma_f16(__builtin_bit_cast(uint4, KB[(4 * m + s) * 64 + lane]), Sh[s], acc);
       f32x4 yy;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = SB * m + 4 * lg + i;
-        // values of padding and of tokens past the end are zeroed (branch-free)
-        const uint32_t keep = 0u - ((valid >> r) & 1u);
-        yy[i] = __uint_as_float((static_cast<uint32_t>(hc.vt[r * LDV + wcol]) << 16) & keep) - acc[i];
-      }
+      for (int i = 0; i < 4; ++i) yy[i] = bf16_to_f32(hc.vt[(SB * m + 4 * lg + i) * LDV + wcol]) - acc[i];
       yf[m] = pack_f16x4(yy[0], yy[1], yy[2], yy[3]);
     }
     // U0 = W00 Y0, U1 = W10 Y0 + W11 Y1, with W as hi + lo parts
@@ -188,6 +205,15 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     split_f16x4(U1, u1h, u1l);
     const uint4 Uh = join(u0h, u1h);   // tokens {4lg+0..3, 16+4lg+0..3} as K=32 B operands
     const uint4 Ul = join(u0l, u1l);
+    // S = diag(exp(G_last)) S0 + (k^ exp(G_last - G))^T U
+#pragma unroll
+    for (int t = 0; t < DK / 16; ++t) {
+      const float4 e = *reinterpret_cast<const float4 *>(hc.rec.ec + 16 * t + 4 * lg);
+      Sacc[t][0] *= e.x; Sacc[t][1] *= e.y; Sacc[t][2] *= e.z; Sacc[t][3] *= e.w;
+      const uint4 kv = __builtin_bit_cast(uint4, KE[t * 64 + lane]);
+      Sacc[t] = mfma_f16(kv, Ul, Sacc[t]);
+      Sacc[t] = mfma_f16(kv, Uh, Sacc[t]);
+    }
     // O = (q^ exp(G)) S0 + Bqk U
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -201,110 +227,47 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
 #pragma unroll
       for (int i = 0; i < 4; ++i) ost[(SB * m + 4 * lg + i) * LDO + wcol] = acc[i];
     }
-    // S = diag(exp(G_last)) S0 + (k^ exp(G_last - G))^T U
-#pragma unroll
-    for (int t = 0; t < DK / 16; ++t) {
-      const float4 e = *reinterpret_cast<const float4 *>(hc.rec.ec + 16 * t + 4 * lg);
-      Sacc[t][0] *= e.x; Sacc[t][1] *= e.y; Sacc[t][2] *= e.z; Sacc[t][3] *= e.w;
-      const uint4 kv = __builtin_bit_cast(uint4, KE[t * 64 + lane]);
-      Sacc[t] = mfma_f16(kv, Ul, Sacc[t]);
-      Sacc[t] = mfma_f16(kv, Uh, Sacc[t]);
-    }
-  };
-
-  // ================================================================ output rows
-  // Token tid/16 of chunk cidx, columns (tid%16)*8..+7: head output, and the gated norm
-  // over the row (the 16 lanes of a row are one DPP row).
-  auto emit = [&](int cidx, const float *ost, u32x4 gv) {
-    const int r = tid >> 4, c8 = (tid & 15) * 8;
-    const int t = t_begin + cidx * C + r;
-    const float4 x0 = *reinterpret_cast<const float4 *>(ost + r * LDO + c8);
-    const float4 x1 = *reinterpret_cast<const float4 *>(ost + r * LDO + c8 + 4);
-    const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    float yv[8];
-    if (NORM) {
-      float ss = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ss += xv[i] * xv[i];
-      ss = row_sum16(ss);
-      const float rn = rsqrtf(ss * (1.f / DV) + eps);
-      const float gf[8] = {lo_bf16(gv[0]), hi_bf16(gv[0]), lo_bf16(gv[1]), hi_bf16(gv[1]),
-                           lo_bf16(gv[2]), hi_bf16(gv[2]), lo_bf16(gv[3]), hi_bf16(gv[3])};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) yv[i] = wv[i] * (xv[i] * rn) * sigmoid_fast(gf[i]);
-    }
-    if (t < t_end) {
-      const size_t off = piece + static_cast<size_t>(t) * tok_stride;
-      if constexpr (sizeof(TOut) == 2) {
-        uint4 w;
-        w.x = pack_bf16x2(xv[0], xv[1]); w.y = pack_bf16x2(xv[2], xv[3]);
-        w.z = pack_bf16x2(xv[4], xv[5]); w.w = pack_bf16x2(xv[6], xv[7]);
-        *reinterpret_cast<uint4 *>(o + off) = w;
-        if (NORM) {
-          w.x = pack_bf16x2(yv[0], yv[1]); w.y = pack_bf16x2(yv[2], yv[3]);
-          w.z = pack_bf16x2(yv[4], yv[5]); w.w = pack_bf16x2(yv[6], yv[7]);
-          *reinterpret_cast<uint4 *>(y + off) = w;
-        }
-      } else {
-        reinterpret_cast<float4 *>(o + off)[0] = x0;
-        reinterpret_cast<float4 *>(o + off)[1] = x1;
-        if (NORM) {
-          reinterpret_cast<float4 *>(y + off)[0] = make_float4(yv[0], yv[1], yv[2], yv[3]);
-          reinterpret_cast<float4 *>(y + off)[1] = make_float4(yv[4], yv[5], yv[6], yv[7]);
-        }
-      }
-    }
   };
 
   if (nchunks > 0) {
-    u32x4 gA = {0u, 0u, 0u, 0u}, gB = gA, gC = gA;   // gate tiles of chunks s-1, s, s+1
     const int last = nchunks - 1;
-    load(pre0, 0);
-    load(pre1, min(1, last));
-    stage(sm.hand[0], pre0);
-    load(pre0, min(2, last));
-    if (NORM) gB = load_gate(0);
-    sync_lds();
-    // step s: stage chunk s+1 (loaded at step s-2), load chunk s+3 into the freed set,
-    // products of chunk s, output rows of chunk s-1.  Chunks past the end repeat the last.
-    auto step = [&](int s, Pre &stage_from) {
-      stage(sm.hand[(s + 1) & 1], stage_from);
-      load(stage_from, min(s + 3, last));
-      if (NORM) gC = load_gate(min(s + 1, last));
-      products(sm.hand[s & 1], sm.ost[s & 1]);
-      if (s >= 1) emit(s - 1, sm.ost[(s + 1) & 1], gA);
-      gA = gB;
-      gB = gC;
-      sync_lds();
-    };
-    int s = 0;
-    for (; s + 1 < nchunks; s += 2) {
-      step(s, pre1);                             // chunk s+1 is in pre1, s+2 in pre0
-      step(s + 1, pre0);
+    if (helper) {
+      load(0);
+      stage(sm.hand[0]);
+      load(min(1, last));
     }
-    if (s < nchunks) step(s, pre1);
-    emit(last, sm.ost[(last + 2) & 1], gA);
+    sync_lds();
+    // step s: helpers stage chunk s+1 (loaded at step s-1), load chunk s+2 and write chunk
+    // s-1's rows; compute waves run chunk s.  Chunks past the end repeat the last.
+    for (int s = 0; s < nchunks; ++s) {
+      if (helper) {
+        stage(sm.hand[(s + 1) & 1]);
+        load(min(s + 2, last));
+        if (s >= 1) emit(s - 1, sm.ost[(s + 1) & 1]);
+      } else {
+        products(sm.hand[s & 1], sm.ost[s & 1]);
+      }
+      sync_lds();
+    }
+    if (helper) emit(last, sm.ost[last & 1]);
   }
 
+  if (!helper) {
 #pragma unroll
-  for (int t = 0; t < DK / 16; ++t)
+    for (int t = 0; t < DK / 16; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fin[slab + static_cast<size_t>(16 * t + 4 * lg + i) * DV + wcol] = Sacc[t][i];
-}
-
-template <typename TOut, bool HAS_INIT, bool NORM>
-hipError_t launch3(const Args &a, const void *ws, hipStream_t st) {
-  const int units = a.N * a.H;
-  hipLaunchKernelGGL((chunk_scan_kernel<TOut, HAS_INIT, NORM>), dim3(static_cast<unsigned>(units)), dim3(NT), 0,
-                     st, static_cast<const uint16_t *>(a.v), static_cast<const Rec *>(ws), a.init, a.state, a.cu,
-                     static_cast<TOut *>(a.o), static_cast<const uint16_t *>(a.gate), a.norm_w,
-                     static_cast<TOut *>(a.y), a.eps, a.T, a.H, units);
-  return hipGetLastError();
+      for (int i = 0; i < 4; ++i) fin[slab + static_cast<size_t>(16 * t + 4 * lg + i) * DV + col0 + wcol] = Sacc[t][i];
+  }
 }
 
 template <typename TOut, bool HAS_INIT>
 hipError_t launch2(const Args &a, const void *ws, hipStream_t st) {
-  return a.y ? launch3<TOut, HAS_INIT, true>(a, ws, st) : launch3<TOut, HAS_INIT, false>(a, ws, st);
+  const int units = a.N * a.H;
+  const unsigned grid = static_cast<unsigned>((units + 7) / 8) * 8 * NTILE;
+  hipLaunchKernelGGL((chunk_scan_kernel<TOut, HAS_INIT>), dim3(grid), dim3(NT), 0, st,
+                     static_cast<const uint16_t *>(a.v), static_cast<const Rec *>(ws), a.init, a.state, a.cu,
+                     static_cast<TOut *>(a.o), a.T, a.H, units);
+  return hipGetLastError();
 }
 
 template <typename TOut>
