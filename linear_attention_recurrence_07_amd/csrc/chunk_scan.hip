@@ -17,9 +17,9 @@
 //     128 x 16 slice of the fp32 state in registers for the whole sequence.  Each chunk's
 //     products run on MFMA with the record's operands read from LDS in fragment order
 //     (16-byte reads, no bank conflicts).
-//   helper waves 4-7: stage the record and value tile of chunk c+1 (loaded one step
+//   helper waves 4-7: stage the record and value tile of chunk c+1 (loaded two steps
 //     earlier into registers) into the other half of a double-buffered LDS hand-over
-//     area, issue the loads of chunk c+2, and write chunk c-1's output rows from the
+//     area, issue the loads of chunk c+3, and write chunk c-1's output rows from the
 //     other of two output tiles, while the compute waves work on chunk c.
 // One work-group barrier per step.  The two tiles of a head get work-group ids 8 apart,
 // so they land on the same XCD and share its L2 for the record reads.
@@ -110,8 +110,8 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
   };
   uint32_t vzero;              // 0 in a vector register: keeps the flag load a per-lane load
   __asm__ volatile("v_mov_b32 %0, 0" : "=v"(vzero));
-  Pre pre;
-  auto load = [&](int cidx) {
+  Pre pre0, pre1;                                // two sets: loads run two steps ahead
+  auto load = [&](Pre &pre, int cidx) {
     const uint8_t *rp = reinterpret_cast<const uint8_t *>(rp0 + static_cast<size_t>(cidx) * H);
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
@@ -122,9 +122,9 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     pre.valid = *reinterpret_cast<const uint32_t *>(rp + offsetof(Rec, valid) + vzero);
     const uint32_t tv = static_cast<uint32_t>(min(t_begin + cidx * C + hr, t_end - 1));
     pre.v = *reinterpret_cast<const u32x4 *>(vrow + (piece + tv * tok_bytes));
-    __asm__ volatile("" ::: "memory");   // keep the loads here, a step ahead of their use
+    __asm__ volatile("" ::: "memory");   // keep the loads here, ahead of their use
   };
-  auto stage = [&](Hand &hd) {
+  auto stage = [&](Hand &hd, const Pre &pre) {
     u32x4 *dst = reinterpret_cast<u32x4 *>(&hd.rec);
 #pragma unroll
     for (int i = 0; i < PPT; ++i)
@@ -164,91 +164,130 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
       for (int i = 0; i < 4; ++i) Sacc[t][i] = init[slab + static_cast<size_t>(16 * t + 4 * lg + i) * DV + col0 + wcol];
   }
 
-  auto products = [&](const Hand &hc, float *ost) {
-    const u32x4 *KB = reinterpret_cast<const u32x4 *>(hc.rec.kb);
-    const u32x4 *QT = reinterpret_cast<const u32x4 *>(hc.rec.qt);
-    const u32x4 *KE = reinterpret_cast<const u32x4 *>(hc.rec.ket);
-    const u32x4 *BQ = reinterpret_cast<const u32x4 *>(hc.rec.bq);
-    // S0 as fp16 B operands; K step s covers channels {32s+4lg+0..3, 32s+16+4lg+0..3}
-    uint4 Sh[DK / 32];
+  // S0 as fp16 B operands; K step s covers channels {32s+4lg+0..3, 32s+16+4lg+0..3}.
+  // Formed at the end of the previous chunk, so the conversion overlaps its last products.
+  uint4 Sh[DK / 32];
+  auto to_f16 = [&]() {
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s) {
       const f32x4 a = Sacc[2 * s], bb = Sacc[2 * s + 1];
       Sh[s] = join(pack_f16x4(a[0], a[1], a[2], a[3]), pack_f16x4(bb[0], bb[1], bb[2], bb[3]));
     }
-    // Y = V - (k^ exp(G)) S0 in fp16 (W carries the extra precision)
-    uint2 yf[2];
+  };
+  to_f16();
+
+  // One chunk's products.  The LDS reads of each phase are issued together ahead of their
+  // first use (the empty asm statements keep them there), so their latency overlaps the
+  // matrix-core work of the previous phase instead of stalling each product.
+  auto products = [&](const Hand &hc, float *ost) {
+    const u32x4 *KB = reinterpret_cast<const u32x4 *>(hc.rec.kb);
+    const u32x4 *QT = reinterpret_cast<const u32x4 *>(hc.rec.qt);
+    const u32x4 *KE = reinterpret_cast<const u32x4 *>(hc.rec.ket);
+    const u32x4 *BQ = reinterpret_cast<const u32x4 *>(hc.rec.bq);
+    // phase 1 operands: k^ exp(G) fragments, W, the value tile
+    uint4 kbf[8];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < DK / 32; ++s)
-        acc = mfma_f16(__builtin_bit_cast(uint4, KB[(4 * m + s) * 64 + lane]), Sh[s], acc);
-      f32x4 yy;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) yy[i] = bf16_to_f32(hc.vt[(SB * m + 4 * lg + i) * LDV + wcol]) - acc[i];
-      yf[m] = pack_f16x4(yy[0], yy[1], yy[2], yy[3]);
-    }
-    // U0 = W00 Y0, U1 = W10 Y0 + W11 Y1, with W as hi + lo parts
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < 8; ++f) kbf[f] = __builtin_bit_cast(uint4, KB[f * 64 + lane]);
     const uint2 w00 = __builtin_bit_cast(uint2, reinterpret_cast<const u32x2 *>(hc.rec.w00)[lane]);
     const uint2 w00l = __builtin_bit_cast(uint2, reinterpret_cast<const u32x2 *>(hc.rec.w00lo)[lane]);
-    f32x4 U0 = mfma_f16k16(w00l, yf[0], zero);
-    U0 = mfma_f16k16(w00, yf[0], U0);
     const uint4 w1 = __builtin_bit_cast(uint4, reinterpret_cast<const u32x4 *>(hc.rec.w1)[lane]);
     const uint4 w1l = __builtin_bit_cast(uint4, reinterpret_cast<const u32x4 *>(hc.rec.w1lo)[lane]);
+    float vv[2][4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[m][i] = bf16_to_f32(hc.vt[(SB * m + 4 * lg + i) * LDV + wcol]);
+    __asm__ volatile("" ::: "memory");
+    // Y = V - (k^ exp(G)) S0 in fp16 (W carries the extra precision)
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+      acc0 = mfma_f16(kbf[s], Sh[s], acc0);
+      acc1 = mfma_f16(kbf[4 + s], Sh[s], acc1);
+    }
+    // phase 2 operands: the transposed decayed keys, the chunk decay
+    uint4 kef[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) kef[t] = __builtin_bit_cast(uint4, KE[t * 64 + lane]);
+    float4 ecv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ecv[t] = *reinterpret_cast<const float4 *>(hc.rec.ec + 16 * t + 4 * lg);
+    __asm__ volatile("" ::: "memory");
+    uint2 yf[2];
+    yf[0] = pack_f16x4(vv[0][0] - acc0[0], vv[0][1] - acc0[1], vv[0][2] - acc0[2], vv[0][3] - acc0[3]);
+    yf[1] = pack_f16x4(vv[1][0] - acc1[0], vv[1][1] - acc1[1], vv[1][2] - acc1[2], vv[1][3] - acc1[3]);
+    // U0 = W00 Y0, U1 = W10 Y0 + W11 Y1, with W as hi + lo parts
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 U0 = mfma_f16k16(w00l, yf[0], zero);
+    U0 = mfma_f16k16(w00, yf[0], U0);
     const uint4 y01 = join(yf[0], yf[1]);
     f32x4 U1 = mfma_f16(w1l, y01, zero);
     U1 = mfma_f16(w1, y01, U1);
+    // the decay over the chunk, applied while the products above run
+#pragma unroll
+    for (int t = 0; t < DK / 16; ++t) {
+      Sacc[t][0] *= ecv[t].x; Sacc[t][1] *= ecv[t].y; Sacc[t][2] *= ecv[t].z; Sacc[t][3] *= ecv[t].w;
+    }
     uint2 u0h, u0l, u1h, u1l;
     split_f16x4(U0, u0h, u0l);
     split_f16x4(U1, u1h, u1l);
     const uint4 Uh = join(u0h, u1h);   // tokens {4lg+0..3, 16+4lg+0..3} as K=32 B operands
     const uint4 Ul = join(u0l, u1l);
+    // phase 3 operands: q^ exp(G) fragments, Bqk
+    uint4 qtf[8], bqf[2];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) qtf[f] = __builtin_bit_cast(uint4, QT[f * 64 + lane]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) bqf[m] = __builtin_bit_cast(uint4, BQ[m * 64 + lane]);
+    __asm__ volatile("" ::: "memory");
     // S = diag(exp(G_last)) S0 + (k^ exp(G_last - G))^T U
 #pragma unroll
     for (int t = 0; t < DK / 16; ++t) {
-      const float4 e = *reinterpret_cast<const float4 *>(hc.rec.ec + 16 * t + 4 * lg);
-      Sacc[t][0] *= e.x; Sacc[t][1] *= e.y; Sacc[t][2] *= e.z; Sacc[t][3] *= e.w;
-      const uint4 kv = __builtin_bit_cast(uint4, KE[t * 64 + lane]);
-      Sacc[t] = mfma_f16(kv, Ul, Sacc[t]);
-      Sacc[t] = mfma_f16(kv, Uh, Sacc[t]);
+      Sacc[t] = mfma_f16(kef[t], Ul, Sacc[t]);
+      Sacc[t] = mfma_f16(kef[t], Uh, Sacc[t]);
     }
     // O = (q^ exp(G)) S0 + Bqk U
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < DK / 32; ++s)
-        acc = mfma_f16(__builtin_bit_cast(uint4, QT[(4 * m + s) * 64 + lane]), Sh[s], acc);
-      const uint4 bqv = __builtin_bit_cast(uint4, BQ[m * 64 + lane]);
-      acc = mfma_f16(bqv, Ul, acc);
-      acc = mfma_f16(bqv, Uh, acc);
+      for (int s = 0; s < DK / 32; ++s) acc = mfma_f16(qtf[4 * m + s], Sh[s], acc);
+      acc = mfma_f16(bqf[m], Ul, acc);
+      acc = mfma_f16(bqf[m], Uh, acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) ost[(SB * m + 4 * lg + i) * LDO + wcol] = acc[i];
     }
+    to_f16();                                    // S0 of the next chunk
   };
 
   if (nchunks > 0) {
     const int last = nchunks - 1;
     if (helper) {
-      load(0);
-      stage(sm.hand[0]);
-      load(min(1, last));
+      load(pre0, 0);
+      load(pre1, min(1, last));
+      stage(sm.hand[0], pre0);
+      load(pre0, min(2, last));
     }
     sync_lds();
-    // step s: helpers stage chunk s+1 (loaded at step s-1), load chunk s+2 and write chunk
-    // s-1's rows; compute waves run chunk s.  Chunks past the end repeat the last.
-    for (int s = 0; s < nchunks; ++s) {
+    // step s: helpers stage chunk s+1 (loaded at step s-2), load chunk s+3 into the freed
+    // set and write chunk s-1's rows; compute waves run chunk s.  Chunks past the end
+    // repeat the last.
+    auto step = [&](int s, Pre &from) {
       if (helper) {
-        stage(sm.hand[(s + 1) & 1]);
-        load(min(s + 2, last));
+        stage(sm.hand[(s + 1) & 1], from);
+        load(from, min(s + 3, last));
         if (s >= 1) emit(s - 1, sm.ost[(s + 1) & 1]);
       } else {
         products(sm.hand[s & 1], sm.ost[s & 1]);
       }
       sync_lds();
+    };
+    int s = 0;
+    for (; s + 1 < nchunks; s += 2) {
+      step(s, pre1);                             // chunk s+1 is in pre1, s+2 in pre0
+      step(s + 1, pre0);
     }
+    if (s < nchunks) step(s, pre1);
     if (helper) emit(last, sm.ost[last & 1]);
   }
 
