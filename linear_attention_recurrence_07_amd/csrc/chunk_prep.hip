@@ -13,15 +13,23 @@
 // the scan only has to run U = W (V - (k^ exp(G)) S0), O = (q^ exp(G)) S0 + Bqk U and the
 // state carry.
 //
-// Decay factoring for the intra-chunk products.  exp(G_s - G_j) is split into a row and a
-// column factor around a reference point: the boundary between the two 16-token
-// sub-blocks for the off-diagonal block (both factors <= 1, fp16), the 8th token of the
-// sub-block for a diagonal block (|exponent| <= 8 * 5 = 40 when g >= -5, so bf16).  The
-// diagonal Bqk blocks take bf16 hi + lo operands (three products), A's diagonal blocks
-// single bf16.
-//
-// Work-group: one (sequence, head, chunk), 512 threads; thread (wave w, lane l) owns
-// tokens 4w..4w+3 and channels 2l, 2l+1.  Two work-groups fit one CU.
+// Work-group: one (sequence, head, chunk), two waves; wave m owns the 16-token sub-block
+// m.  Each lane loads its token's channels directly in MFMA operand order (lane 16 lg + r:
+// token r of the sub-block, channels 32 s + kidx(lg, e) of K block s), so
+//   * G is a prefix sum over the 16 lanes of a row (DPP row shifts), in log2 units, and
+//     every decay factor is one exp2 of a difference of running sums;
+//   * the decayed key and query fragments go from registers straight to the record;
+//   * the intra-chunk products take both operands from registers (the off-diagonal block
+//     reads sub-block 0's operand from LDS), with the operands swapped where the record
+//     wants the transposed product;
+//   * k^ exp(G_last - G) is transposed to its channel-major fragments by a matrix-core
+//     product with a 0/1 selection operand (exact: one nonzero term per output).
+// Decay factoring for the intra-chunk products: exp(G_s - G_j) is split into a row and a
+// column factor around a reference token, the 8th token of the sub-block for a diagonal
+// block (|exponent| <= 8 * 5 = 40 when g >= -5, bf16 operands; Bqk's diagonal blocks take
+// bf16 hi + lo parts, three products), the sub-block boundary for the off-diagonal block
+// (both factors <= 1, fp16).  The diagonal blocks of I + A are inverted by forward
+// substitution; the off-diagonal block of W comes from two fp32 matrix-core products.
 #include "kda_chunk.h"
 #include "kda_launch.h"
 
@@ -29,121 +37,66 @@ namespace kda {
 namespace {
 using namespace chunk;
 
-constexpr int NW = 8;
-constexpr int NT = NW * 64;
-constexpr int TPW = C / NW;       // tokens per wave (4)
-constexpr int LDK = DK + 8;       // [token][channel] operand rows, 16-byte reads
-constexpr int LDA = SB * SB + 8;  // fp32 16x16 diagonal blocks of A, transposed
+constexpr int NT = 128;
 
-// LDS layout (bytes).  The operand arrays are dead once the intra-chunk products are
-// formed; the record's fragments of k^ exp(G), q^ exp(G) and the transposed decayed keys
-// are staged over their tail, in a padded layout (16 bytes after every 16 lanes) so the
-// scattered 4- and 8-byte staging writes spread over the banks.  The rest of the record
-// (Bqk, W, exp(G_last), flags) is staged after them, unpadded.
-constexpr int OPB = C * LDK * 2;                // one [32][LDK] 16-bit operand array
-constexpr int O_RKD = 0, O_RQH = OPB, O_RQL = 2 * OPB, O_CKH = 3 * OPB, O_CKL = 4 * OPB;
-constexpr int O_KOF = 5 * OPB, O_RQ1 = 6 * OPB;
-constexpr int OPS_END = 6 * OPB + SB * LDK * 2;
-constexpr int LGB = 16 * 16 + 16;               // one padded group of 16 lanes
-constexpr int TILEB = 4 * LGB;                  // one padded fragment (64 lanes)
-constexpr int REGB = 8 * TILEB;                 // 8 fragments
-constexpr int O_STG = OPS_END - 3 * REGB;       // kb, qt, ket staging (overlaps the operands)
-constexpr int O_TAIL = OPS_END;                 // bq, w1, w00, ec, valid (as in the record)
-constexpr int TAIL_BYTES = static_cast<int>(sizeof(Rec)) - 3 * 8 * 64 * 16;
-constexpr int O_GTOT = O_TAIL + TAIL_BYTES;
-constexpr int O_BETA = O_GTOT + NW * DK * 4;
-constexpr int O_AT = O_BETA + C * 4;
-constexpr int O_TM = O_AT + 2 * LDA * 4;
-constexpr int O_A10 = O_TM + 2 * SB * (SB + 1) * 4;
-constexpr int O_P = O_A10 + SB * (SB + 1) * 4;
-constexpr int O_VB = O_P + SB * (SB + 1) * 4;
-constexpr int LDS_BYTES = O_VB + C;
-static_assert(O_STG >= 0 && O_STG % 16 == 0 && O_GTOT % 16 == 0 && O_AT % 16 == 0, "alignment");
-static_assert(LDS_BYTES <= 80 * 1024, "two work-groups per CU");
-
-// Key-side 16x16 blocks.  Result layout: acc[i] = block[4*lg + i][l16].
-__device__ __forceinline__ f32x4 a_diag(const uint16_t *rkd, const uint16_t *ckh, int a, int l16, int lg) {
-  const uint16_t *rp = rkd + (SB * a + l16) * LDK + 8 * lg;
-  const uint16_t *cp = ckh + (SB * a + l16) * LDK + 8 * lg;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < DK / 32; ++s) acc = mfma_bf16(lds_u4(rp + 32 * s), lds_u4(cp + 32 * s), acc);
-  return acc;
-}
-__device__ __forceinline__ f32x4 bqk_diag(const uint16_t *rqh, const uint16_t *rql, const uint16_t *ckh,
-                                          const uint16_t *ckl, int a, int l16, int lg) {
-  const int ro = (SB * a + l16) * LDK + 8 * lg;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < DK / 32; ++s) {
-    const uint4 rh = lds_u4(rqh + ro + 32 * s), rl = lds_u4(rql + ro + 32 * s);
-    const uint4 ch = lds_u4(ckh + ro + 32 * s), cl = lds_u4(ckl + ro + 32 * s);
-    acc = mfma_bf16(rl, ch, acc);
-    acc = mfma_bf16(rh, cl, acc);
-    acc = mfma_bf16(rh, ch, acc);
-  }
-  return acc;
-}
-__device__ __forceinline__ f32x4 off_block(const uint16_t *rows, const uint16_t *kof, int l16, int lg) {
-  const uint16_t *rp = rows + l16 * LDK + 8 * lg;
-  const uint16_t *cp = kof + l16 * LDK + 8 * lg;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < DK / 32; ++s) acc = mfma_f16(lds_u4(rp + 32 * s), lds_u4(cp + 32 * s), acc);
-  return acc;
-}
-// Element (r, c) of a 32x32 token-by-token matrix in the bq fragments.
-__device__ __forceinline__ int bq_elem(int r, int c) {
-  return ((r >> 4) * 64 + 16 * kidx_lg(c) + (r & 15)) * 8 + kidx_e(c);
-}
-// The part of the record after the three channel-fragment arrays.
-struct Tail {
-  uint16_t bq[2][64][8];
-  uint16_t w1[64][8];
-  uint16_t w00[64][4];
-  uint16_t w1lo[64][8];
-  uint16_t w00lo[64][4];
-  float ec[DK];
-  uint32_t valid;
-  uint32_t pad[3];
+struct Shared {
+  float gx[2][2][DK];      // per sub-block: running sum of g (log2) at its 8th and its last token
+  float sb[C];             // beta (0 for padding)
+  u32x4 kof0[4][64];       // sub-block 0: fp16 k^ exp(G_15 - G) fragments, one per K block
+  float at[2][SB][SB + 4]; // A's diagonal blocks, transposed: at[a][j][s] = A[16a+s][16a+j]
+  float tm[2][SB][SB + 1]; // (I + A_aa)^-1
+  float a10[SB][SB + 1];   // A(1,0)
+  float pp[SB][SB + 1];    // A(1,0) (I + A_00)^-1
+  u32x2 kx[2][4][64];      // k^ exp(G_last - G) fragment halves handed to the other wave
 };
-static_assert(sizeof(Tail) == TAIL_BYTES && offsetof(Rec, bq) == 3 * 8 * 64 * 16, "record tail");
-// x = hi + lo with both parts fp16.
-__device__ __forceinline__ void split_f16(float x, uint16_t &hi, uint16_t &lo) {
-  const _Float16 h = static_cast<_Float16>(x);
-  hi = __builtin_bit_cast(uint16_t, h);
-  lo = f16_bits(x - static_cast<float>(h));
+static_assert(sizeof(Shared) <= 20 * 1024, "LDS per work-group");
+
+// Value of lane r - N of the same 16-lane row (0 for r < N).
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, true));
 }
-// Byte offset of lane L of fragment `tile` in the padded staging layout.
-__device__ __forceinline__ int stg_off(int tile, int L) { return tile * TILEB + (L >> 4) * LGB + (L & 15) * 16; }
+// Inclusive prefix sum over the 16 lanes of each row.
+__device__ __forceinline__ float row_prefix(float x) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  x += row_shr<8>(x);
+  return x;
+}
+// Sum over the four lanes r, r + 16, r + 32, r + 48.
+__device__ __forceinline__ float col_sum4(float x) {
+  x += __shfl_xor(x, 16, 64);
+  return x + __shfl_xor(x, 32, 64);
+}
+__device__ __forceinline__ f32x4 mfma_f32k4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// x = hi + lo with both parts fp16, four values -> two fp16 pairs each.
+__device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
+  uint2 h, l;
+  split_f16x4(x, h, l);
+  hi = u32x2{h.x, h.y};
+  lo = u32x2{l.x, l.y};
+}
+__device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
+__device__ __forceinline__ f32x4 mma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
 
 template <bool HAS_MASK>
-__global__ void __launch_bounds__(NT, 2)
+__global__ void __launch_bounds__(NT)
 chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const float *__restrict__ g, const float *__restrict__ beta,
                   const int32_t *__restrict__ cu, const uint8_t *__restrict__ mask,
                   Rec *__restrict__ ws, int T, int H, int N, float scale, int use_l2) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-  uint16_t *rkd = reinterpret_cast<uint16_t *>(lds + O_RKD);   // bf16 k exp(G - G_mid(block))
-  uint16_t *rqh = reinterpret_cast<uint16_t *>(lds + O_RQH);   // bf16 q exp(G - G_mid(block)), hi
-  uint16_t *rql = reinterpret_cast<uint16_t *>(lds + O_RQL);   //                                lo
-  uint16_t *ckh = reinterpret_cast<uint16_t *>(lds + O_CKH);   // bf16 k exp(G_mid(block) - G), hi
-  uint16_t *ckl = reinterpret_cast<uint16_t *>(lds + O_CKL);   //                                lo
-  uint16_t *kof = reinterpret_cast<uint16_t *>(lds + O_KOF);   // fp16 k exp(G_15 - G) | k exp(G - G_15)
-  uint16_t *rq1 = reinterpret_cast<uint16_t *>(lds + O_RQ1);   // fp16 q exp(G - G_15), block 1 rows
-  uint8_t *stg = lds + O_STG;                                    // staged kb, qt, ket (padded)
-  Tail &st = *reinterpret_cast<Tail *>(lds + O_TAIL);           // staged rest of the record
-  float *gtot = reinterpret_cast<float *>(lds + O_GTOT);        // decay product of each 4-token group
-  float *sbeta = reinterpret_cast<float *>(lds + O_BETA);
-  float *at = reinterpret_cast<float *>(lds + O_AT);            // A_aa transposed: at[a][j][s]
-  auto tm = reinterpret_cast<float (*)[SB][SB + 1]>(lds + O_TM);   // (I + A_aa)^-1
-  auto a10 = reinterpret_cast<float (*)[SB + 1]>(lds + O_A10);     // A(1,0)
-  auto pp = reinterpret_cast<float (*)[SB + 1]>(lds + O_P);        // A(1,0) (I + A_00)^-1
-  uint8_t *vb = lds + O_VB;                                        // token flags
-
+  __shared__ Shared sh;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15, lg = lane >> 4;
+  const int m = __builtin_amdgcn_readfirstlane(tid >> 6);   // sub-block of this wave
+  const int r = lane & 15, lg = lane >> 4;
 
   // ---------------------------------------------------------------- locate the chunk
   const int h = static_cast<int>(blockIdx.x) % H;
@@ -171,262 +124,264 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
   if (c < 0 || c * C >= t_end - t_begin) return;   // no chunk in this slot (whole work-group)
   const int c0 = t_begin + c * C;
   Rec *rec = ws + static_cast<size_t>(slot) * H + h;
-
-  const int tok_stride = H * DK;
   const size_t row0 = static_cast<size_t>(b) * T;
-  const uint16_t *kp = k + row0 * tok_stride + h * DK + 2 * lane;
-  const uint16_t *qp = q + row0 * tok_stride + h * DK + 2 * lane;
-  const float *gp = g + row0 * tok_stride + h * DK + 2 * lane;
-  const float *bp = beta + row0 * H + h;
 
-  // ---------------------------------------------------------------- phase 1
-  // Load, normalise q/k, per-group decay products.
-  float kx[TPW][2], qx[TPW][2], fw[TPW][2], bw[TPW][2];
+  // ---------------------------------------------------------------- load (operand order)
+  const int tok = c0 + SB * m + r;
+  const int tcl = min(tok, t_end - 1);
+  bool valid = tok < t_end;
+  if constexpr (HAS_MASK) valid = valid && mask[row0 + tcl] != 0;
+  const int off = tcl * (H * DK) + h * DK + 4 * lg;
+  const uint16_t *kp = k + row0 * H * DK + off;
+  const uint16_t *qp = q + row0 * H * DK + off;
+  const float *gp = g + row0 * H * DK + off;
+  u32x2 kr[4][2], qr[4][2];
+  f32x4 G[4][2];
 #pragma unroll
-  for (int j = 0; j < TPW; ++j) {
-    const int t = c0 + TPW * wave + j;
-    const int tc = min(t, t_end - 1);
-    bool valid = t < t_end;
-    if constexpr (HAS_MASK) valid = valid && mask[row0 + tc] != 0;
-    const int off = tc * tok_stride;
-    const uint32_t kk = *reinterpret_cast<const uint32_t *>(kp + off);
-    const uint32_t qq = *reinterpret_cast<const uint32_t *>(qp + off);
-    const float2 gg = *reinterpret_cast<const float2 *>(gp + off);
-    const float bb = bp[tc * H];
-    // padding and tokens past the sequence act as no-ops
-    kx[j][0] = valid ? lo_bf16(kk) : 0.f; kx[j][1] = valid ? hi_bf16(kk) : 0.f;
-    qx[j][0] = valid ? lo_bf16(qq) : 0.f; qx[j][1] = valid ? hi_bf16(qq) : 0.f;
-    fw[j][0] = valid ? gg.x : 0.f; fw[j][1] = valid ? gg.y : 0.f;
-    if (lane == 0) {
-      sbeta[TPW * wave + j] = valid ? bb : 0.f;
-      vb[TPW * wave + j] = valid;
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      kr[s][hh] = *reinterpret_cast<const u32x2 *>(kp + 32 * s + 16 * hh);
+      qr[s][hh] = *reinterpret_cast<const u32x2 *>(qp + 32 * s + 16 * hh);
+      G[s][hh] = *reinterpret_cast<const f32x4 *>(gp + 32 * s + 16 * hh);
     }
-  }
+  const float bt = beta[(row0 + tcl) * H + h];
+
+  // ---------------------------------------------------------------- norms, running sums
+  // Padding and tokens past the end act as no-ops: zero key, query, beta and decay.
+  float nk, nq;
   {
-    float ss[2 * TPW];
+    float ssk = 0.f, ssq = 0.f;
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      ss[j] = kx[j][0] * kx[j][0] + kx[j][1] * kx[j][1];
-      ss[TPW + j] = qx[j][0] * qx[j][0] + qx[j][1] * qx[j][1];
-    }
-    float x0, x1;
-    wave_sum8(ss, x0, x1);
-    // rows 0-1 of x0/x1 hold key sums, rows 2-3 query sums
-    const float qs = lane >= 32 ? scale : 1.f;
-    const float n0 = (use_l2 ? rsqrtf(x0 + kL2Eps) : 1.f) * qs;
-    const float n1 = (use_l2 ? rsqrtf(x1 + kL2Eps) : 1.f) * qs;
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      const float kn = readlane(j & 1 ? n1 : n0, 16 * (j >> 1));
-      const float qn = readlane(j & 1 ? n1 : n0, 32 + 16 * (j >> 1));
-      kx[j][0] *= kn; kx[j][1] *= kn;
-      qx[j][0] *= qn; qx[j][1] *= qn;
-    }
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const float k0 = lo_bf16(kr[s][hh][w]), k1 = hi_bf16(kr[s][hh][w]);
+          const float q0 = lo_bf16(qr[s][hh][w]), q1 = hi_bf16(qr[s][hh][w]);
+          ssk += k0 * k0 + k1 * k1;
+          ssq += q0 * q0 + q1 * q1;
+        }
+    ssk = col_sum4(ssk);
+    ssq = col_sum4(ssq);
+    nk = valid ? (use_l2 ? rsqrtf(ssk + kL2Eps) : 1.f) : 0.f;
+    nq = valid ? (use_l2 ? rsqrtf(ssq + kL2Eps) : 1.f) * scale : 0.f;
   }
-  // fw[j] = prod_{i<=j} e_i (inclusive), bw[j] = prod_{j<i<4} e_i (exclusive)
+  const float gsc = valid ? kLog2e : 0.f;
 #pragma unroll
-  for (int ch = 0; ch < 2; ++ch) {
-    float e[TPW];
+  for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) e[j] = fast_exp2(fw[j][ch] * kLog2e);
-    float run = 1.f;
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      run *= e[j];
-      fw[j][ch] = run;
-    }
-    run = 1.f;
+      for (int i = 0; i < 4; ++i) G[s][hh][i] = row_prefix(G[s][hh][i] * gsc);
+  if (r == 7 || r == 15) {
 #pragma unroll
-    for (int j = TPW - 1; j >= 0; --j) {
-      bw[j][ch] = run;
-      run *= e[j];
-    }
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        *reinterpret_cast<f32x4 *>(&sh.gx[m][r >> 3][32 * s + 16 * hh + 4 * lg]) = G[s][hh];
   }
-  *reinterpret_cast<float2 *>(gtot + wave * DK + 2 * lane) = make_float2(fw[TPW - 1][0], fw[TPW - 1][1]);
-  sync_lds();
-
-  // ---------------------------------------------------------------- phase 2
-  // Row and column factors of the intra-chunk products (to LDS) and the decayed operands
-  // (kept in registers until the operand area is free).
-  const int blk = wave >> 2;                     // sub-block of this wave's tokens
-  const int gi = wave & 3;                       // group within the sub-block
-  uint32_t okb[TPW], oqt[TPW];                   // fp16 pairs (channels 2l, 2l+1) per token
-  uint2 oke[2];                                  // fp16 k^ exp(G_last - G) of the 4 tokens, per channel
-  float ecv[2];
-  {
-    float e3m[2], e4m[2], ih1[2], ih2[2], pre[2], post[2];
-#pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
-      float gt[NW];
-#pragma unroll
-      for (int m = 0; m < NW; ++m) gt[m] = gtot[m * DK + 2 * lane + ch];
-      const float b0 = blk ? gt[4] : gt[0], b1 = blk ? gt[5] : gt[1];
-      const float b2 = blk ? gt[6] : gt[2], b3 = blk ? gt[7] : gt[3];
-      const float p01 = b0 * b1, p23 = b2 * b3;
-      e3m[ch] = gi == 0 ? 1.f : gi == 1 ? b0 : gi == 2 ? p01 : p01 * b2;   // block start -> group
-      e4m[ch] = gi == 3 ? 1.f : gi == 2 ? b3 : gi == 1 ? p23 : b1 * p23;   // group -> block end
-      ih1[ch] = __builtin_amdgcn_rcpf(p01);      // block start -> 8th token
-      ih2[ch] = __builtin_amdgcn_rcpf(p23);      // 8th token -> block end
-      const float d0 = (gt[0] * gt[1]) * (gt[2] * gt[3]);     // decay over block 0
-      const float d1 = (gt[4] * gt[5]) * (gt[6] * gt[7]);     // decay over block 1
-      pre[ch] = blk ? d0 * e3m[ch] : e3m[ch];    // chunk start -> group start
-      post[ch] = blk ? e4m[ch] : e4m[ch] * d1;   // group end -> chunk end
-      ecv[ch] = d0 * d1;
-    }
-    float ke[TPW][2];
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      const int r = TPW * wave + j;
-      float k3[2], q3[2], k4[2], rk[2], rq[2], ck[2], kb[2], qt[2];
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        const float e3 = e3m[ch] * fw[j][ch];    // exp(G_r - G_block_start)
-        const float e4 = bw[j][ch] * e4m[ch];    // exp(G_block_end - G_r)
-        k3[ch] = kx[j][ch] * e3;
-        q3[ch] = qx[j][ch] * e3;
-        k4[ch] = kx[j][ch] * e4;
-        rk[ch] = k3[ch] * ih1[ch];               // k exp(G_r - G_mid)
-        rq[ch] = q3[ch] * ih1[ch];
-        ck[ch] = k4[ch] * ih2[ch];               // k exp(G_mid - G_r)
-        const float ef = pre[ch] * fw[j][ch];    // exp(G_r)
-        kb[ch] = kx[j][ch] * ef;
-        qt[ch] = qx[j][ch] * ef;
-        ke[j][ch] = kx[j][ch] * (bw[j][ch] * post[ch]);   // k^ exp(G_last - G_r)
-      }
-      okb[j] = pack_f16x2(kb[0], kb[1]);
-      oqt[j] = pack_f16x2(qt[0], qt[1]);
-      const int o2 = r * LDK + 2 * lane;
-      *reinterpret_cast<uint32_t *>(rkd + o2) = pack_bf16x2(rk[0], rk[1]);
-      uint32_t hi, lo;
-      split_bf16x2(rq[0], rq[1], hi, lo);
-      *reinterpret_cast<uint32_t *>(rqh + o2) = hi;
-      *reinterpret_cast<uint32_t *>(rql + o2) = lo;
-      split_bf16x2(ck[0], ck[1], hi, lo);
-      *reinterpret_cast<uint32_t *>(ckh + o2) = hi;
-      *reinterpret_cast<uint32_t *>(ckl + o2) = lo;
-      // off-diagonal factors around token 15
-      *reinterpret_cast<uint32_t *>(kof + o2) =
-          blk ? pack_f16x2(k3[0], k3[1]) : pack_f16x2(k4[0], k4[1]);
-      if (blk) *reinterpret_cast<uint32_t *>(rq1 + o2 - SB * LDK) = pack_f16x2(q3[0], q3[1]);
-    }
-#pragma unroll
-    for (int ch = 0; ch < 2; ++ch) oke[ch] = pack_f16x4(ke[0][ch], ke[1][ch], ke[2][ch], ke[3][ch]);
-  }
-  sync_lds();
-
-  // ---------------------------------------------------------------- phase 3
-  // A and Bqk blocks on the matrix cores, inverses of the diagonal blocks of I + A.
-  if (wave == 0) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const f32x4 acc = a_diag(rkd, ckh, a, l16, lg);
-      float4 w;   // A[s][j] = beta_s * acc for j < s, stored transposed at at[a][j][s]
-      const float *bs = sbeta + SB * a + 4 * lg;
-      w.x = (l16 < 4 * lg + 0) ? bs[0] * acc[0] : 0.f;
-      w.y = (l16 < 4 * lg + 1) ? bs[1] * acc[1] : 0.f;
-      w.z = (l16 < 4 * lg + 2) ? bs[2] * acc[2] : 0.f;
-      w.w = (l16 < 4 * lg + 3) ? bs[3] * acc[3] : 0.f;
-      *reinterpret_cast<float4 *>(at + a * LDA + l16 * SB + 4 * lg) = w;
-    }
+  if (lg == 0) sh.sb[SB * m + r] = valid ? bt : 0.f;
+  auto kval = [&](int s, int e) {
+    const uint32_t w = kr[s][e >> 2][(e >> 1) & 1];
+    return (e & 1 ? hi_bf16(w) : lo_bf16(w)) * nk;
+  };
+  auto qval = [&](int s, int e) {
+    const uint32_t w = qr[s][e >> 2][(e >> 1) & 1];
+    return (e & 1 ? hi_bf16(w) : lo_bf16(w)) * nq;
+  };
+  if (m == 0) {
+    // sub-block 0's off-diagonal operand k^ exp(G_15 - G), needed by the other wave
     wave_sync_lds();
-    // (I + A_aa)^-1, column cc, by forward substitution; lanes 32-63 repeat 0-31
-    const int a = (lane >> 4) & 1, cc = l16;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float x[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f32x4 t0 = *reinterpret_cast<const f32x4 *>(&sh.gx[0][1][32 * s + 16 * hh + 4 * lg]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * hh + i] = kval(s, 4 * hh + i) * fast_exp2(t0[i] - G[s][hh][i]);
+      }
+      sh.kof0[s][lane] = u32x4{pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]),
+                               pack_f16x2(x[4], x[5]), pack_f16x2(x[6], x[7])};
+    }
+  }
+  sync_lds();
+
+  // ---------------------------------------------------------------- operands and products
+  // Selection operands for the transpose of k^ exp(G_last - G): slot e of lane (lg, n) is 1
+  // when kidx(lg, e) = n (first half of the K block) or 16 + n (second half).
+  const uint32_t one = (lg == (r >> 2)) ? (0x3C00u << (16 * (r & 1))) : 0u;
+  const bool wsel = (r & 2) != 0;
+  const u32x4 id0 = {wsel ? 0u : one, wsel ? one : 0u, 0u, 0u};
+  const u32x4 id1 = {0u, 0u, wsel ? 0u : one, wsel ? one : 0u};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 accA = zero, accB = zero, accA10 = zero, accB10 = zero;
+  u32x2 kown[4];   // this wave's halves of its own four transposed fragments
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    float rk[8], ck[8], rq[8], kb[8], qt[8], ke[8], k1[8], q1[8];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int ch = 32 * s + 16 * hh + 4 * lg;
+      const f32x4 gm = *reinterpret_cast<const f32x4 *>(&sh.gx[m][0][ch]);
+      const f32x4 t0 = *reinterpret_cast<const f32x4 *>(&sh.gx[0][1][ch]);
+      const f32x4 t1 = *reinterpret_cast<const f32x4 *>(&sh.gx[1][1][ch]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * hh + i;
+        const float gl = G[s][hh][i];
+        const float kk = kval(s, e), qq = qval(s, e);
+        const float d1 = gl - gm[i];
+        const float e1 = fast_exp2(d1), e1n = fast_exp2(-d1);
+        // chunk-relative G and the distance to the chunk's last token
+        const float gc = m ? gl + t0[i] : gl;
+        const float tail = m ? t1[i] - gl : (t0[i] + t1[i]) - gl;
+        const float eg = fast_exp2(gc), el = fast_exp2(tail);
+        rk[e] = kk * e1;
+        rq[e] = qq * e1;
+        ck[e] = kk * e1n;
+        kb[e] = kk * eg;
+        qt[e] = qq * eg;
+        ke[e] = kk * el;
+        if (m) {
+          const float e2 = fast_exp2(gl);   // exp(G - G_15) in sub-block 1
+          k1[e] = kk * e2;
+          q1[e] = qq * e2;
+        }
+      }
+    }
+    u32x4 rkb, ckh, ckl, rqh, rql, kbf, qtf, kef;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t h0, l0, h1, l1;
+      rkb[w] = pack_bf16x2(rk[2 * w], rk[2 * w + 1]);
+      split_bf16x2(ck[2 * w], ck[2 * w + 1], h0, l0);
+      split_bf16x2(rq[2 * w], rq[2 * w + 1], h1, l1);
+      ckh[w] = h0; ckl[w] = l0; rqh[w] = h1; rql[w] = l1;
+      kbf[w] = pack_f16x2(kb[2 * w], kb[2 * w + 1]);
+      qtf[w] = pack_f16x2(qt[2 * w], qt[2 * w + 1]);
+      kef[w] = pack_f16x2(ke[2 * w], ke[2 * w + 1]);
+    }
+    reinterpret_cast<u32x4 *>(rec->kb[4 * m + s])[lane] = kbf;
+    reinterpret_cast<u32x4 *>(rec->qt[4 * m + s])[lane] = qtf;
+    // A_mm (rows s, cols j) and Bqk_mm transposed (rows key token, cols query token)
+    accA = mma_bf16(rkb, ckh, accA);
+    accB = mma_bf16(ckl, rqh, accB);
+    accB = mma_bf16(ckh, rql, accB);
+    accB = mma_bf16(ckh, rqh, accB);
+    if (m) {
+      const u32x4 ko = sh.kof0[s][lane];
+      const u32x4 k14 = {pack_f16x2(k1[0], k1[1]), pack_f16x2(k1[2], k1[3]),
+                         pack_f16x2(k1[4], k1[5]), pack_f16x2(k1[6], k1[7])};
+      const u32x4 q14 = {pack_f16x2(q1[0], q1[1]), pack_f16x2(q1[2], q1[3]),
+                         pack_f16x2(q1[4], q1[5]), pack_f16x2(q1[6], q1[7])};
+      accA10 = mma_f16(k14, ko, accA10);    // A(1,0) without beta
+      accB10 = mma_f16(ko, q14, accB10);    // Bqk(1,0) transposed
+    }
+    // transposed fragments 2s and 2s + 1: rows = channels, K = this wave's tokens
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f32x4 t = mma_f16(kef, j ? id1 : id0, zero);
+      const u32x2 half = {pack_f16x2(t[0], t[1]), pack_f16x2(t[2], t[3])};
+      const int tile = 2 * s + j;
+      if ((tile >> 2) == m) kown[tile & 3] = half;
+      else sh.kx[m][tile & 3][lane] = half;
+    }
+  }
+
+  // ---------------------------------------------------------------- intra-chunk blocks
+  const f32x4 bm = *reinterpret_cast<const f32x4 *>(&sh.sb[SB * m + 4 * lg]);   // beta of rows 4lg + i
+  {
+    // accA[i] = A'[4 lg + i][r]: A[s][j] = beta_s A'[s][j] for j < s, stored at[j][s]
+    f32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (r < 4 * lg + i) ? bm[i] * accA[i] : 0.f;
+    *reinterpret_cast<f32x4 *>(&sh.at[m][r][4 * lg]) = w;
+    // accB[i] = Bqk[r][4 lg + i] of this sub-block (query row r, key column 4 lg + i)
+    float bd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bd[i] = (4 * lg + i <= r) ? accB[i] : 0.f;
+    const u32x2 diag = {pack_f16x2(bd[0], bd[1]), pack_f16x2(bd[2], bd[3])};
+    const u32x2 left = m ? u32x2{pack_f16x2(accB10[0], accB10[1]), pack_f16x2(accB10[2], accB10[3])}
+                         : u32x2{0u, 0u};
+    // row r of bq[m]: slots 0-3 = key tokens 4 lg + i, slots 4-7 = key tokens 16 + 4 lg + i
+    reinterpret_cast<u32x4 *>(rec->bq[m])[lane] = m ? cat(left, diag) : cat(diag, u32x2{0u, 0u});
+    if (m) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sh.a10[4 * lg + i][r] = bm[i] * accA10[i];
+    }
+  }
+  wave_sync_lds();
+  {
+    // column r of (I + A_mm)^-1 by forward substitution (lanes 16..63 repeat lanes 0..15)
     float tc[SB];
 #pragma unroll
-    for (int r = 0; r < SB; ++r) tc[r] = (r == cc) ? 1.f : 0.f;
+    for (int i = 0; i < SB; ++i) tc[i] = (i == r) ? 1.f : 0.f;
 #pragma unroll
     for (int j = 0; j < SB - 1; ++j) {
-      const float *col = at + a * LDA + j * SB;   // A[.][j]
+      const float *col = sh.at[m][j];
 #pragma unroll
-      for (int r = j + 1; r < SB; ++r) tc[r] -= col[r] * tc[j];
+      for (int i = j + 1; i < SB; ++i) tc[i] -= col[i] * tc[j];
     }
-    if (lane < 32) {
+    if (lg == 0) {
 #pragma unroll
-      for (int r = 0; r < SB; ++r) tm[a][r][cc] = tc[r];
-    }
-  } else if (wave == 1) {
-    const f32x4 accA = off_block(kof + SB * LDK, kof, l16, lg);
-    const f32x4 accB = off_block(rq1, kof, l16, lg);
-    uint16_t *bq = &st.bq[0][0][0];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sl = 4 * lg + i;
-      a10[sl][l16] = sbeta[SB + sl] * accA[i];
-      bq[bq_elem(SB + sl, l16)] = f16_bits(accB[i]);
-      bq[bq_elem(sl, SB + l16)] = 0;             // above the diagonal blocks
-    }
-  } else if (wave < 4) {
-    const int a = wave - 2;
-    const f32x4 acc = bqk_diag(rqh, rql, ckh, ckl, a, l16, lg);
-    uint16_t *bq = &st.bq[0][0][0];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sl = 4 * lg + i;
-      bq[bq_elem(SB * a + sl, SB * a + l16)] = f16_bits(l16 <= sl ? acc[i] : 0.f);
+      for (int i = 0; i < SB; ++i) sh.tm[m][i][r] = tc[i];
     }
   }
   sync_lds();
 
-  // ---------------------------------------------------------------- phase 4
-  // W = (I + A)^-1 diag(beta) = [[T0 B0, 0], [-T1 A10 T0 B0, T1 B1]], T_a = (I + A_aa)^-1;
-  // the decayed operands into the staged record.
-  {
-    const int e = tid & 255, r = e >> 4, cc = e & 15;
-    if (tid < 256) {
-      float s = 0.f;
+  // ---------------------------------------------------------------- W, the transposed keys, exp(G_last)
+  // W = (I + A)^-1 diag(beta) = [[T0 B0, 0], [-T1 A10 T0 B0, T1 B1]], T_a = (I + A_aa)^-1.
 #pragma unroll
-      for (int m = 0; m < SB; ++m) s += a10[r][m] * tm[0][m][cc];
-      pp[r][cc] = s;
-    } else {
-      const float w00 = tm[0][r][cc] * sbeta[cc];
-      split_f16(w00, st.w00[16 * (cc >> 2) + r][cc & 3], st.w00lo[16 * (cc >> 2) + r][cc & 3]);
-      const int c1 = SB + cc;                    // W(1,1) block of rows 16..31
-      const float w11 = tm[1][r][cc] * sbeta[SB + cc];
-      split_f16(w11, st.w1[16 * kidx_lg(c1) + r][kidx_e(c1)], st.w1lo[16 * kidx_lg(c1) + r][kidx_e(c1)]);
-    }
-    // k^ exp(G) and q^ exp(G): token r = 4w + j, channels 2l, 2l+1 -> tile (r/16, l/16),
-    // lane 16 * lg(ch) + r % 16, slots e(ch) and e(ch) + 1.
-    {
-      const int ch = 2 * lane;
-      const int tile = blk * 4 + (ch >> 5);
-      const int ln = 16 * kidx_lg(ch & 31);
-      const int el = kidx_e(ch & 31);
-#pragma unroll
-      for (int j = 0; j < TPW; ++j) {
-        const int off = stg_off(tile, ln + ((TPW * wave + j) & 15)) + 2 * el;
-        *reinterpret_cast<uint32_t *>(stg + off) = okb[j];
-        *reinterpret_cast<uint32_t *>(stg + REGB + off) = oqt[j];
-      }
-      // transposed: channel ch + cc2 -> tile ch/16, lane 16 * lg(token) + ch % 16, slots of
-      // tokens 4w..4w+3 (consecutive)
-#pragma unroll
-      for (int cc2 = 0; cc2 < 2; ++cc2) {
-        const int chc = ch + cc2;
-        const int off = stg_off(chc >> 4, 16 * kidx_lg(TPW * wave) + (chc & 15)) + 2 * kidx_e(TPW * wave);
-        *reinterpret_cast<uint2 *>(stg + 2 * REGB + off) = oke[cc2];
-      }
-    }
-    if (wave == 0) *reinterpret_cast<float2 *>(&st.ec[2 * lane]) = make_float2(ecv[0], ecv[1]);
-    sync_lds();
-    if (tid < 256) {
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < SB; ++m) s += tm[1][r][m] * pp[m][cc];
-      split_f16(-s * sbeta[cc], st.w1[16 * kidx_lg(cc) + r][kidx_e(cc)], st.w1lo[16 * kidx_lg(cc) + r][kidx_e(cc)]);
-    } else if (tid == 256) {
-      uint32_t v = 0;
-      for (int t = 0; t < C; ++t) v |= static_cast<uint32_t>(vb[t] != 0) << t;
-      st.valid = v;
-    }
-    sync_lds();
+  for (int tt = 0; tt < 4; ++tt) {
+    const u32x2 other = sh.kx[1 - m][tt][lane];
+    reinterpret_cast<u32x4 *>(rec->ket[4 * m + tt])[lane] = m ? cat(other, kown[tt]) : cat(kown[tt], other);
   }
-  // write the record out in 16-byte pieces
-  constexpr int kPieces = static_cast<int>(sizeof(Rec) / 16);
-  constexpr int kFragPieces = 3 * 8 * 64;
-  for (int p = tid; p < kPieces; p += NT) {
-    const int src = p < kFragPieces ? O_STG + (p >> 9) * REGB + stg_off((p >> 6) & 7, p & 63)
-                                    : O_TAIL + (p - kFragPieces) * 16;
-    reinterpret_cast<uint4 *>(rec)[p] = *reinterpret_cast<const uint4 *>(lds + src);
+  // lane (lg, r) holds row r of W's block, key tokens 4 lg + i of the block
+  const f32x4 bc = *reinterpret_cast<const f32x4 *>(&sh.sb[SB * m + 4 * lg]);
+  f32x4 wd;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wd[i] = sh.tm[m][r][4 * lg + i] * bc[i];
+  u32x2 wdh, wdl;
+  split4(wd, wdh, wdl);
+  if (m == 0) {
+    reinterpret_cast<u32x2 *>(rec->w00)[lane] = wdh;
+    reinterpret_cast<u32x2 *>(rec->w00lo)[lane] = wdl;
+    if (r < 8) {   // exp(G_last) of channels 32 s + 16 hh + 4 lg + i, (s, hh) = (r / 2, r % 2)
+      const int ch = 32 * (r >> 1) + 16 * (r & 1) + 4 * lg;
+      const f32x4 t0 = *reinterpret_cast<const f32x4 *>(&sh.gx[0][1][ch]);
+      const f32x4 t1 = *reinterpret_cast<const f32x4 *>(&sh.gx[1][1][ch]);
+      f32x4 ec;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ec[i] = fast_exp2(t0[i] + t1[i]);
+      *reinterpret_cast<f32x4 *>(&rec->ec[ch]) = ec;
+    }
+    const int tt = c0 + (lane & 31);
+    bool v = tt < t_end;
+    if constexpr (HAS_MASK) v = v && mask[row0 + min(tt, t_end - 1)] != 0;
+    const uint64_t bal = __ballot(v);
+    if (lane == 0) rec->valid = static_cast<uint32_t>(bal);
+  } else {
+    // P = A10 T0, then W10^T = -diag(beta0) P^T T1^T (rows = tokens of sub-block 0)
+    f32x4 p = zero;
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4) p = mfma_f32k4(sh.a10[r][4 * kb4 + lg], sh.tm[0][4 * kb4 + lg][r], p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sh.pp[4 * lg + i][r] = p[i];
+    wave_sync_lds();
+    f32x4 wt = zero;
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4) wt = mfma_f32k4(sh.pp[4 * kb4 + lg][r], sh.tm[1][r][4 * kb4 + lg], wt);
+    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&sh.sb[4 * lg]);
+    f32x4 w10;   // W10[r][4 lg + i]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w10[i] = -wt[i] * b0[i];
+    u32x2 wlh, wll;
+    split4(w10, wlh, wll);
+    reinterpret_cast<u32x4 *>(rec->w1)[lane] = cat(wlh, wdh);
+    reinterpret_cast<u32x4 *>(rec->w1lo)[lane] = cat(wll, wdl);
   }
 }
 
