@@ -129,6 +129,39 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p,
 size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed);
 
 /*
+ * kda_chunk_prepare, kda_chunk_scan -- the two launches of kda_chunk_prefill's bf16,
+ * dk = dv = 128 kernel, callable one at a time (same chunked form as kda_chunk_prefill;
+ * nnterp Kimi-Linear page, Notes, "Loading").  kda_chunk_prefill without the gated norm
+ * is exactly kda_chunk_prepare followed by kda_chunk_scan on the same stream.
+ *
+ * kda_chunk_prepare reads q, k, g, beta (and cu_seqlens or mask, as in kda_chunk_prefill)
+ * and fills the workspace with one record per (sequence, head, chunk): everything about a
+ * chunk that does not depend on the incoming state.  It needs no state, so it may run
+ * ahead of the scan that consumes it.
+ *
+ * kda_chunk_scan reads v, initial_state (or NULL) and the records, and writes o and
+ * final_state.  p and cu_seqlens must be those the workspace was prepared with, and the
+ * preparation must have completed or be ordered before the scan on the stream; the
+ * workspace must not be modified in between.  The records already hold the effect of a
+ * mask, so the scan takes none.
+ *
+ * Arguments have the meaning, layout and alignment given for kda_chunk_prefill; the
+ * workspace is at least kda_chunk_prefill_workspace_size(p, cu_seqlens != NULL) bytes.
+ * Both return KDA_ERR_UNSUPPORTED unless p selects the bf16, dk = dv = 128 kernel
+ * (in_dtype bf16, chunk 0 or 32, T * H * 128 < 2^31).  Ownership: all buffers stay the
+ * caller's; nothing is allocated.  Errors: as for kda_chunk_prefill.
+ */
+kda_status_t kda_chunk_prepare(const kda_params_t *p,
+                               const void *q, const void *k,
+                               const float *g, const float *beta,
+                               const int32_t *cu_seqlens, const uint8_t *mask,
+                               void *workspace, size_t workspace_bytes, void *stream);
+kda_status_t kda_chunk_scan(const kda_params_t *p, const void *v,
+                            const float *initial_state, const int32_t *cu_seqlens,
+                            const void *workspace, size_t workspace_bytes,
+                            void *o, float *final_state, void *stream);
+
+/*
  * kda_recurrent_step -- the decode kernel: the token-by-token form, for one new token
  * per row (T = 1) or a few tokens (T >= 1, applied in order).  The state is read and
  * written in place: state [B, H, dk, dv] fp32 holds S before the call and S after the

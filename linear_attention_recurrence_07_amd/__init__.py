@@ -7,6 +7,7 @@ works but every call raises; there is no CPU fallback.
 
     o, final_state = chunk_prefill(q, k, v, g, beta, initial_state=None)
     o, final_state, y = chunk_prefill(..., gate=gate, norm_weight=w)      # fused gated norm
+    ws = chunk_prepare(q, k, g, beta); o, final_state = chunk_scan(v, ws)   # the same, in two launches
     o = recurrent_step(q, k, v, g, beta, state)                            # state updated in place
     y = gated_rmsnorm(x, gate, w)
 
@@ -23,15 +24,15 @@ from typing import Optional
 
 import torch
 
-__all__ = ["chunk_prefill", "chunk_prefill_workspace_size", "recurrent_step", "gated_rmsnorm", "library_path", "load_library",
-           "KdaError", "version"]
+__all__ = ["chunk_prefill", "chunk_prefill_workspace_size", "chunk_prepare", "chunk_scan", "recurrent_step",
+           "gated_rmsnorm", "library_path", "load_library", "KdaError", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_ALIGN",
-           5: "KDA_ERR_CONFLICT", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_HIP"}
+           5: "KDA_ERR_CONFLICT", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_HIP", 8: "KDA_ERR_WORKSPACE"}
 
 
 class KdaError(RuntimeError):
@@ -71,6 +72,10 @@ def load_library():
     lib.kda_chunk_prefill.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 13 + [P, ctypes.c_size_t, P]
     lib.kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_prefill_workspace_size.argtypes = [ctypes.POINTER(KdaParams), i32]
+    lib.kda_chunk_prepare.restype = ctypes.c_int
+    lib.kda_chunk_prepare.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 7 + [ctypes.c_size_t, P]
+    lib.kda_chunk_scan.restype = ctypes.c_int
+    lib.kda_chunk_scan.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 4 + [ctypes.c_size_t, P, P, P]
     lib.kda_recurrent_step.restype = ctypes.c_int
     lib.kda_recurrent_step.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 12
     lib.kda_gated_rmsnorm.restype = ctypes.c_int
@@ -230,6 +235,85 @@ def chunk_prefill_workspace_size(B: int, T: int, H: int, dk: int, dv: int, *,
     p = _params(B, T, H, dk, dv, num_seqs=num_seqs or 0, chunk=chunk, in_dtype=_dtype_code(dtype),
                 out_dtype=_dtype_code(dtype))
     return int(lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), 1 if num_seqs is not None else 0))
+
+
+def _packing(cu_seqlens, attention_mask, B, T, dev):
+    cu_dev = None
+    N = B
+    if cu_seqlens is not None:
+        if cu_seqlens.device.type == "cpu":
+            _check_cu_seqlens(cu_seqlens, T)
+            cu_dev = cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
+        else:
+            cu_dev = _dev(cu_seqlens, "cu_seqlens", dev)
+            if cu_dev.dtype != torch.int32:
+                raise TypeError("cu_seqlens must be int32")
+        N = cu_dev.numel() - 1
+    mask_dev = None
+    if attention_mask is not None:
+        if attention_mask.shape != (B, T):
+            raise ValueError("attention_mask must be [B, T]")
+        mask_dev = (attention_mask != 0).to(device=dev, dtype=torch.uint8).contiguous()
+    return cu_dev, mask_dev, N
+
+
+def chunk_prepare(q: torch.Tensor, k: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
+                  cu_seqlens: Optional[torch.Tensor] = None,
+                  attention_mask: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                  use_qk_l2norm_in_kernel: bool = True, workspace: Optional[torch.Tensor] = None,
+                  dv: Optional[int] = None) -> torch.Tensor:
+    """First launch of the bf16, d = 128 chunked prefill: the per-chunk records (no state
+    needed).  Returns the workspace that chunk_scan consumes."""
+    lib = load_library()
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = dk if dv is None else dv
+    for name, t in (("q", q), ("k", k), ("g", g), ("beta", beta)):
+        _dev(t, name, dev)
+    if k.shape != q.shape or k.dtype != q.dtype or g.shape != (B, T, H, dk) or beta.shape != (B, T, H):
+        raise ValueError("q, k must be [B,T,H,dk] of one dtype, g [B,T,H,dk], beta [B,T,H]")
+    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("g and beta must be float32")
+    cu_dev, mask_dev, N = _packing(cu_seqlens, attention_mask, B, T, dev)
+    p = _params(B, T, H, dk, dv, num_seqs=N if cu_dev is not None else 0, scale=scale,
+                use_qk_l2norm=use_qk_l2norm_in_kernel, in_dtype=_dtype_code(q.dtype))
+    need = lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), 1 if cu_dev is not None else 0)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", dev)
+    _check(lib.kda_chunk_prepare(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(cu_dev),
+                                 _ptr(mask_dev), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(dev)))
+    return workspace
+
+
+def chunk_scan(v: torch.Tensor, workspace: torch.Tensor, initial_state: Optional[torch.Tensor] = None, *,
+               cu_seqlens: Optional[torch.Tensor] = None, dk: Optional[int] = None,
+               output_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+               final_state: Optional[torch.Tensor] = None):
+    """Second launch of the bf16, d = 128 chunked prefill: the state scan over the records
+    chunk_prepare wrote (same shapes and cu_seqlens).  Returns (o, final_state)."""
+    lib = load_library()
+    dev = v.device
+    B, T, H, dv = v.shape
+    dk = dv if dk is None else dk
+    _dev(v, "v", dev)
+    _dev(workspace, "workspace", dev)
+    cu_dev, _, N = _packing(cu_seqlens, None, B, T, dev)
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", dev)
+        if initial_state.dtype != torch.float32 or initial_state.shape != (N, H, dk, dv):
+            raise ValueError(f"initial_state must be float32 [{N},{H},{dk},{dv}]")
+    out_dt = output_dtype or v.dtype
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
+    _dev(o, "out", dev)
+    fs = final_state if final_state is not None else torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _dev(fs, "final_state", dev)
+    p = _params(B, T, H, dk, dv, num_seqs=N if cu_dev is not None else 0, in_dtype=_dtype_code(v.dtype),
+                out_dtype=_dtype_code(o.dtype))
+    _check(lib.kda_chunk_scan(ctypes.byref(p), _ptr(v), _ptr(initial_state), _ptr(cu_dev), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(o), _ptr(fs), _stream(dev)))
+    return o, fs
 
 
 def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

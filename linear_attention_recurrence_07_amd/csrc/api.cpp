@@ -108,6 +108,32 @@ kda_status_t hip_status(hipError_t e, const char *what) {
   return KDA_OK;
 }
 
+// Packed offsets or a padding mask, and the sequence count that goes with them.
+kda_status_t check_layout(const kda_params_t *p, const int32_t *cu, const uint8_t *mask) {
+  KDA_TRY(check_ptr(cu, "cu_seqlens", false, 4));
+  KDA_TRY(check_ptr(mask, "mask", false, 1));
+  if (cu && mask) return fail(KDA_ERR_CONFLICT, "give cu_seqlens or mask, not both");
+  if (cu && p->B != 1) return fail(KDA_ERR_CONFLICT, "cu_seqlens needs B == 1 (packed batch)");
+  if (cu && p->num_seqs <= 0) return fail(KDA_ERR_SHAPE, "num_seqs must be > 0 with cu_seqlens");
+  return KDA_OK;
+}
+
+// The two stages exist only for the bf16, d = 128 matrix-core kernel.
+kda_status_t check_stage_kernel(const kda_params_t *p) {
+  if (!use_mfma_prefill(p))
+    return fail(KDA_ERR_UNSUPPORTED, "the two-stage prefill needs bf16 inputs, dk = dv = 128, chunk 0 or 32 "
+                                     "and T * H * 128 < 2^31");
+  return KDA_OK;
+}
+
+kda_status_t check_workspace(const kda_params_t *p, const int32_t *cu, const void *ws, size_t bytes) {
+  const size_t need = prefill_workspace(p, cu != nullptr);
+  if (bytes < need || (need > 0 && ws == nullptr))
+    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, bytes,
+                ws == nullptr ? " (NULL)" : "");
+  return check_ptr(ws, "workspace", false);
+}
+
 }  // namespace
 
 extern "C" {
@@ -126,12 +152,8 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
   KDA_TRY(check_ptr(o, "o", true));
   KDA_TRY(check_ptr(final_state, "final_state", true));
   KDA_TRY(check_ptr(initial_state, "initial_state", false));
-  KDA_TRY(check_ptr(cu_seqlens, "cu_seqlens", false, 4));
-  KDA_TRY(check_ptr(mask, "mask", false, 1));
+  KDA_TRY(check_layout(p, cu_seqlens, mask));
   KDA_TRY(check_norm(gate, norm_weight, y, p->dv));
-  if (cu_seqlens && mask) return fail(KDA_ERR_CONFLICT, "give cu_seqlens or mask, not both");
-  if (cu_seqlens && p->B != 1) return fail(KDA_ERR_CONFLICT, "cu_seqlens needs B == 1 (packed batch)");
-  if (cu_seqlens && p->num_seqs <= 0) return fail(KDA_ERR_SHAPE, "num_seqs must be > 0 with cu_seqlens");
   kda::Args a = make_args(p);
   a.N = cu_seqlens ? p->num_seqs : p->B;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
@@ -148,11 +170,7 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
       return fail(KDA_ERR_UNSUPPORTED, "chunk 32 needs bf16 inputs with dk = dv = 128 and T * H * 128 < 2^31");
   }
   if (mfma) {
-    const size_t need = prefill_workspace(p, cu_seqlens != nullptr);
-    if (workspace_bytes < need || (need > 0 && workspace == nullptr))
-      return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, workspace_bytes,
-                  workspace == nullptr ? " (NULL)" : "");
-    KDA_TRY(check_ptr(workspace, "workspace", false));
+    KDA_TRY(check_workspace(p, cu_seqlens, workspace, workspace_bytes));
     KDA_TRY(hip_status(kda::launch_chunk_prep(a, workspace, st), "prefill (chunk preparation)"));
     KDA_TRY(hip_status(kda::launch_chunk_scan(a, workspace, st), "prefill (state scan)"));
     if (norm) {
@@ -172,6 +190,45 @@ size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed) {
   if (p == nullptr || check_params(p, true) != KDA_OK) return 0;
   if (packed && p->num_seqs <= 0) return 0;
   return prefill_workspace(p, packed != 0);
+}
+
+kda_status_t kda_chunk_prepare(const kda_params_t *p, const void *q, const void *k, const float *g,
+                               const float *beta, const int32_t *cu_seqlens, const uint8_t *mask,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  KDA_TRY(check_params(p, true));
+  KDA_TRY(check_ptr(q, "q", true));
+  KDA_TRY(check_ptr(k, "k", true));
+  KDA_TRY(check_ptr(g, "g", true));
+  KDA_TRY(check_ptr(beta, "beta", true, 4));
+  KDA_TRY(check_layout(p, cu_seqlens, mask));
+  KDA_TRY(check_stage_kernel(p));
+  KDA_TRY(check_workspace(p, cu_seqlens, workspace, workspace_bytes));
+  kda::Args a = make_args(p);
+  a.N = cu_seqlens ? p->num_seqs : p->B;
+  a.q = q; a.k = k; a.g = g; a.beta = beta;
+  a.cu = cu_seqlens; a.mask = mask;
+  KDA_TRY(hip_status(kda::launch_chunk_prep(a, workspace, static_cast<hipStream_t>(stream)),
+                     "chunk preparation"));
+  return KDA_OK;
+}
+
+kda_status_t kda_chunk_scan(const kda_params_t *p, const void *v, const float *initial_state,
+                            const int32_t *cu_seqlens, const void *workspace, size_t workspace_bytes,
+                            void *o, float *final_state, void *stream) {
+  KDA_TRY(check_params(p, true));
+  KDA_TRY(check_ptr(v, "v", true));
+  KDA_TRY(check_ptr(o, "o", true));
+  KDA_TRY(check_ptr(final_state, "final_state", true));
+  KDA_TRY(check_ptr(initial_state, "initial_state", false));
+  KDA_TRY(check_layout(p, cu_seqlens, nullptr));
+  KDA_TRY(check_stage_kernel(p));
+  KDA_TRY(check_workspace(p, cu_seqlens, workspace, workspace_bytes));
+  kda::Args a = make_args(p);
+  a.N = cu_seqlens ? p->num_seqs : p->B;
+  a.v = v; a.init = initial_state; a.state = final_state;
+  a.cu = cu_seqlens; a.o = o;
+  KDA_TRY(hip_status(kda::launch_chunk_scan(a, workspace, static_cast<hipStream_t>(stream)), "state scan"));
+  return KDA_OK;
 }
 
 kda_status_t kda_recurrent_step(const kda_params_t *p, const void *q, const void *k, const void *v,

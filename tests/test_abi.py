@@ -116,6 +116,40 @@ def test_prefill_workspace_size_and_checks():
     assert lib.kda_status_string(8) == b"KDA_ERR_WORKSPACE"
 
 
+def test_stage_validation_codes():
+    lib = K.load_library()
+    need = lib.kda_chunk_prefill_workspace_size(ctypes.byref(_p()), 0)
+
+    def prep(p, ws=A, nbytes=need, **ptrs):
+        d = dict(q=A, k=A, g=A, beta=A, cu=None, mask=None)
+        d.update(ptrs)
+        return lib.kda_chunk_prepare(None if p is None else ctypes.byref(p),
+                                     *[d[n] for n in ("q", "k", "g", "beta", "cu", "mask")], ws, nbytes, None)
+
+    def scan(p, ws=A, nbytes=need, **ptrs):
+        d = dict(v=A, init=None, cu=None, o=A, fs=A)
+        d.update(ptrs)
+        return lib.kda_chunk_scan(None if p is None else ctypes.byref(p), d["v"], d["init"], d["cu"],
+                                  ws, nbytes, d["o"], d["fs"], None)
+
+    for f in (prep, scan):
+        assert f(None) == 1
+        assert f(_p(B=0)) == 2
+        assert f(_p(in_dtype=0)) == 6                       # fp32: no two-stage kernel
+        assert f(_p(chunk=16)) == 6
+        assert f(_p(dk=64, dv=64)) == 6
+        assert f(_p(), ws=None, nbytes=0) == 8
+        assert f(_p(), nbytes=need - 1) == 8
+        assert f(_p(), ws=MIS) == 4
+        assert f(_p(B=2, num_seqs=2), cu=A) == 5
+    assert prep(_p(), q=None) == 1
+    assert prep(_p(), g=MIS) == 4
+    assert prep(_p(B=1, num_seqs=1), cu=A, mask=A) == 5
+    assert scan(_p(), v=None) == 1
+    assert scan(_p(), fs=None) == 1
+    assert scan(_p(), init=MIS) == 4
+
+
 def test_recurrent_and_norm_validation_codes():
     lib = K.load_library()
     names = ["q", "k", "v", "g", "beta", "state", "mask", "o", "gate", "w", "y"]

@@ -219,6 +219,34 @@ def test_no_write_no_decay_keeps_state_exactly():
     assert torch.equal(fs, d["initial_state"])
 
 
+def test_two_stage_prefill_equals_one_call():
+    """chunk_prepare then chunk_scan runs the kernels chunk_prefill runs: identical
+    outputs for packed, padded and plain batches, and within tolerance of the oracle."""
+    import linear_attention_recurrence_07_amd as kda
+    x = gi.varlen_packed((100, 0, 37, 64, 129, 1), H=3, d=128)
+    cases = [("packed", x), ("left-padded", gi.padded_from_packed(x, left=True)),
+             ("plain+init", gi.make_inputs("stages", B=2, T=77, H=2, dk=128, dv=128, in_dtype=gi.BF16,
+                                           seed=29, initial_state_std=0.02))]
+    for name, c in cases:
+        U.log(f"two-stage {name}")
+        d = U.device_inputs(c, DEV)
+        o1, f1 = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                                   cu_seqlens=d["cu_seqlens"], attention_mask=d["mask"],
+                                   output_dtype=torch.float32)
+        ws = kda.chunk_prepare(d["q"], d["k"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                               attention_mask=d["mask"])
+        o2, f2 = kda.chunk_scan(d["v"], ws, d["initial_state"], cu_seqlens=d["cu_seqlens"],
+                                output_dtype=torch.float32)
+        torch.cuda.synchronize()
+        m = torch.from_numpy(U.valid_token_mask(c)).to(DEV)
+        assert torch.equal(o1[m], o2[m]), name
+        assert torch.equal(f1, f2), name
+        ro, rfs, _ = U.oracle(c)
+        vm = U.valid_token_mask(c)
+        U.assert_close(f"two-stage {name} o", U.to_numpy64(o2)[vm], ro[vm], U.BF16_TOL)
+        U.assert_close(f"two-stage {name} state", U.to_numpy64(f2), rfs, U.BF16_TOL)
+
+
 def test_deterministic():
     x = gi.make_inputs("det", B=1, T=256, H=4, dk=128, dv=128, in_dtype=gi.BF16, seed=23,
                        initial_state_std=0.02, norm=True)
