@@ -110,7 +110,6 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
   };
   uint32_t vzero;              // 0 in a vector register: keeps the flag load a per-lane load
   __asm__ volatile("v_mov_b32 %0, 0" : "=v"(vzero));
-  Pre pre0, pre1;                                // two sets: loads run two steps ahead
   auto load = [&](Pre &pre, int cidx) {
     const uint8_t *rp = reinterpret_cast<const uint8_t *>(rp0 + static_cast<size_t>(cidx) * H);
 #pragma unroll
@@ -184,7 +183,8 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     const u32x4 *QT = reinterpret_cast<const u32x4 *>(hc.rec.qt);
     const u32x4 *KE = reinterpret_cast<const u32x4 *>(hc.rec.ket);
     const u32x4 *BQ = reinterpret_cast<const u32x4 *>(hc.rec.bq);
-    // phase 1 operands: k^ exp(G) fragments, W, the value tile
+    // Every operand of the chunk is read at the start, in order of first use; each
+    // phase then waits only for its own part.
     uint4 kbf[8];
 #pragma unroll
     for (int f = 0; f < 8; ++f) kbf[f] = __builtin_bit_cast(uint4, KB[f * 64 + lane]);
@@ -197,6 +197,17 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) vv[m][i] = bf16_to_f32(hc.vt[(SB * m + 4 * lg + i) * LDV + wcol]);
+    uint4 kef[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) kef[t] = __builtin_bit_cast(uint4, KE[t * 64 + lane]);
+    float4 ecv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ecv[t] = *reinterpret_cast<const float4 *>(hc.rec.ec + 16 * t + 4 * lg);
+    uint4 qtf[8], bqf[2];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) qtf[f] = __builtin_bit_cast(uint4, QT[f * 64 + lane]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) bqf[m] = __builtin_bit_cast(uint4, BQ[m * 64 + lane]);
     __asm__ volatile("" ::: "memory");
     // Y = V - (k^ exp(G)) S0 in fp16 (W carries the extra precision)
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
@@ -205,14 +216,6 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
       acc0 = mfma_f16(kbf[s], Sh[s], acc0);
       acc1 = mfma_f16(kbf[4 + s], Sh[s], acc1);
     }
-    // phase 2 operands: the transposed decayed keys, the chunk decay
-    uint4 kef[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) kef[t] = __builtin_bit_cast(uint4, KE[t * 64 + lane]);
-    float4 ecv[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) ecv[t] = *reinterpret_cast<const float4 *>(hc.rec.ec + 16 * t + 4 * lg);
-    __asm__ volatile("" ::: "memory");
     uint2 yf[2];
     yf[0] = pack_f16x4(vv[0][0] - acc0[0], vv[0][1] - acc0[1], vv[0][2] - acc0[2], vv[0][3] - acc0[3]);
     yf[1] = pack_f16x4(vv[1][0] - acc1[0], vv[1][1] - acc1[1], vv[1][2] - acc1[2], vv[1][3] - acc1[3]);
@@ -233,13 +236,6 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     split_f16x4(U1, u1h, u1l);
     const uint4 Uh = join(u0h, u1h);   // tokens {4lg+0..3, 16+4lg+0..3} as K=32 B operands
     const uint4 Ul = join(u0l, u1l);
-    // phase 3 operands: q^ exp(G) fragments, Bqk
-    uint4 qtf[8], bqf[2];
-#pragma unroll
-    for (int f = 0; f < 8; ++f) qtf[f] = __builtin_bit_cast(uint4, QT[f * 64 + lane]);
-#pragma unroll
-    for (int m = 0; m < 2; ++m) bqf[m] = __builtin_bit_cast(uint4, BQ[m * 64 + lane]);
-    __asm__ volatile("" ::: "memory");
     // S = diag(exp(G_last)) S0 + (k^ exp(G_last - G))^T U
 #pragma unroll
     for (int t = 0; t < DK / 16; ++t) {
@@ -260,35 +256,39 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     to_f16();                                    // S0 of the next chunk
   };
 
+  // Step s: helpers stage chunk s+1 (loaded at step s-2), load chunk s+3 into the freed
+  // register set and write chunk s-1's rows; compute waves run chunk s.  Chunks past the
+  // end repeat the last.  The two sides run separate loops with one work-group barrier
+  // per step each (nchunks + 1 in all), so their loop-carried registers never overlap.
   if (nchunks > 0) {
     const int last = nchunks - 1;
     if (helper) {
+      Pre pre0, pre1;                            // two sets: loads run two steps ahead
       load(pre0, 0);
       load(pre1, min(1, last));
       stage(sm.hand[0], pre0);
       load(pre0, min(2, last));
-    }
-    sync_lds();
-    // step s: helpers stage chunk s+1 (loaded at step s-2), load chunk s+3 into the freed
-    // set and write chunk s-1's rows; compute waves run chunk s.  Chunks past the end
-    // repeat the last.
-    auto step = [&](int s, Pre &from) {
-      if (helper) {
+      sync_lds();
+      auto hstep = [&](int s, Pre &from) {
         stage(sm.hand[(s + 1) & 1], from);
         load(from, min(s + 3, last));
         if (s >= 1) emit(s - 1, sm.ost[(s + 1) & 1]);
-      } else {
-        products(sm.hand[s & 1], sm.ost[s & 1]);
+        sync_lds();
+      };
+      int s = 0;
+      for (; s + 1 < nchunks; s += 2) {
+        hstep(s, pre1);                          // chunk s+1 is in pre1, s+2 in pre0
+        hstep(s + 1, pre0);
       }
+      if (s < nchunks) hstep(s, pre1);
+      emit(last, sm.ost[last & 1]);
+    } else {
       sync_lds();
-    };
-    int s = 0;
-    for (; s + 1 < nchunks; s += 2) {
-      step(s, pre1);                             // chunk s+1 is in pre1, s+2 in pre0
-      step(s + 1, pre0);
+      for (int s = 0; s < nchunks; ++s) {
+        products(sm.hand[s & 1], sm.ost[s & 1]);
+        sync_lds();
+      }
     }
-    if (s < nchunks) step(s, pre1);
-    if (helper) emit(last, sm.ost[last & 1]);
   }
 
   if (!helper) {
