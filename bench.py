@@ -88,6 +88,8 @@ KERNEL_SOURCES = {
     "gated_rmsnorm_kernel": ["gated_rmsnorm.hip", "kda_device.h"],
 }
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "bench_T8192_B64_hbm_counters.md")
+MFMA_FILE = os.path.join(ROOT, "profiles", "bench_T8192_B64_mfma_counters.md")
+MFMA_PEAK_TFLOPS = 2500.0     # dense bf16 / fp16
 
 
 def source_digest(kernel: str) -> str:
@@ -98,6 +100,59 @@ def source_digest(kernel: str) -> str:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def _profile_lines(path: str, tag: str) -> dict:
+    """Lines `tag kernel digest value...` of a committed profile summary whose kernel
+    sources still match the recorded digest."""
+    out = {}
+    if not os.path.exists(path):
+        return out
+    for line in open(path):
+        f = line.split()
+        if len(f) >= 4 and f[0] == tag and f[1] in KERNEL_SOURCES and source_digest(f[1]) == f[2]:
+            out[f[1]] = [float(x) for x in f[3:]]
+    return out
+
+
+def measured_mfma() -> dict:
+    """Matrix-core work per launch from the committed rocprofv3 summary
+    (SQ_INSTS_VALU_MFMA_MOPS_* x 512 flop, and SQ_VALU_MFMA_BUSY_CYCLES as a share of
+    all SIMD-cycles of the launch), for kernels unchanged since it was taken."""
+    return {k: {"flops_per_launch": v[0], "busy_pct": v[1]} for k, v in _profile_lines(MFMA_FILE, "mfma").items()}
+
+
+def _algorithmic_flops(T: int, H: int, d: int, chunk: int) -> float:
+    """Flops the chunked form needs per launch: the three state contractions (6 d^2 per
+    token), the intra-chunk products (2 C (dk + dv)) and the triangular solve (C^2 / 3)."""
+    return float(T) * H * (6 * d * d + 2 * chunk * 2 * d + chunk * chunk / 3.0)
+
+
+def ceilings() -> dict:
+    """Practical ceilings on this GPU: a plain streaming kernel (torch.neg over 1 GiB of
+    bf16: 1 GiB read + 1 GiB written) and a large bf16 GEMM (torch.mm, 8192^3)."""
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: torch.neg(src, out=dst))
+    del src, dst
+    n = 8192
+    a = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda").to(torch.bfloat16)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    t_mm = timed(lambda: torch.mm(a, b, out=c))
+    del a, b, c
+    return {"copy_GBps": 2 * (1 << 30) / t_copy / 1e9, "gemm_bf16_TFLOPs": 2.0 * n ** 3 / t_mm / 1e12,
+            "how": "torch.neg over 1 GiB bf16 (read + write); torch.mm bf16 8192x8192x8192"}
 
 
 def measured_traffic() -> dict:
@@ -272,12 +327,22 @@ def main():
     b_dec_all = b_dec + _bytes_decode_io(B_DECODE, H, D)
 
     traffic = measured_traffic()
+    mfma = measured_mfma()
+    print("[bench] copy and GEMM ceilings", file=sys.stderr, flush=True)
+    ceil = ceilings()
 
     def roof(kernel, nbytes, t, **extra):
         gbs = nbytes / t / 1e9
-        return {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": gbs / HBM_PEAK_GBPS, "traffic": traffic.get(kernel), "algorithmic_bytes_per_launch": nbytes,
-                "avg_launch_us": t * 1e6, **extra}
+        r = {"bound": "hbm", "kernel": kernel, "achieved": gbs, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": gbs / HBM_PEAK_GBPS, "traffic": traffic.get(kernel), "algorithmic_bytes_per_launch": nbytes,
+             "avg_launch_us": t * 1e6, "frac_of_copy_ceiling": gbs / ceil["copy_GBps"], **extra}
+        if kernel in mfma:
+            tf = mfma[kernel]["flops_per_launch"] / t / 1e12
+            r["mfma"] = {"flops_per_launch": mfma[kernel]["flops_per_launch"], "achieved_tflops": tf,
+                         "peak_tflops": MFMA_PEAK_TFLOPS, "frac": tf / MFMA_PEAK_TFLOPS,
+                         "frac_of_gemm_ceiling": tf / ceil["gemm_bf16_TFLOPs"],
+                         "busy_pct_rocprof": mfma[kernel]["busy_pct"]}
+        return r
 
     r_prep = roof("chunk_prep_kernel", b_prep, t_prep)
     r_scan = roof("chunk_scan_kernel", b_scan, t_scan)
@@ -311,9 +376,12 @@ def main():
         "roofline_scan": r_scan,
         # whole prefill against the bytes it must move (inputs in, o and final state out;
         # the workspace records are the two-launch design's own traffic)
-        "roofline_prefill_path": roof("chunk_prep_kernel + chunk_scan_kernel", b_path, t_prep + t_scan),
+        "roofline_prefill_path": roof("chunk_prep_kernel + chunk_scan_kernel", b_path, t_prep + t_scan,
+                                      algorithmic_tflops=_algorithmic_flops(T_PREFILL, H, D, CHUNK) / (t_prep + t_scan) / 1e12,
+                                      algorithmic_flops_per_launch=_algorithmic_flops(T_PREFILL, H, D, CHUNK)),
         "roofline_decode": roof("recurrent_kernel", b_dec_all, t_dec),
         "roofline_norm": roof("gated_rmsnorm_kernel", b_nrm, t_nrm),
+        "ceilings": ceil,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
