@@ -261,3 +261,73 @@ def long_context(T: int = 65536, seed: int = 0, *, H: int = 96, d: int = 128) ->
     ranges = [(-5.0, -3.0)] * (H // 2) + [(-0.05, 0.0)] * (H - H // 2)
     return make_inputs(f"long_T{T}", B=1, T=T, H=H, dk=d, dv=d, chunk=64, in_dtype=BF16,
                        seed=seed, g_ranges_by_head=ranges, norm=True)
+
+
+# --------------------------------------------------------------------------- short convolution
+@dataclasses.dataclass
+class ConvInputs:
+    """One seeded problem for the causal short convolution in front of the kernel: x holds
+    projected queries, keys or values [B, T, D] (D = heads x head_dim, or the three
+    concatenated), one width-W filter per channel, and the carried inputs of each sequence."""
+
+    name: str
+    B: int
+    T: int
+    D: int
+    width: int
+    in_dtype: str
+    x: np.ndarray                                # [B, T, D] (raw bf16 bits or fp32)
+    weight: np.ndarray                           # [D, W] fp32
+    initial_state: Optional[np.ndarray] = None   # [N, W-1, D] in in_dtype
+    cu_seqlens: Optional[np.ndarray] = None
+    mask: Optional[np.ndarray] = None
+    seed: int = 0
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.cu_seqlens) - 1 if self.cu_seqlens is not None else self.B
+
+    def f64(self, name: str) -> Optional[np.ndarray]:
+        a = getattr(self, name)
+        if a is None:
+            return None
+        if name in ("x", "initial_state"):
+            return to_f64(a, self.in_dtype)
+        return np.asarray(a, dtype=np.float64)
+
+
+def conv_inputs(name: str, *, B: int, T: int, D: int, width: int = 4, in_dtype: str = BF16,
+                seed: int = 0, with_state: bool = False, num_seqs: Optional[int] = None,
+                cu_seqlens: Optional[Sequence[int]] = None, mask: Optional[np.ndarray] = None) -> ConvInputs:
+    """Draw in the fixed order x, weight, initial_state.  x ~ N(0,1) (the projections the
+    configs feed the kernel); weight ~ U(-1/sqrt(W), 1/sqrt(W)), the default initialisation
+    of a depthwise Conv1d of kernel size W (the pages give no trained weights); the
+    carried inputs ~ N(0,1) like x."""
+    rng = np.random.default_rng(seed)
+    x = _draw(rng, (B, T, D), "normal")
+    bound = 1.0 / np.sqrt(width)
+    w = _draw(rng, (D, width), "uniform", low=-bound, high=bound)
+    cu = None if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int32)
+    n = num_seqs if num_seqs is not None else (len(cu) - 1 if cu is not None else B)
+    init = _draw(rng, (n, width - 1, D), "normal") if with_state else None
+    return ConvInputs(name=name, B=B, T=T, D=D, width=width, in_dtype=in_dtype, x=_cast(x, in_dtype),
+                      weight=w, initial_state=None if init is None else _cast(init, in_dtype),
+                      cu_seqlens=cu, mask=None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8),
+                      seed=seed)
+
+
+def conv_padded_from_packed(x: ConvInputs, *, left: bool = False) -> ConvInputs:
+    """The packed sequences of x as [N, max_len, D] rows with a 0/1 mask."""
+    cu = x.cu_seqlens
+    lengths = np.diff(cu)
+    N, L = len(lengths), int(lengths.max())
+    out = np.zeros((N, L, x.D), dtype=x.x.dtype)
+    mask = np.zeros((N, L), np.uint8)
+    for n in range(N):
+        ln = int(lengths[n])
+        lo = L - ln if left else 0
+        out[n, lo:lo + ln] = x.x[0, cu[n]:cu[n + 1]]
+        mask[n, lo:lo + ln] = 1
+    return dataclasses.replace(x, name=x.name + ("_left" if left else "_right"), B=N, T=L, x=out,
+                               cu_seqlens=None, mask=mask)
+
