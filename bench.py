@@ -36,6 +36,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "KDA prefill tokens/s (H=96,d=128,T=8192) + decode-step state GB/s at B=64"
 
 T_PREFILL, H, D = 8192, 96, 128
+D_HEAD = D
 B_DECODE, P_DECODE = 64, 1000
 
 
@@ -69,6 +70,43 @@ def _bytes_scan(T: int, H: int, d: int, with_init: bool) -> int:
 
 def _bytes_norm(rows: int, d: int) -> int:
     return rows * d * 2 * 3 + d * 4            # o and gate read, y written (bf16)
+
+
+def _bytes_conv(B: int, T: int, D: int, width: int, with_init: bool) -> int:
+    """Algorithmic bytes of one short-convolution launch (bf16 in and out): x read, y
+    written, the carried inputs of each row written (and read when given), the fp32 taps."""
+    state = B * (width - 1) * D * 2
+    return B * T * D * 2 * 2 + state * (2 if with_init else 1) + D * width * 4
+
+
+def time_short_conv(kda, reps: int = 10) -> dict:
+    """The short convolution in front of the kernel, timed on its own (it is not part of
+    the step): the T=8192 prompt's q, k and v projections side by side (D = 3 x 96 x 128),
+    and one decode token for 64 rows with the carried inputs updated in place."""
+    D = 3 * H * D_HEAD
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    w = (torch.rand((D, 4), generator=gen, device="cuda") - 0.5)
+    out = {}
+    for name, B, T in (("prefill", 1, T_PREFILL), ("decode", B_DECODE, 1)):
+        x = torch.randn((B, T, D), generator=gen, device="cuda").to(torch.bfloat16)
+        y = torch.empty_like(x)
+        st = torch.randn((B, 3, D), generator=gen, device="cuda").to(torch.bfloat16)
+        for _ in range(2):
+            kda.short_conv(x, w, st, final_state=st, out=y)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            kda.short_conv(x, w, st, final_state=st, out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        nbytes = _bytes_conv(B, T, D, 4, True)
+        out[name] = {"B": B, "T": T, "D": D, "avg_call_us": t * 1e6, "algorithmic_bytes": nbytes,
+                     "achieved": nbytes / t / 1e9, "unit": "GB/s", "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS}
+        del x, y, st
+    return out
 
 
 def _bytes_decode_state(B: int, H: int, d: int) -> int:
@@ -330,6 +368,8 @@ def main():
     mfma = measured_mfma()
     print("[bench] copy and GEMM ceilings", file=sys.stderr, flush=True)
     ceil = ceilings()
+    print("[bench] short convolution", file=sys.stderr, flush=True)
+    conv = time_short_conv(kda)
 
     def roof(kernel, nbytes, t, **extra):
         gbs = nbytes / t / 1e9
@@ -382,6 +422,9 @@ def main():
         "roofline_decode": roof("recurrent_kernel", b_dec_all, t_dec),
         "roofline_norm": roof("gated_rmsnorm_kernel", b_nrm, t_nrm),
         "ceilings": ceil,
+        # the causal short convolution in front of the kernel, timed on its own (two
+        # launches per call: the filter over all tokens, then the carried-input update)
+        "short_conv": conv,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)

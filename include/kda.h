@@ -185,6 +185,52 @@ kda_status_t kda_gated_rmsnorm(const void *x, const void *gate, const float *wei
                                int64_t rows, int32_t width, float eps,
                                int32_t in_dtype, int32_t out_dtype, void *stream);
 
+/* Problem description of the short convolution. */
+typedef struct {
+  int32_t B;             /* batch rows; 1 when cu_seqlens packs the sequences              */
+  int32_t T;             /* tokens per row (packed total with cu_seqlens)                  */
+  int32_t D;             /* channels per token (a multiple of 8), e.g. heads * head_dim    */
+  int32_t num_seqs;      /* sequences: len(cu_seqlens)-1 with cu_seqlens, else ignored (=B) */
+  int32_t width;         /* filter width W, 2..4 (4 in the pages' configuration)           */
+  int32_t activation;    /* 1: SiLU after the filter (the pages' setting), 0: none         */
+  int32_t in_dtype;      /* kda_dtype_t of x and of the carried state                      */
+  int32_t out_dtype;     /* kda_dtype_t of y                                               */
+} kda_conv_params_t;
+
+/*
+ * kda_short_conv -- the causal short convolution that runs over the projected queries,
+ * keys and values in front of the KDA kernel (Kimi-K3 atlas, KDA layer page, kda-init
+ * code: a ShortConvolution with activation 'silu' on each projection; nnterp Kimi-Linear
+ * page, module tree: a Conv1d with one width-4 filter per channel, padding 3, no bias).
+ * Per channel c and token t of a sequence:
+ *     z = sum_{j<W} weight[c][j] * x[t-(W-1)+j][c],    y[t][c] = z * sigmoid(z)  (or z)
+ * Inputs before a sequence's first token come from its carried state, oldest first.
+ *
+ *   x              [B, T, D]         in_dtype
+ *   weight         [D, W]            fp32, 4-byte aligned; weight[c][W-1] meets the newest input
+ *   initial_state  [N, W-1, D]       in_dtype, the W-1 inputs before each sequence (oldest
+ *                                    first), or NULL for zeros (start of a prompt)
+ *   cu_seqlens     [N + 1]           int32 device offsets of packed sequences (B == 1,
+ *                                    p->num_seqs = N), or NULL; not together with mask
+ *   mask           [B, T]            uint8, 0 = padding: output 0 and the token never enters
+ *                                    the window (it is skipped), or NULL
+ *   y              [B, T, D]         out_dtype; must not overlap x
+ *   final_state    [N, W-1, D]       in_dtype: the last W-1 inputs of each sequence (with
+ *                                    the carried state in front when a sequence is shorter),
+ *                                    or NULL to skip.  It may be the same buffer as
+ *                                    initial_state (decode: state updated in place).
+ * N = B without cu_seqlens.  Tokens of a packed batch outside [0, cu_seqlens[N]) are not
+ * written.  A decode step is a call with T = 1 and the state passed as both
+ * initial_state and final_state.  x, y and the states must be 16-byte aligned.
+ * Errors: KDA_ERR_NULL (params, x, weight or y NULL), KDA_ERR_SHAPE (sizes, activation),
+ * KDA_ERR_DTYPE, KDA_ERR_ALIGN, KDA_ERR_CONFLICT (cu_seqlens with mask, cu_seqlens with
+ * B != 1, y overlapping x), KDA_ERR_UNSUPPORTED (D not a multiple of 8, W outside 2..4,
+ * more than 65535 rows, sequences or 64-token tiles), KDA_ERR_HIP.  Nothing is allocated.
+ */
+kda_status_t kda_short_conv(const kda_conv_params_t *p, const void *x, const float *weight,
+                            const void *initial_state, const int32_t *cu_seqlens,
+                            const uint8_t *mask, void *y, void *final_state, void *stream);
+
 /* Text of a status code (static storage). */
 const char *kda_status_string(kda_status_t s);
 /* Detail of the last non-OK status returned on this thread (thread-local storage). */

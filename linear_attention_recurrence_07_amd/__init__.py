@@ -10,6 +10,7 @@ works but every call raises; there is no CPU fallback.
     ws = chunk_prepare(q, k, g, beta); o, final_state = chunk_scan(v, ws)   # the same, in two launches
     o = recurrent_step(q, k, v, g, beta, state)                            # state updated in place
     y = gated_rmsnorm(x, gate, w)
+    y, conv_state = short_conv(x, weight, conv_state)                      # causal width-4 conv + SiLU
 
 The call mirrors the kernels on the nnterp Kimi-Linear page (section 04): queries,
 keys, values [B, T, H, d], g= per-key-channel log decays [B, T, H, dk] (fp32, <= 0),
@@ -25,7 +26,7 @@ from typing import Optional
 import torch
 
 __all__ = ["chunk_prefill", "chunk_prefill_workspace_size", "chunk_prepare", "chunk_scan", "recurrent_step",
-           "gated_rmsnorm", "library_path", "load_library", "KdaError", "version"]
+           "gated_rmsnorm", "short_conv", "library_path", "load_library", "KdaError", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
@@ -41,6 +42,12 @@ class KdaError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{_STATUS.get(status, status)}: {detail}")
         self.status = status
+
+
+class KdaConvParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("width", ctypes.c_int32), ("activation", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
 
 
 class KdaParams(ctypes.Structure):
@@ -76,6 +83,8 @@ def load_library():
     lib.kda_chunk_prepare.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 7 + [ctypes.c_size_t, P]
     lib.kda_chunk_scan.restype = ctypes.c_int
     lib.kda_chunk_scan.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 4 + [ctypes.c_size_t, P, P, P]
+    lib.kda_short_conv.restype = ctypes.c_int
+    lib.kda_short_conv.argtypes = [ctypes.POINTER(KdaConvParams)] + [P] * 8
     lib.kda_recurrent_step.restype = ctypes.c_int
     lib.kda_recurrent_step.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 12
     lib.kda_gated_rmsnorm.restype = ctypes.c_int
@@ -390,3 +399,45 @@ def gated_rmsnorm(x: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor, eps
     _check(lib.kda_gated_rmsnorm(_ptr(x), _ptr(gate), _ptr(weight), _ptr(y), rows, width, float(eps),
                                  _dtype_code(x.dtype), _dtype_code(y.dtype), _stream(dev)))
     return y
+
+
+def short_conv(x: torch.Tensor, weight: torch.Tensor, initial_state: Optional[torch.Tensor] = None, *,
+               cu_seqlens: Optional[torch.Tensor] = None, attention_mask: Optional[torch.Tensor] = None,
+               activation: Optional[str] = "silu", output_dtype: Optional[torch.dtype] = None,
+               out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+               with_final_state: bool = True):
+    """Causal short convolution over the token axis of x [B, T, D] (one width-W filter per
+    channel, weight [D, W] float32), then SiLU.  initial_state / final_state [N, W-1, D] hold
+    the W-1 inputs before / at the end of each sequence, oldest first, in x's dtype; pass
+    the same tensor as both for an in-place decode step.  Returns (y, final_state) (or y
+    alone with with_final_state=False)."""
+    lib = load_library()
+    dev = x.device
+    _dev(x, "x", dev)
+    _dev(weight, "weight", dev)
+    B, T, D = x.shape
+    if weight.dtype != torch.float32 or weight.dim() != 2 or weight.shape[0] != D:
+        raise ValueError("weight must be float32 [D, W]")
+    W = weight.shape[1]
+    if activation not in ("silu", None):
+        raise ValueError("activation must be 'silu' or None")
+    cu_dev, mask_dev, N = _packing(cu_seqlens, attention_mask, B, T, dev)
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", dev)
+        if initial_state.dtype != x.dtype or initial_state.shape != (N, W - 1, D):
+            raise ValueError(f"initial_state must be {x.dtype} [{N},{W - 1},{D}]")
+    y = out if out is not None else torch.empty((B, T, D), dtype=output_dtype or x.dtype, device=dev)
+    _dev(y, "out", dev)
+    fs = final_state
+    if fs is None and with_final_state:
+        fs = torch.empty((N, W - 1, D), dtype=x.dtype, device=dev)
+    if fs is not None:
+        _dev(fs, "final_state", dev)
+        if fs.dtype != x.dtype or fs.shape != (N, W - 1, D):
+            raise ValueError(f"final_state must be {x.dtype} [{N},{W - 1},{D}]")
+    p = KdaConvParams(B, T, D, N if cu_dev is not None else 0, W, 1 if activation == "silu" else 0,
+                      _dtype_code(x.dtype), _dtype_code(y.dtype))
+    _check(lib.kda_short_conv(ctypes.byref(p), _ptr(x), _ptr(weight), _ptr(initial_state), _ptr(cu_dev),
+                              _ptr(mask_dev), _ptr(y), _ptr(fs), _stream(dev)))
+    return (y, fs) if with_final_state else y
+

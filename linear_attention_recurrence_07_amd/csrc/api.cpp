@@ -277,6 +277,46 @@ kda_status_t kda_gated_rmsnorm(const void *x, const void *gate, const float *wei
   return KDA_OK;
 }
 
+kda_status_t kda_short_conv(const kda_conv_params_t *p, const void *x, const float *weight,
+                            const void *initial_state, const int32_t *cu_seqlens, const uint8_t *mask,
+                            void *y, void *final_state, void *stream) {
+  if (p == nullptr) return fail(KDA_ERR_NULL, "params is NULL");
+  if (p->B <= 0 || p->T < 0 || p->D <= 0)
+    return fail(KDA_ERR_SHAPE, "bad sizes B=%d T=%d D=%d", p->B, p->T, p->D);
+  if (!valid_dtype(p->in_dtype) || !valid_dtype(p->out_dtype))
+    return fail(KDA_ERR_DTYPE, "unknown dtype code in=%d out=%d", p->in_dtype, p->out_dtype);
+  if (p->activation != 0 && p->activation != 1) return fail(KDA_ERR_SHAPE, "activation must be 0 or 1");
+  KDA_TRY(check_ptr(x, "x", true));
+  KDA_TRY(check_ptr(weight, "weight", true, 4));
+  KDA_TRY(check_ptr(y, "y", true));
+  KDA_TRY(check_ptr(initial_state, "initial_state", false));
+  KDA_TRY(check_ptr(final_state, "final_state", false));
+  KDA_TRY(check_ptr(cu_seqlens, "cu_seqlens", false, 4));
+  KDA_TRY(check_ptr(mask, "mask", false, 1));
+  if (cu_seqlens && mask) return fail(KDA_ERR_CONFLICT, "give cu_seqlens or mask, not both");
+  if (cu_seqlens && p->B != 1) return fail(KDA_ERR_CONFLICT, "cu_seqlens needs B == 1 (packed batch)");
+  if (cu_seqlens && p->num_seqs <= 0) return fail(KDA_ERR_SHAPE, "num_seqs must be > 0 with cu_seqlens");
+  if (p->D % 8 != 0) return fail(KDA_ERR_UNSUPPORTED, "D=%d must be a multiple of 8", p->D);
+  if (p->width < 2 || p->width > 4) return fail(KDA_ERR_UNSUPPORTED, "width %d not in 2..4", p->width);
+  const int N = cu_seqlens ? p->num_seqs : p->B;
+  if (p->B > 65535 || N > 65535 || (p->T + 63) / 64 > 65535)
+    return fail(KDA_ERR_UNSUPPORTED, "more than 65535 rows, sequences or 64-token tiles");
+  const double elems = static_cast<double>(p->B) * p->T * p->D;
+  if (elems * 4 > 9.0e18) return fail(KDA_ERR_SHAPE, "problem too large");
+  const uintptr_t xs = reinterpret_cast<uintptr_t>(x), ys = reinterpret_cast<uintptr_t>(y);
+  const uintptr_t xb = static_cast<uintptr_t>(elems) * (p->in_dtype == KDA_BF16 ? 2u : 4u);
+  const uintptr_t yb = static_cast<uintptr_t>(elems) * (p->out_dtype == KDA_BF16 ? 2u : 4u);
+  if (elems > 0 && xs < ys + yb && ys < xs + xb) return fail(KDA_ERR_CONFLICT, "y overlaps x");
+  kda::ConvArgs a{};
+  a.x = x; a.w = weight; a.init = initial_state; a.cu = cu_seqlens; a.mask = mask;
+  a.y = y; a.fin = final_state;
+  a.B = p->B; a.T = p->T; a.D = p->D; a.N = N; a.W = p->width; a.silu = p->activation;
+  a.in_bf16 = p->in_dtype == KDA_BF16;
+  a.out_bf16 = p->out_dtype == KDA_BF16;
+  KDA_TRY(hip_status(kda::launch_short_conv(a, static_cast<hipStream_t>(stream)), "short convolution"));
+  return KDA_OK;
+}
+
 const char *kda_status_string(kda_status_t s) {
   switch (s) {
     case KDA_OK: return "KDA_OK";

@@ -26,7 +26,21 @@ struct Args {
   int in_bf16, out_bf16;
 };
 
+// Arguments of one short-convolution call after host validation.
+struct ConvArgs {
+  const void *x;
+  const float *w;             // [D, W]
+  const void *init;           // [N, W-1, D] or null
+  const int32_t *cu;
+  const uint8_t *mask;
+  void *y;
+  void *fin;                  // [N, W-1, D] or null
+  int B, T, D, N, W, silu;
+  int in_bf16, out_bf16;
+};
+
 hipError_t launch_recurrent(const Args &a, hipStream_t s);
+hipError_t launch_short_conv(const ConvArgs &a, hipStream_t s);
 hipError_t launch_prefill_valu(const Args &a, hipStream_t s);
 // bf16 chunked prefill, d = 128: the per-chunk preparation (writes one record per
 // (slot, head) into ws), then the state scan that reads them.

@@ -22,7 +22,7 @@ def _declared_functions():
 
 def test_header_declares_the_three_entry_points():
     names = _declared_functions()
-    for n in ("kda_chunk_prefill", "kda_chunk_prefill_workspace_size", "kda_recurrent_step",
+    for n in ("kda_chunk_prefill", "kda_chunk_prefill_workspace_size", "kda_recurrent_step", "kda_short_conv",
               "kda_gated_rmsnorm", "kda_status_string", "kda_last_error", "kda_version"):
         assert n in names
 
@@ -171,6 +171,53 @@ def test_recurrent_and_norm_validation_codes():
     assert norm(A, A, A, A, 10, 128, 1e-6, 5, 1, None) == 3
     assert norm(A, A, A, A, 10, 128, -1.0, 1, 1, None) == 2
     assert norm(A, A, A, A, 0, 128, 1e-6, 1, 1, None) == 0   # zero rows: no launch
+
+
+def test_conv_params_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "conv_layout.c"
+    src.write_text(f'''#include <stdio.h>
+#include <stddef.h>
+#include "{HEADER}"
+int main(void) {{
+  printf("%zu", sizeof(kda_conv_params_t));
+#define F(x) printf(" %zu", offsetof(kda_conv_params_t, x));
+  F(B) F(T) F(D) F(num_seqs) F(width) F(activation) F(in_dtype) F(out_dtype)
+  return 0;
+}}''')
+    exe = tmp_path / "conv_layout"
+    subprocess.run(["gcc", "-o", str(exe), str(src)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(K.KdaConvParams)] + [getattr(K.KdaConvParams, f).offset for f, _ in K.KdaConvParams._fields_]
+    assert got == want
+
+
+def test_conv_validation_codes():
+    lib = K.load_library()
+
+    def conv(B=1, T=64, D=64, N=0, W=4, act=1, ind=1, outd=1, **ptrs):
+        p = K.KdaConvParams(B, T, D, N, W, act, ind, outd)
+        d = dict(x=A, w=A, init=None, cu=None, mask=None, y=ctypes.c_void_p(1 << 30), fs=None)
+        d.update(ptrs)
+        return lib.kda_short_conv(ctypes.byref(p), *[d[n] for n in ("x", "w", "init", "cu", "mask", "y", "fs")], None)
+
+    assert lib.kda_short_conv(None, A, A, None, None, None, A, None, None) == 1
+    assert conv(x=None) == 1
+    assert conv(w=None) == 1
+    assert conv(y=None) == 1
+    assert conv(B=0) == 2
+    assert conv(T=-1) == 2
+    assert conv(act=2) == 2
+    assert conv(ind=5) == 3
+    assert conv(x=MIS) == 4
+    assert conv(init=MIS) == 4
+    assert conv(cu=A, mask=A, N=1) == 5
+    assert conv(B=2, cu=A, N=2) == 5
+    assert conv(y=A) == 5                                    # y overlapping x
+    assert conv(D=60) == 6
+    assert conv(W=5) == 6
+    assert conv(W=1) == 6
+    assert conv(B=70000) == 6
+    assert conv(cu=A, N=0) == 2
 
 
 def test_status_strings_and_version():
