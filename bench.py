@@ -109,6 +109,29 @@ def time_short_conv(kda, reps: int = 10) -> dict:
     return out
 
 
+def time_per_head_decay(kda, P, ws, o, fs, reps: int = 10) -> dict:
+    """The T=8192 prefill with one decay per (token, head) (g [1, T, H]: the gated
+    DeltaNet's scalar decay), both launches timed with events; not part of the step."""
+    g1 = P["g"][..., 0].contiguous()
+    for _ in range(2):
+        kda.chunk_prepare(P["q"], P["k"], g1, P["beta"], workspace=ws)
+        kda.chunk_scan(P["v"], ws, out=o, final_state=fs)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        kda.chunk_prepare(P["q"], P["k"], g1, P["beta"], workspace=ws)
+        e[1].record()
+        kda.chunk_scan(P["v"], ws, out=o, final_state=fs)
+        e[2].record()
+    torch.cuda.synchronize()
+    tp = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    ts = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    b_prep = (T_PREFILL // CHUNK) * H * (CHUNK * (2 * D * 2 + 4 + 4) + REC_BYTES)
+    return {"prepare_us": tp * 1e6, "scan_us": ts * 1e6, "tokens_per_s": T_PREFILL / (tp + ts),
+            "prepare_algorithmic_bytes": b_prep, "prepare_GBps": b_prep / tp / 1e9}
+
+
 def _bytes_decode_state(B: int, H: int, d: int) -> int:
     return 2 * B * H * d * d * 4               # state read + written (fp32)
 
@@ -370,6 +393,8 @@ def main():
     ceil = ceilings()
     print("[bench] short convolution", file=sys.stderr, flush=True)
     conv = time_short_conv(kda)
+    print("[bench] prefill with one decay per head", file=sys.stderr, flush=True)
+    per_head = time_per_head_decay(kda, P, ws, o, fs)
 
     def roof(kernel, nbytes, t, **extra):
         gbs = nbytes / t / 1e9
@@ -425,6 +450,8 @@ def main():
         # the causal short convolution in front of the kernel, timed on its own (two
         # launches per call: the filter over all tokens, then the carried-input update)
         "short_conv": conv,
+        # the same prefill with g [1, T, H] (one decay per head), timed on its own
+        "prefill_per_head_decay": per_head,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)

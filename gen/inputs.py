@@ -79,7 +79,7 @@ class KdaInputs:
     q: np.ndarray                       # [B,T,H,dk]
     k: np.ndarray                       # [B,T,H,dk]
     v: np.ndarray                       # [B,T,H,dv]
-    g: np.ndarray                       # [B,T,H,dk] fp32, <= 0
+    g: np.ndarray                       # [B,T,H,dk] fp32, <= 0 ([B,T,H]: one decay per head)
     beta: np.ndarray                    # [B,T,H] fp32 in (0,1)
     initial_state: Optional[np.ndarray] = None   # [N,H,dk,dv] fp32
     gate: Optional[np.ndarray] = None            # [B,T,H,dv]
@@ -137,6 +137,7 @@ def make_inputs(
     cu_seqlens: Optional[Sequence[int]] = None,
     mask: Optional[np.ndarray] = None,
     normalize_qk: bool = True,
+    decay_per_head: bool = False,
 ) -> KdaInputs:
     """Draw one problem in the fixed order q, k, v, g, beta-logits, initial_state, gate, w.
 
@@ -151,7 +152,9 @@ def make_inputs(
         q = _unit_rows_f32(q)
         k = _unit_rows_f32(k)
     v = _draw(rng, (B, T, H, dv), "normal")
-    if g_ranges_by_head is None:
+    if decay_per_head:        # one decay per (token, head): the gated DeltaNet's scalar decay
+        g = _draw(rng, (B, T, H), "uniform", low=g_range[0], high=g_range[1])
+    elif g_ranges_by_head is None:
         g = _draw(rng, (B, T, H, dk), "uniform", low=g_range[0], high=g_range[1])
     else:
         u = rng.random(size=(B, T, H, dk), dtype=np.float32)

@@ -76,6 +76,10 @@ typedef struct {
   int32_t in_dtype;      /* kda_dtype_t of q, k, v and gate                                */
   int32_t out_dtype;     /* kda_dtype_t of o and y                                         */
   float norm_eps;        /* gated-RMSNorm epsilon                                          */
+  int32_t decay_per_head; /* 0: g is [B, T, H, dk], one log decay per key channel (KDA);
+                            1: g is [B, T, H], one per head, shared by its key channels
+                            (the gated DeltaNet's scalar decay; nnterp Kimi-Linear page,
+                            Notes: KDA is the gated DeltaNet with the decay made per channel) */
 } kda_params_t;
 
 /*
@@ -87,7 +91,7 @@ typedef struct {
  *
  *   q, k          [B, T, H, dk]   in_dtype
  *   v             [B, T, H, dv]   in_dtype
- *   g             [B, T, H, dk]   fp32 log decays (<= 0)
+ *   g             [B, T, H, dk]   fp32 log decays (<= 0); [B, T, H] with p->decay_per_head
  *   beta          [B, T, H]       fp32 write strengths in (0, 1), already sigmoided
  *   initial_state [N, H, dk, dv]  fp32, or NULL for a zero state (start of a prompt)
  *   cu_seqlens    [N + 1]         int32 device array of packed sequence offsets

@@ -55,7 +55,8 @@ class KdaParams(ctypes.Structure):
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("use_qk_l2norm", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("norm_eps", ctypes.c_float)]
+                ("out_dtype", ctypes.c_int32), ("norm_eps", ctypes.c_float),
+                ("decay_per_head", ctypes.c_int32)]
 
 
 _lib = None
@@ -133,9 +134,22 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def _params(B, T, H, dk, dv, *, num_seqs=0, chunk=0, scale=None, use_qk_l2norm=True,
-            in_dtype=KDA_BF16, out_dtype=KDA_BF16, norm_eps=1e-6) -> KdaParams:
+            in_dtype=KDA_BF16, out_dtype=KDA_BF16, norm_eps=1e-6, decay_per_head=False) -> KdaParams:
     return KdaParams(B, T, H, dk, dv, num_seqs, chunk, 0.0 if scale is None else float(scale),
-                     1 if use_qk_l2norm else 0, in_dtype, out_dtype, float(norm_eps))
+                     1 if use_qk_l2norm else 0, in_dtype, out_dtype, float(norm_eps),
+                     1 if decay_per_head else 0)
+
+
+def _decay_layout(g: torch.Tensor, B: int, T: int, H: int, dk: int) -> bool:
+    """True for one decay per head ([B, T, H]: the gated DeltaNet's scalar decay), False
+    for one per key channel ([B, T, H, dk]: KDA)."""
+    if g.dtype != torch.float32:
+        raise TypeError("g must be float32")
+    if g.shape == (B, T, H):
+        return True
+    if g.shape == (B, T, H, dk):
+        return False
+    raise ValueError("g must be [B,T,H,dk] (per key channel) or [B,T,H] (per head)")
 
 
 def _check_cu_seqlens(cu: torch.Tensor, T: int) -> None:
@@ -176,10 +190,9 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         raise ValueError("q, k must be [B,T,H,dk] and v [B,T,H,dv]")
     _dev(g, "g", dev)
     _dev(beta, "beta", dev)
-    if g.dtype != torch.float32 or beta.dtype != torch.float32:
-        raise TypeError("g and beta must be float32")
-    if g.shape != (B, T, H, dk) or beta.shape != (B, T, H):
-        raise ValueError("g must be [B,T,H,dk] and beta [B,T,H]")
+    per_head = _decay_layout(g, B, T, H, dk)
+    if beta.dtype != torch.float32 or beta.shape != (B, T, H):
+        raise ValueError("beta must be float32 [B,T,H]")
     cu_dev = None
     if cu_seqlens is not None:
         if cu_seqlens.device.type == "cpu":
@@ -221,7 +234,7 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         y = None
     p = _params(B, T, H, dk, dv, num_seqs=N if cu_dev is not None else 0, chunk=chunk, scale=scale,
                 use_qk_l2norm=use_qk_l2norm_in_kernel, in_dtype=_dtype_code(in_dt),
-                out_dtype=_dtype_code(out_dt), norm_eps=norm_eps)
+                out_dtype=_dtype_code(out_dt), norm_eps=norm_eps, decay_per_head=per_head)
     need = lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), 1 if cu_dev is not None else 0)
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
@@ -279,13 +292,14 @@ def chunk_prepare(q: torch.Tensor, k: torch.Tensor, g: torch.Tensor, beta: torch
     dv = dk if dv is None else dv
     for name, t in (("q", q), ("k", k), ("g", g), ("beta", beta)):
         _dev(t, name, dev)
-    if k.shape != q.shape or k.dtype != q.dtype or g.shape != (B, T, H, dk) or beta.shape != (B, T, H):
-        raise ValueError("q, k must be [B,T,H,dk] of one dtype, g [B,T,H,dk], beta [B,T,H]")
-    if g.dtype != torch.float32 or beta.dtype != torch.float32:
-        raise TypeError("g and beta must be float32")
+    if k.shape != q.shape or k.dtype != q.dtype or beta.shape != (B, T, H):
+        raise ValueError("q, k must be [B,T,H,dk] of one dtype, beta [B,T,H]")
+    per_head = _decay_layout(g, B, T, H, dk)
+    if beta.dtype != torch.float32:
+        raise TypeError("beta must be float32")
     cu_dev, mask_dev, N = _packing(cu_seqlens, attention_mask, B, T, dev)
     p = _params(B, T, H, dk, dv, num_seqs=N if cu_dev is not None else 0, scale=scale,
-                use_qk_l2norm=use_qk_l2norm_in_kernel, in_dtype=_dtype_code(q.dtype))
+                use_qk_l2norm=use_qk_l2norm_in_kernel, in_dtype=_dtype_code(q.dtype), decay_per_head=per_head)
     need = lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), 1 if cu_dev is not None else 0)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
@@ -348,8 +362,9 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
         raise ValueError("q, k must be [B,T,H,dk] and v [B,T,H,dv]")
     _dev(g, "g", dev)
     _dev(beta, "beta", dev)
-    if g.dtype != torch.float32 or beta.dtype != torch.float32 or g.shape != (B, T, H, dk) or beta.shape != (B, T, H):
-        raise ValueError("g must be float32 [B,T,H,dk] and beta float32 [B,T,H]")
+    per_head = _decay_layout(g, B, T, H, dk)
+    if beta.dtype != torch.float32 or beta.shape != (B, T, H):
+        raise ValueError("beta must be float32 [B,T,H]")
     _dev(state, "state", dev)
     if state.dtype != torch.float32 or state.shape != (B, H, dk, dv):
         raise ValueError("state must be float32 [B,H,dk,dv]")
@@ -373,7 +388,8 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     else:
         y = None
     p = _params(B, T, H, dk, dv, scale=scale, use_qk_l2norm=use_qk_l2norm_in_kernel,
-                in_dtype=_dtype_code(in_dt), out_dtype=_dtype_code(out_dt), norm_eps=norm_eps)
+                in_dtype=_dtype_code(in_dt), out_dtype=_dtype_code(out_dt), norm_eps=norm_eps,
+                decay_per_head=per_head)
     _check(lib.kda_recurrent_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(state), _ptr(mask_dev), _ptr(o), _ptr(gate), _ptr(norm_weight),
                                   _ptr(y), _stream(dev)))

@@ -53,6 +53,7 @@ kda_status_t check_params(const kda_params_t *p, bool prefill) {
   if (!(p->scale >= 0.f) || !std::isfinite(p->scale)) return fail(KDA_ERR_SHAPE, "scale must be finite and >= 0");
   if (!(p->norm_eps >= 0.f) || !std::isfinite(p->norm_eps)) return fail(KDA_ERR_SHAPE, "norm_eps must be finite and >= 0");
   if (p->use_qk_l2norm != 0 && p->use_qk_l2norm != 1) return fail(KDA_ERR_SHAPE, "use_qk_l2norm must be 0 or 1");
+  if (p->decay_per_head != 0 && p->decay_per_head != 1) return fail(KDA_ERR_SHAPE, "decay_per_head must be 0 or 1");
   if (prefill && p->chunk != 0 && p->chunk != 16 && p->chunk != 32)
     return fail(KDA_ERR_UNSUPPORTED, "chunk %d not supported (0, 16 or 32)", p->chunk);
   // Element counts must stay addressable with 32-bit token indices times heads.
@@ -87,6 +88,7 @@ kda::Args make_args(const kda_params_t *p) {
   a.use_l2 = p->use_qk_l2norm;
   a.in_bf16 = p->in_dtype == KDA_BF16;
   a.out_bf16 = p->out_dtype == KDA_BF16;
+  a.g_head = p->decay_per_head;
   return a;
 }
 
@@ -147,7 +149,7 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
   KDA_TRY(check_ptr(q, "q", true));
   KDA_TRY(check_ptr(k, "k", true));
   KDA_TRY(check_ptr(v, "v", true));
-  KDA_TRY(check_ptr(g, "g", true));
+  KDA_TRY(check_ptr(g, "g", true, p->decay_per_head ? 4u : 16u));
   KDA_TRY(check_ptr(beta, "beta", true, 4));
   KDA_TRY(check_ptr(o, "o", true));
   KDA_TRY(check_ptr(final_state, "final_state", true));
@@ -198,7 +200,7 @@ kda_status_t kda_chunk_prepare(const kda_params_t *p, const void *q, const void 
   KDA_TRY(check_params(p, true));
   KDA_TRY(check_ptr(q, "q", true));
   KDA_TRY(check_ptr(k, "k", true));
-  KDA_TRY(check_ptr(g, "g", true));
+  KDA_TRY(check_ptr(g, "g", true, p->decay_per_head ? 4u : 16u));
   KDA_TRY(check_ptr(beta, "beta", true, 4));
   KDA_TRY(check_layout(p, cu_seqlens, mask));
   KDA_TRY(check_stage_kernel(p));
@@ -239,7 +241,7 @@ kda_status_t kda_recurrent_step(const kda_params_t *p, const void *q, const void
   KDA_TRY(check_ptr(q, "q", true));
   KDA_TRY(check_ptr(k, "k", true));
   KDA_TRY(check_ptr(v, "v", true));
-  KDA_TRY(check_ptr(g, "g", true));
+  KDA_TRY(check_ptr(g, "g", true, p->decay_per_head ? 4u : 16u));
   KDA_TRY(check_ptr(beta, "beta", true, 4));
   KDA_TRY(check_ptr(state, "state", true));
   KDA_TRY(check_ptr(o, "o", true));

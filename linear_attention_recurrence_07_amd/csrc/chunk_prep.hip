@@ -87,7 +87,8 @@ __device__ __forceinline__ f32x4 mma_f16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-template <bool HAS_MASK>
+// G_HEAD: g holds one decay per (token, head), shared by every key channel.
+template <bool HAS_MASK, bool G_HEAD>
 __global__ void __launch_bounds__(NT)
 chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const float *__restrict__ g, const float *__restrict__ beta,
@@ -134,7 +135,7 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
   const int off = tcl * (H * DK) + h * DK + 4 * lg;
   const uint16_t *kp = k + row0 * H * DK + off;
   const uint16_t *qp = q + row0 * H * DK + off;
-  const float *gp = g + row0 * H * DK + off;
+  const float *gp = G_HEAD ? g + (row0 + tcl) * H + h : g + row0 * H * DK + off;
   u32x2 kr[4][2], qr[4][2];
   f32x4 G[4][2];
 #pragma unroll
@@ -143,7 +144,12 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     for (int hh = 0; hh < 2; ++hh) {
       kr[s][hh] = *reinterpret_cast<const u32x2 *>(kp + 32 * s + 16 * hh);
       qr[s][hh] = *reinterpret_cast<const u32x2 *>(qp + 32 * s + 16 * hh);
-      G[s][hh] = *reinterpret_cast<const f32x4 *>(gp + 32 * s + 16 * hh);
+      if constexpr (G_HEAD) {
+        const float gs = *gp;
+        G[s][hh] = f32x4{gs, gs, gs, gs};
+      } else {
+        G[s][hh] = *reinterpret_cast<const f32x4 *>(gp + 32 * s + 16 * hh);
+      }
     }
   const float bt = beta[(row0 + tcl) * H + h];
 
@@ -400,12 +406,21 @@ hipError_t launch_chunk_prep(const Args &a, void *ws, hipStream_t st) {
   const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k);
   Rec *rec = static_cast<Rec *>(ws);
   const dim3 grid(static_cast<unsigned>(blocks));
-  if (a.mask)
-    hipLaunchKernelGGL((chunk_prep_kernel<true>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                       rec, a.T, a.H, a.N, a.scale, a.use_l2);
-  else
-    hipLaunchKernelGGL((chunk_prep_kernel<false>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                       rec, a.T, a.H, a.N, a.scale, a.use_l2);
+  if (a.g_head) {
+    if (a.mask)
+      hipLaunchKernelGGL((chunk_prep_kernel<true, true>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
+                         rec, a.T, a.H, a.N, a.scale, a.use_l2);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<false, true>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
+                         rec, a.T, a.H, a.N, a.scale, a.use_l2);
+  } else {
+    if (a.mask)
+      hipLaunchKernelGGL((chunk_prep_kernel<true, false>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
+                         rec, a.T, a.H, a.N, a.scale, a.use_l2);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<false, false>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
+                         rec, a.T, a.H, a.N, a.scale, a.use_l2);
+  }
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ struct Args {
   float scale, eps;
   int use_l2;
   int in_bf16, out_bf16;
+  int g_head;                 // g is [B, T, H] (one decay per head), not [B, T, H, dk]
 };
 
 // Arguments of one short-convolution call after host validation.

@@ -28,7 +28,7 @@ prefill_valu_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
                     const float *init, float *fin, const int32_t *__restrict__ cu,
                     const uint8_t *__restrict__ mask, TOut *__restrict__ o,
                     const TIn *__restrict__ gate, const float *__restrict__ norm_w,
-                    TOut *__restrict__ y, int T, int H, float scale, int use_l2, float eps) {
+                    TOut *__restrict__ y, int T, int H, float scale, int use_l2, float eps, int g_head) {
   constexpr int C = kC;
   __shared__ float sS[D][D];
   __shared__ float sK[C][D], sQ[C][D], sG[C][D], sV[C][D], sU[C][D];
@@ -63,7 +63,7 @@ prefill_valu_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
       const size_t idx = ((static_cast<size_t>(b) * T + t) * H + h) * D + col;
       sK[r][col] = valid ? Elem<TIn>::load(k, idx) : 0.f;
       sQ[r][col] = valid ? Elem<TIn>::load(q, idx) : 0.f;
-      sG[r][col] = valid ? g[idx] : 0.f;
+      sG[r][col] = valid ? (g_head ? g[idx / D] : g[idx]) : 0.f;
       sV[r][col] = valid ? Elem<TIn>::load(v, idx) : 0.f;
     }
     if (tid < C) {
@@ -191,11 +191,11 @@ hipError_t launch_typed(const Args &a, hipStream_t st) {
   if (a.y)
     hipLaunchKernelGGL((prefill_valu_kernel<D, TIn, TOut, true>), grid, block, 0, st, q, k, v, a.g,
                        a.beta, a.init, a.state, a.cu, a.mask, o, gate, a.norm_w, y, a.T, a.H,
-                       a.scale, a.use_l2, a.eps);
+                       a.scale, a.use_l2, a.eps, a.g_head);
   else
     hipLaunchKernelGGL((prefill_valu_kernel<D, TIn, TOut, false>), grid, block, 0, st, q, k, v, a.g,
                        a.beta, a.init, a.state, a.cu, a.mask, o, gate, a.norm_w, y, a.T, a.H,
-                       a.scale, a.use_l2, a.eps);
+                       a.scale, a.use_l2, a.eps, a.g_head);
   return hipGetLastError();
 }
 

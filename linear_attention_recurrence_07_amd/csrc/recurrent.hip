@@ -28,7 +28,7 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
                  float *__restrict__ state, const uint8_t *__restrict__ mask,
                  TOut *__restrict__ o, const TIn *__restrict__ gate,
                  const float *__restrict__ norm_w, TOut *__restrict__ y,
-                 int T, int H, float scale, int use_l2, float eps) {
+                 int T, int H, float scale, int use_l2, float eps, int g_head) {
   constexpr int CG = D / 4;          // column groups (float4 each)
   constexpr int RG = D / RPT;        // row groups
   constexpr int NT = RG * CG;
@@ -65,7 +65,7 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
         if (e < D) {
           kk[j] = Elem<TIn>::load(k, tok * D + e);
           qq[j] = Elem<TIn>::load(q, tok * D + e);
-          ee[j] = fast_exp2(g[tok * D + e] * kLog2e);
+          ee[j] = fast_exp2((g_head ? g[tok] : g[tok * D + e]) * kLog2e);
           sk += kk[j] * kk[j];
           sq += qq[j] * qq[j];
         }
@@ -172,11 +172,11 @@ hipError_t launch_typed(const Args &a, hipStream_t st) {
   if (a.y)
     hipLaunchKernelGGL((recurrent_kernel<D, RPT, TIn, TOut, true>), grid, block, 0, st, q, k, v,
                        a.g, a.beta, a.state, a.mask, o, gate, a.norm_w, y, a.T, a.H, a.scale,
-                       a.use_l2, a.eps);
+                       a.use_l2, a.eps, a.g_head);
   else
     hipLaunchKernelGGL((recurrent_kernel<D, RPT, TIn, TOut, false>), grid, block, 0, st, q, k, v,
                        a.g, a.beta, a.state, a.mask, o, gate, a.norm_w, y, a.T, a.H, a.scale,
-                       a.use_l2, a.eps);
+                       a.use_l2, a.eps, a.g_head);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ def recurrence(q, k, v, g, beta, initial_state=None, *, in_dtype: str = "f32",
                mask=None, cu_seqlens=None, heads: Optional[Sequence[int]] = None,
                num_threads: int = 0):
     """C oracle.  q, k, v are fp32 arrays, or uint16 raw bf16 bits with in_dtype='bf16';
-    g, beta, initial_state fp32.  heads selects a subset of heads (outputs are laid out
+    g ([B,T,H,dk], or [B,T,H] for one decay per head), beta, initial_state fp32.  heads selects a subset of heads (outputs are laid out
     over that subset).  Returns o [B,T,len(heads),dv] and final_state [N,len(heads),dk,dv],
     both fp64."""
     lib = _load()
@@ -67,9 +67,12 @@ def recurrence(q, k, v, g, beta, initial_state=None, *, in_dtype: str = "f32",
     q = np.ascontiguousarray(q, dtype=want)
     k = np.ascontiguousarray(k, dtype=want)
     v = np.ascontiguousarray(v, dtype=want)
-    g = np.ascontiguousarray(g, dtype=np.float32)
     beta = np.ascontiguousarray(beta, dtype=np.float32)
     B, T, H, dk = q.shape
+    g = np.asarray(g, dtype=np.float32)
+    if g.ndim == 3:                    # one decay per head: the same factor on every key channel
+        g = np.repeat(g[..., None], dk, axis=-1)
+    g = np.ascontiguousarray(g)
     dv = v.shape[-1]
     init = None if initial_state is None else np.ascontiguousarray(initial_state, dtype=np.float32)
     cu = None if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, dtype=np.int32)

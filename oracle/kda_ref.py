@@ -46,6 +46,16 @@ def l2_normalize(x: np.ndarray, eps: float = L2_EPS) -> np.ndarray:
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
 
 
+def per_channel_decay(g, dk: int) -> np.ndarray:
+    """g as one log decay per key channel, [B,T,H,dk].  A per-head decay [B,T,H] (the
+    gated DeltaNet's: nnterp Kimi-Linear page, Notes, where KDA is that model with the
+    decay made per channel) applies the same factor to every key channel of the head."""
+    g = np.asarray(g, dtype=np.float64)
+    if g.ndim == 3:
+        g = np.repeat(g[..., None], dk, axis=-1)
+    return g
+
+
 def _segments(B: int, T: int, cu_seqlens) -> list:
     """(batch row, first token, end token) for every independent sequence."""
     if cu_seqlens is None:
@@ -61,8 +71,9 @@ def kda_recurrence(q, k, v, g, beta, initial_state=None, *, scale: Optional[floa
                    cu_seqlens=None, return_states: bool = False):
     """Token-by-token KDA recurrence in fp64.
 
-    q, k: [B,T,H,dk]; v: [B,T,H,dv]; g: [B,T,H,dk] (natural-log decays, <= 0);
-    beta: [B,T,H]; initial_state: [N,H,dk,dv] or None (zeros); mask: [B,T] (0 = padding)
+    q, k: [B,T,H,dk]; v: [B,T,H,dv]; g: [B,T,H,dk] (natural-log decays, <= 0), or
+    [B,T,H] for one decay per head; beta: [B,T,H]; initial_state: [N,H,dk,dv] or None
+    (zeros); mask: [B,T] (0 = padding)
     or None; cu_seqlens: [N+1] with B == 1, or None.
     Returns o [B,T,H,dv] and final_state [N,H,dk,dv]; with return_states also the
     state after every token, [B,T,H,dk,dv] (padding positions keep the carried state).
@@ -70,6 +81,7 @@ def kda_recurrence(q, k, v, g, beta, initial_state=None, *, scale: Optional[floa
     q, k, v, g, beta = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    g = per_channel_decay(g, dk)
     if scale is None:
         scale = 1.0 / np.sqrt(dk)
     if cu_seqlens is not None and mask is not None:
@@ -143,6 +155,7 @@ def kda_chunked(q, k, v, g, beta, initial_state=None, *, chunk: int = 64,
     """
     q, k, v, g, beta = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta))
     B, T, H, dk = q.shape
+    g = per_channel_decay(g, dk)
     dv = v.shape[-1]
     if scale is None:
         scale = 1.0 / np.sqrt(dk)

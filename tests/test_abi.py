@@ -47,6 +47,7 @@ int main(void) {{
   printf("%zu", sizeof(kda_params_t));
 #define F(x) printf(" %zu", offsetof(kda_params_t, x));
   F(B) F(T) F(H) F(dk) F(dv) F(num_seqs) F(chunk) F(scale) F(use_qk_l2norm) F(in_dtype) F(out_dtype) F(norm_eps)
+  F(decay_per_head)
   return 0;
 }}''')
     exe = tmp_path / "layout"
@@ -95,6 +96,11 @@ def test_prefill_validation_codes():
     assert _prefill(_p(dk=16, dv=16, chunk=32)) == 6         # 32-token chunks only on the MFMA path
     assert _prefill(_p(in_dtype=0, chunk=32)) == 6
     assert _prefill(_p(scale=float("nan"))) == 2
+    bad = _p()
+    bad.decay_per_head = 2
+    assert _prefill(bad) == 2
+    assert _prefill(_p(), g=ctypes.c_void_p((1 << 20) + 4)) == 4            # per-channel g: 16-byte aligned
+    assert _prefill(_p(decay_per_head=1), g=ctypes.c_void_p((1 << 20) + 4), o=None) == 1   # per-head g: 4 bytes
 
 
 def test_prefill_workspace_size_and_checks():

@@ -247,6 +247,50 @@ def test_two_stage_prefill_equals_one_call():
         U.assert_close(f"two-stage {name} state", U.to_numpy64(f2), rfs, U.BF16_TOL)
 
 
+@pytest.mark.parametrize("case", ["mfma_init_norm", "mfma_packed", "mfma_masked", "valu_f32", "valu_bf16_chunk16"])
+def test_per_head_decay(case):
+    """One decay per (token, head) (g [B,T,H], the gated DeltaNet's scalar decay) through
+    every prefill kernel and the decode kernel."""
+    if case == "mfma_init_norm":
+        x = gi.make_inputs("ph_init", B=2, T=201, H=3, dk=128, dv=128, in_dtype=gi.BF16, seed=41,
+                           initial_state_std=0.02, norm=True, decay_per_head=True)
+        _check_prefill(x, tol=U.BF16_TOL, tag=" per-head g")
+    elif case == "mfma_packed":
+        x = gi.make_inputs("ph_packed", B=1, T=240, H=2, dk=128, dv=128, in_dtype=gi.BF16, seed=42,
+                           initial_state_std=0.02, num_seqs=4, cu_seqlens=[0, 31, 31, 150, 240],
+                           decay_per_head=True)
+        _check_prefill(x, tol=U.BF16_TOL, tag=" per-head g")
+    elif case == "mfma_masked":
+        m = np.ones((2, 100), np.uint8)
+        m[0, :17] = 0
+        m[1, 60:] = 0
+        x = gi.make_inputs("ph_mask", B=2, T=100, H=2, dk=128, dv=128, in_dtype=gi.BF16, seed=43,
+                           mask=m, decay_per_head=True)
+        _check_prefill(x, tol=U.BF16_TOL, tag=" per-head g")
+    elif case == "valu_f32":
+        x = gi.make_inputs("ph_tiny", B=1, T=64, H=2, dk=16, dv=16, chunk=16, in_dtype=gi.F32, seed=44,
+                           norm=True, decay_per_head=True)
+        _check_prefill(x, tol=U.F32_TOL, tag=" per-head g")
+    else:
+        x = gi.make_inputs("ph_valu", B=1, T=77, H=2, dk=128, dv=128, in_dtype=gi.BF16, seed=45,
+                           initial_state_std=0.02, decay_per_head=True)
+        _check_prefill(x, tol=U.BF16_TOL, chunk=16, tag=" per-head g")
+
+
+def test_per_head_decay_decode_steps():
+    import linear_attention_recurrence_07_amd as kda
+    x = gi.make_inputs("ph_dec", B=3, T=5, H=4, dk=128, dv=128, in_dtype=gi.BF16, seed=46,
+                       initial_state_std=0.05, norm=True, decay_per_head=True)
+    d = U.device_inputs(x, DEV)
+    ro, rfs, ry = U.oracle(x)
+    st = d["initial_state"].clone()
+    U.log("per-head g: 5 recurrent steps")
+    o = kda.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st, output_dtype=torch.float32)
+    torch.cuda.synchronize()
+    U.assert_close("per-head g decode o", U.to_numpy64(o), ro, U.BF16_TOL)
+    U.assert_close("per-head g decode state", U.to_numpy64(st), rfs, U.BF16_TOL)
+
+
 def test_deterministic():
     x = gi.make_inputs("det", B=1, T=256, H=4, dk=128, dv=128, in_dtype=gi.BF16, seed=23,
                        initial_state_std=0.02, norm=True)

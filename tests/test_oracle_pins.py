@@ -328,3 +328,45 @@ def test_p12_c_oracle_matches_numpy_bf16_cut_with_state_mask_and_heads():
     p = gi.padded_from_packed(xv, left=True)
     op, sp = cref.recurrence(p.q, p.k, p.v, p.g, p.beta, p.initial_state, in_dtype="bf16", mask=p.mask)
     assert R.rel_err(sp, s) < 1e-12
+
+
+# ----------------------------------------------------------------- one decay per head
+def test_per_head_decay_closed_form_without_writes():
+    """beta = 0 with one decay per (token, head): every entry of head h's state scales by
+    exp(sum_t g_t[h]); heads decay independently (a head mix-up or an axis slip fails)."""
+    rng = np.random.default_rng(31)
+    B, T, H, dk, dv = 1, 9, 3, 4, 5
+    q, k, v, _, _ = _problem(rng, B, T, H, dk, dv)
+    g = rng.uniform(-2.0, 0.0, size=(B, T, H))
+    S0 = rng.standard_normal((B, H, dk, dv))
+    o, S = R.kda_recurrence(q, k, v, g, np.zeros((B, T, H)), S0)
+    for h in range(H):
+        np.testing.assert_allclose(S[0, h], np.exp(g[0, :, h].sum()) * S0[0, h], rtol=1e-13)
+    qn = R.l2_normalize(q) / np.sqrt(dk)
+    t = 4
+    np.testing.assert_allclose(o[0, t, 1], np.exp(g[0, :t + 1, 1].sum()) * (S0[0, 1].T @ qn[0, t, 1]), rtol=1e-12)
+
+
+def test_per_head_decay_is_the_per_channel_decay_repeated():
+    """The gated DeltaNet's scalar decay is KDA's per-channel decay with all key channels
+    of a head equal; also through the chunked form and the C oracle."""
+    rng = np.random.default_rng(32)
+    B, T, H, dk, dv = 2, 21, 2, 8, 6
+    q, k, v, _, beta = _problem(rng, B, T, H, dk, dv)
+    g = rng.uniform(-5.0, 0.0, size=(B, T, H))
+    S0 = 0.1 * rng.standard_normal((B, H, dk, dv))
+    gfull = np.repeat(g[..., None], dk, axis=-1)
+    o1, s1 = R.kda_recurrence(q, k, v, g, beta, S0)
+    o2, s2 = R.kda_recurrence(q, k, v, gfull, beta, S0)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+    o3, s3 = R.kda_chunked(q, k, v, g, beta, S0, chunk=8)
+    np.testing.assert_allclose(o3, o1, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(s3, s1, rtol=1e-10, atol=1e-12)
+    o4, s4 = cref.recurrence(q.astype(np.float32), k.astype(np.float32), v.astype(np.float32),
+                             g.astype(np.float32), beta.astype(np.float32), S0.astype(np.float32))
+    o5, s5 = R.kda_recurrence(q.astype(np.float32), k.astype(np.float32), v.astype(np.float32),
+                              g.astype(np.float32), beta.astype(np.float32), S0.astype(np.float32))
+    np.testing.assert_allclose(o4, o5, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(s4, s5, rtol=1e-9, atol=1e-11)
+
