@@ -132,6 +132,39 @@ def time_per_head_decay(kda, P, ws, o, fs, reps: int = 10) -> dict:
             "prepare_algorithmic_bytes": b_prep, "prepare_GBps": b_prep / tp / 1e9}
 
 
+def time_recurrent_states(kda, T: int = 256, reps: int = 5) -> dict:
+    """The token-by-token kernel over a T-token prompt at the 96-head, 128-dim shape,
+    storing the state after every token (64 KB per token and head); not part of the step."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    shp = (1, T, H, D)
+    q = _unit_rows(_dev_randn(shp, gen, torch.bfloat16))
+    k = _unit_rows(_dev_randn(shp, gen, torch.bfloat16))
+    v = _dev_randn(shp, gen, torch.bfloat16)
+    g = torch.rand(shp, generator=gen, device="cuda") * -5.0
+    beta = torch.sigmoid(torch.randn((1, T, H), generator=gen, device="cuda"))
+    st0 = torch.zeros((1, H, D, D), device="cuda")
+    states = torch.empty((1, T, H, D, D), device="cuda")
+    o = torch.empty_like(v)
+    st = st0.clone()
+    kda.recurrent_step(q, k, v, g, beta, st, out=o, states=states)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        st.copy_(st0)
+        e0.record()
+        kda.recurrent_step(q, k, v, g, beta, st, out=o, states=states)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    t = float(np.mean(ts))
+    nbytes = T * H * D * D * 4 + 2 * H * D * D * 4 + T * H * (4 * D * 2 + D * 4 + 4)
+    del states
+    return {"T": T, "H": H, "avg_call_us": t * 1e6, "algorithmic_bytes": nbytes, "achieved": nbytes / t / 1e9,
+            "unit": "GB/s", "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS}
+
+
 def _bytes_decode_state(B: int, H: int, d: int) -> int:
     return 2 * B * H * d * d * 4               # state read + written (fp32)
 
@@ -395,6 +428,8 @@ def main():
     conv = time_short_conv(kda)
     print("[bench] prefill with one decay per head", file=sys.stderr, flush=True)
     per_head = time_per_head_decay(kda, P, ws, o, fs)
+    print("[bench] per-token states", file=sys.stderr, flush=True)
+    rec_states = time_recurrent_states(kda)
 
     def roof(kernel, nbytes, t, **extra):
         gbs = nbytes / t / 1e9
@@ -452,6 +487,8 @@ def main():
         "short_conv": conv,
         # the same prefill with g [1, T, H] (one decay per head), timed on its own
         "prefill_per_head_decay": per_head,
+        # the token-by-token kernel storing the state after every token, timed on its own
+        "recurrent_states": rec_states,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)

@@ -180,6 +180,24 @@ kda_status_t kda_recurrent_step(const kda_params_t *p,
                                 void *stream);
 
 /*
+ * kda_recurrent_states -- kda_recurrent_step that also stores the state after every
+ * token: the per-token states a prompt yields when it runs through the token-by-token
+ * kernel rather than the chunked one (nnterp Kimi-Linear page, support() table, the
+ * 'states' row [batch, seq, heads, key_dim, value_dim]; Notes, "Loading").
+ *   states [B, T, H, dk, dv] fp32, 16-byte aligned: states[b, t, h] is S after token t
+ *          (for a padding token, the carried state).  64 KB per token and head at d = 128.
+ * Other arguments, ownership and errors as for kda_recurrent_step (KDA_ERR_NULL when
+ * states is NULL).
+ */
+kda_status_t kda_recurrent_states(const kda_params_t *p,
+                                  const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta,
+                                  float *state, const uint8_t *mask,
+                                  void *o,
+                                  const void *gate, const float *norm_weight, void *y,
+                                  float *states, void *stream);
+
+/*
  * kda_gated_rmsnorm -- y = w * x / sqrt(mean(x^2) + eps) * sigmoid(gate) over each row
  * of `width` features (one head).  x and gate: [rows, width] in in_dtype; weight:
  * [width] fp32 shared by every row; y: [rows, width] out_dtype.  width must be a power

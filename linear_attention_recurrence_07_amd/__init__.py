@@ -88,6 +88,8 @@ def load_library():
     lib.kda_short_conv.argtypes = [ctypes.POINTER(KdaConvParams)] + [P] * 8
     lib.kda_recurrent_step.restype = ctypes.c_int
     lib.kda_recurrent_step.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 12
+    lib.kda_recurrent_states.restype = ctypes.c_int
+    lib.kda_recurrent_states.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 13
     lib.kda_gated_rmsnorm.restype = ctypes.c_int
     lib.kda_gated_rmsnorm.argtypes = [P, P, P, P, i64, i32, f32, i32, i32, P]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -345,9 +347,11 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
                    gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
                    norm_eps: float = 1e-6, scale: Optional[float] = None,
                    use_qk_l2norm_in_kernel: bool = True, output_dtype: Optional[torch.dtype] = None,
-                   out: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None):
+                   out: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                   states: Optional[torch.Tensor] = None):
     """Token-by-token step(s): advances `state` ([B,H,dk,dv] fp32) in place over the T
-    tokens of q/k/v and returns o (and y with the gated norm)."""
+    tokens of q/k/v and returns o (and y with the gated norm).  With `states` (a float32
+    [B,T,H,dk,dv] tensor) the state after every token is stored there as well."""
     lib = load_library()
     dev = q.device
     B, T, H, dk = q.shape
@@ -390,9 +394,17 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     p = _params(B, T, H, dk, dv, scale=scale, use_qk_l2norm=use_qk_l2norm_in_kernel,
                 in_dtype=_dtype_code(in_dt), out_dtype=_dtype_code(out_dt), norm_eps=norm_eps,
                 decay_per_head=per_head)
-    _check(lib.kda_recurrent_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                  _ptr(state), _ptr(mask_dev), _ptr(o), _ptr(gate), _ptr(norm_weight),
-                                  _ptr(y), _stream(dev)))
+    if states is None:
+        _check(lib.kda_recurrent_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(state), _ptr(mask_dev), _ptr(o), _ptr(gate), _ptr(norm_weight),
+                                      _ptr(y), _stream(dev)))
+    else:
+        _dev(states, "states", dev)
+        if states.dtype != torch.float32 or states.shape != (B, T, H, dk, dv):
+            raise ValueError(f"states must be float32 [{B},{T},{H},{dk},{dv}]")
+        _check(lib.kda_recurrent_states(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                        _ptr(state), _ptr(mask_dev), _ptr(o), _ptr(gate), _ptr(norm_weight),
+                                        _ptr(y), _ptr(states), _stream(dev)))
     return o if y is None else (o, y)
 
 

@@ -233,10 +233,11 @@ kda_status_t kda_chunk_scan(const kda_params_t *p, const void *v, const float *i
   return KDA_OK;
 }
 
-kda_status_t kda_recurrent_step(const kda_params_t *p, const void *q, const void *k, const void *v,
-                                const float *g, const float *beta, float *state,
-                                const uint8_t *mask, void *o, const void *gate,
-                                const float *norm_weight, void *y, void *stream) {
+// Shared body of the two token-by-token entry points.
+static kda_status_t recurrent_impl(const kda_params_t *p, const void *q, const void *k, const void *v,
+                            const float *g, const float *beta, float *state, const uint8_t *mask,
+                            void *o, const void *gate, const float *norm_weight, void *y,
+                            float *states, void *stream) {
   KDA_TRY(check_params(p, false));
   KDA_TRY(check_ptr(q, "q", true));
   KDA_TRY(check_ptr(k, "k", true));
@@ -254,8 +255,24 @@ kda_status_t kda_recurrent_step(const kda_params_t *p, const void *q, const void
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.state = state; a.mask = mask; a.o = o;
   a.gate = gate; a.norm_w = norm_weight; a.y = y;
+  a.states_out = states;
   KDA_TRY(hip_status(kda::launch_recurrent(a, static_cast<hipStream_t>(stream)), "recurrent step"));
   return KDA_OK;
+}
+
+kda_status_t kda_recurrent_step(const kda_params_t *p, const void *q, const void *k, const void *v,
+                                const float *g, const float *beta, float *state,
+                                const uint8_t *mask, void *o, const void *gate,
+                                const float *norm_weight, void *y, void *stream) {
+  return recurrent_impl(p, q, k, v, g, beta, state, mask, o, gate, norm_weight, y, nullptr, stream);
+}
+
+kda_status_t kda_recurrent_states(const kda_params_t *p, const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta, float *state,
+                                  const uint8_t *mask, void *o, const void *gate,
+                                  const float *norm_weight, void *y, float *states, void *stream) {
+  KDA_TRY(check_ptr(states, "states", true));
+  return recurrent_impl(p, q, k, v, g, beta, state, mask, o, gate, norm_weight, y, states, stream);
 }
 
 kda_status_t kda_gated_rmsnorm(const void *x, const void *gate, const float *weight, void *y,

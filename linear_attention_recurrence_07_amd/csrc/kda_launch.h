@@ -25,6 +25,7 @@ struct Args {
   int use_l2;
   int in_bf16, out_bf16;
   int g_head;                 // g is [B, T, H] (one decay per head), not [B, T, H, dk]
+  float *states_out;          // recurrent: the state after every token [B, T, H, dk, dv], or null
 };
 
 // Arguments of one short-convolution call after host validation.

@@ -15,6 +15,11 @@
 // column reductions (S'^T k, S'^T q) run over lanes with cross-lane adds, then over
 // waves through LDS.  This kernel is HBM-bound: at B=64, H=96, d=128 it moves 805 MB
 // of state per step and does 0.86 flop per byte.
+//
+// With `states` set it also stores the state after every token ([B, T, H, dk, dv]; a
+// padding token stores the carried state): the per-token states that the pages read by
+// running a prompt through the token-by-token kernel (nnterp Kimi-Linear page, support()
+// table, the 'states' row, and Notes, "Loading").
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -28,7 +33,7 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
                  float *__restrict__ state, const uint8_t *__restrict__ mask,
                  TOut *__restrict__ o, const TIn *__restrict__ gate,
                  const float *__restrict__ norm_w, TOut *__restrict__ y,
-                 int T, int H, float scale, int use_l2, float eps, int g_head) {
+                 int T, int H, float scale, int use_l2, float eps, int g_head, float *__restrict__ states) {
   constexpr int CG = D / 4;          // column groups (float4 each)
   constexpr int RG = D / RPT;        // row groups
   constexpr int NT = RG * CG;
@@ -138,6 +143,12 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
         s[m].x += kv * u.x; s[m].y += kv * u.y; s[m].z += kv * u.z; s[m].w += kv * u.w;
       }
     }
+    if (states) {
+      float *St = states + tok * D * D;
+#pragma unroll
+      for (int m = 0; m < RPT; ++m)
+        *reinterpret_cast<float4 *>(St + static_cast<size_t>(rg + RG * m) * D + 4 * cg) = s[m];
+    }
     if (rg == 0) {   // the first CG threads (wave 0) hold one full output row
       Elem<TOut>::store4(o, tok * D + 4 * cg, out);
       if constexpr (NORM) {
@@ -172,11 +183,11 @@ hipError_t launch_typed(const Args &a, hipStream_t st) {
   if (a.y)
     hipLaunchKernelGGL((recurrent_kernel<D, RPT, TIn, TOut, true>), grid, block, 0, st, q, k, v,
                        a.g, a.beta, a.state, a.mask, o, gate, a.norm_w, y, a.T, a.H, a.scale,
-                       a.use_l2, a.eps, a.g_head);
+                       a.use_l2, a.eps, a.g_head, a.states_out);
   else
     hipLaunchKernelGGL((recurrent_kernel<D, RPT, TIn, TOut, false>), grid, block, 0, st, q, k, v,
                        a.g, a.beta, a.state, a.mask, o, gate, a.norm_w, y, a.T, a.H, a.scale,
-                       a.use_l2, a.eps, a.g_head);
+                       a.use_l2, a.eps, a.g_head, a.states_out);
   return hipGetLastError();
 }
 

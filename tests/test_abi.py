@@ -170,6 +170,17 @@ def test_recurrent_and_norm_validation_codes():
     assert rec(_p(), y=A) == 5
     assert rec(_p(), g=MIS) == 4
     assert rec(_p(T=0)) == 0                                  # nothing to do, nothing launched
+    st_names = names[:-1] + ["y", "states"]
+
+    def rec_states(p, **ptrs):
+        d = dict(q=A, k=A, v=A, g=A, beta=A, state=A, mask=None, o=A, gate=None, w=None, y=None, states=A)
+        d.update(ptrs)
+        return lib.kda_recurrent_states(ctypes.byref(p), *[d[n] for n in names], d["states"], None)
+
+    assert rec_states(_p(), states=None) == 1
+    assert rec_states(_p(), states=MIS) == 4
+    assert rec_states(_p(), state=None) == 1
+    assert rec_states(_p(dk=128, dv=64)) == 6
     norm = lib.kda_gated_rmsnorm
     assert norm(A, A, A, A, 10, 100, 1e-6, 1, 1, None) == 6
     assert norm(A, A, A, A, -1, 128, 1e-6, 1, 1, None) == 2

@@ -291,6 +291,43 @@ def test_per_head_decay_decode_steps():
     U.assert_close("per-head g decode state", U.to_numpy64(st), rfs, U.BF16_TOL)
 
 
+@pytest.mark.parametrize("case", ["bf16_mask", "f32_tiny", "bf16_per_head"])
+def test_per_token_states(case):
+    """kda_recurrent_states: the state after every token against the oracle's per-token
+    states (padding tokens repeat the carried state), plus o and the final state."""
+    import linear_attention_recurrence_07_amd as kda
+    if case == "bf16_mask":
+        m = np.ones((2, 37), np.uint8)
+        m[0, 5] = 0
+        m[1, 30:] = 0
+        x = gi.make_inputs("states", B=2, T=37, H=3, dk=128, dv=128, in_dtype=gi.BF16, seed=51,
+                           initial_state_std=0.05, mask=m)
+        tol = U.BF16_TOL
+    elif case == "f32_tiny":
+        x = gi.make_inputs("states_tiny", B=1, T=64, H=2, dk=16, dv=16, chunk=16, in_dtype=gi.F32, seed=52)
+        tol = U.F32_TOL
+    else:
+        x = gi.make_inputs("states_ph", B=1, T=20, H=2, dk=128, dv=128, in_dtype=gi.BF16, seed=53,
+                           initial_state_std=0.05, decay_per_head=True)
+        tol = U.BF16_TOL
+    d = U.device_inputs(x, DEV)
+    st = d["initial_state"].clone() if d["initial_state"] is not None else \
+        torch.zeros((x.B, x.H, x.dk, x.dv), device=DEV)
+    states = torch.empty((x.B, x.T, x.H, x.dk, x.dv), device=DEV)
+    U.log(f"per-token states {case}: B={x.B} T={x.T} H={x.H} d={x.dk}")
+    m = None if x.mask is None else torch.from_numpy(x.mask.copy())
+    o = kda.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st, attention_mask=m,
+                           output_dtype=torch.float32, states=states)
+    torch.cuda.synchronize()
+    init = x.initial_state if x.initial_state is not None else None
+    ro, rfs, rst = R.kda_recurrence(x.f64("q"), x.f64("k"), x.f64("v"), x.f64("g"), x.f64("beta"), init,
+                                    mask=x.mask, return_states=True)
+    U.assert_close(f"states {case}", U.to_numpy64(states), rst, tol)
+    U.assert_close(f"states {case} o", U.to_numpy64(o)[U.valid_token_mask(x)], ro[U.valid_token_mask(x)], tol)
+    U.assert_close(f"states {case} final", U.to_numpy64(st), rfs, tol)
+    assert torch.equal(states[:, -1], st)
+
+
 def test_deterministic():
     x = gi.make_inputs("det", B=1, T=256, H=4, dk=128, dv=128, in_dtype=gi.BF16, seed=23,
                        initial_state_std=0.02, norm=True)

@@ -370,3 +370,21 @@ def test_per_head_decay_is_the_per_channel_decay_repeated():
     np.testing.assert_allclose(o4, o5, rtol=1e-9, atol=1e-11)
     np.testing.assert_allclose(s4, s5, rtol=1e-9, atol=1e-11)
 
+
+def test_per_token_states_are_the_final_states_of_the_prefixes():
+    """The state after token t (the per-token states the pages read) is the final state of
+    the same recurrence run over tokens 0..t; a padding token repeats the carried state."""
+    rng = np.random.default_rng(33)
+    B, T, H, dk, dv = 2, 7, 2, 4, 3
+    q, k, v, g, beta = _problem(rng, B, T, H, dk, dv)
+    S0 = rng.standard_normal((B, H, dk, dv))
+    m = np.ones((B, T), np.uint8)
+    m[1, 3] = 0
+    _, fin, states = R.kda_recurrence(q, k, v, g, beta, S0, mask=m, return_states=True)
+    for t in range(T):
+        _, ft = R.kda_recurrence(q[:, :t + 1], k[:, :t + 1], v[:, :t + 1], g[:, :t + 1], beta[:, :t + 1], S0,
+                                 mask=m[:, :t + 1])
+        np.testing.assert_allclose(states[:, t], ft, rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(states[1, 3], states[1, 2])
+    np.testing.assert_array_equal(states[:, -1], fin)
+
