@@ -165,6 +165,39 @@ def time_recurrent_states(kda, T: int = 256, reps: int = 5) -> dict:
             "unit": "GB/s", "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS}
 
 
+def time_layer_exit(kda, rows: int = B_DECODE, N: int = 7168, reps: int = 10) -> dict:
+    """The layer's exit at decode (gated norm of the 96 heads, then the 12,288 -> 7,168
+    output projection) for one new token per row, timed on its own; torch's bf16 Linear
+    on the same normed rows is timed beside it for reference."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(13)
+    K = H * D
+    o = torch.randn((rows, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+    gate = torch.randn((rows, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+    w = (1.0 + 0.1 * torch.randn((D,), generator=gen, device="cuda")).float()
+    W = ((torch.rand((N, K), generator=gen, device="cuda") * 2 - 1) / K ** 0.5).to(torch.bfloat16)
+    y = torch.empty((rows, K), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((rows, N), dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+    t = timed(lambda: kda.gated_norm_proj(o, gate, w, W, 1e-6, y=y, out=out))
+    t_ref = timed(lambda: torch.nn.functional.linear(y, W))
+    nbytes = N * K * 2 + rows * K * 2 * 3 + rows * N * 2 + D * 4
+    return {"rows": rows, "in_features": K, "out_features": N, "avg_call_us": t * 1e6, "algorithmic_bytes": nbytes,
+            "achieved": nbytes / t / 1e9, "unit": "GB/s", "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
+            "torch_linear_us": t_ref * 1e6}
+
+
 def _bytes_decode_state(B: int, H: int, d: int) -> int:
     return 2 * B * H * d * d * 4               # state read + written (fp32)
 
@@ -430,6 +463,8 @@ def main():
     per_head = time_per_head_decay(kda, P, ws, o, fs)
     print("[bench] per-token states", file=sys.stderr, flush=True)
     rec_states = time_recurrent_states(kda)
+    print("[bench] layer exit (gated norm + output projection)", file=sys.stderr, flush=True)
+    exit_ = time_layer_exit(kda)
 
     def roof(kernel, nbytes, t, **extra):
         gbs = nbytes / t / 1e9
@@ -489,6 +524,8 @@ def main():
         "prefill_per_head_decay": per_head,
         # the token-by-token kernel storing the state after every token, timed on its own
         "recurrent_states": rec_states,
+        # the gated norm + output projection of one decode token per row, timed on its own
+        "layer_exit_decode": exit_,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)

@@ -334,3 +334,39 @@ def conv_padded_from_packed(x: ConvInputs, *, left: bool = False) -> ConvInputs:
     return dataclasses.replace(x, name=x.name + ("_left" if left else "_right"), B=N, T=L, x=out,
                                cu_seqlens=None, mask=mask)
 
+
+# --------------------------------------------------------------------------- layer exit
+@dataclasses.dataclass
+class ProjInputs:
+    """The layer's exit at decode: head outputs o and output-gate values [rows, heads,
+    head_dim] (bf16 bits), the norm weight [head_dim] fp32 and the output projection
+    [out_features, heads * head_dim] (bf16 bits; the pages give no trained weights)."""
+
+    name: str
+    rows: int
+    heads: int
+    head_dim: int
+    out_features: int
+    o: np.ndarray
+    gate: np.ndarray
+    norm_weight: np.ndarray
+    proj_weight: np.ndarray
+    eps: float = 1e-6
+    seed: int = 0
+
+
+def proj_inputs(name: str, *, rows: int, heads: int = 96, head_dim: int = 128, out_features: int = 7168,
+                seed: int = 0) -> ProjInputs:
+    """Draw in the fixed order o, gate, norm weight, projection.  o, gate ~ N(0,1); the norm
+    weight ~ 1 + N(0, 0.1) as in the gated-norm configs; the projection ~ U(-1/sqrt(K),
+    1/sqrt(K)) with K = heads * head_dim, the default initialisation of a bias-free Linear."""
+    rng = np.random.default_rng(seed)
+    o = _draw(rng, (rows, heads, head_dim), "normal")
+    gate = _draw(rng, (rows, heads, head_dim), "normal")
+    w = _draw(rng, (head_dim,), "normal", std=0.1, mean=1.0)
+    K = heads * head_dim
+    bound = 1.0 / np.sqrt(K)
+    W = _draw(rng, (out_features, K), "uniform", low=-bound, high=bound)
+    return ProjInputs(name=name, rows=rows, heads=heads, head_dim=head_dim, out_features=out_features,
+                      o=_cast(o, BF16), gate=_cast(gate, BF16), norm_weight=w, proj_weight=_cast(W, BF16), seed=seed)
+

@@ -253,6 +253,38 @@ kda_status_t kda_short_conv(const kda_conv_params_t *p, const void *x, const flo
                             const void *initial_state, const int32_t *cu_seqlens,
                             const uint8_t *mask, void *y, void *final_state, void *stream);
 
+/*
+ * kda_gated_norm_proj -- the layer's exit at decode: the sigmoid-gated RMSNorm of each
+ * head's output, then the output projection (Kimi-K3 atlas, gate-project page: the heads
+ * [B, 1, 96 x 128] leave as [B, 1, 7168]; Parameters table: gated RMSNorm 128, output
+ * projection 88,080,384 = 12,288 x 7,168, no bias).
+ *   o, gate      [rows, heads * head_dim]  bf16 (rows = B * T, heads side by side)
+ *   norm_weight  [head_dim]                fp32, shared by all heads
+ *   proj_weight  [out_features, heads * head_dim]  bf16 (the Linear layout [out, in])
+ *   y            [rows, heads * head_dim]  bf16 output: the gated-normed heads (the
+ *                                          projection's input; may alias o)
+ *   out          [rows, out_features]      out_dtype: out = y proj_weight^T, fp32 accumulation
+ * head_dim a power of two in [8, 512]; heads * head_dim a multiple of 256; out_features a
+ * multiple of 32; rows <= 65535 * 64.  Two launches: the norm once per row and head, then
+ * the projection (a fused per-tile norm would repeat the norm in every output tile).
+ * All pointers 16-byte aligned device memory owned by the caller; nothing is allocated.
+ * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_ALIGN, KDA_ERR_UNSUPPORTED,
+ * KDA_ERR_HIP.
+ */
+kda_status_t kda_gated_norm_proj(const void *o, const void *gate, const float *norm_weight,
+                                 const void *proj_weight, void *y, void *out, int64_t rows,
+                                 int32_t heads, int32_t head_dim, int32_t out_features, float eps,
+                                 int32_t out_dtype, void *stream);
+
+/*
+ * kda_out_proj -- the output projection alone: out[rows, out_features] = x W^T with
+ * x [rows, in_features] bf16 and W [out_features, in_features] bf16 (Linear layout, no
+ * bias), fp32 accumulation, out in out_dtype.  in_features a multiple of 256,
+ * out_features a multiple of 32.  Pointers 16-byte aligned; errors as above.
+ */
+kda_status_t kda_out_proj(const void *x, const void *weight, void *out, int64_t rows,
+                          int32_t in_features, int32_t out_features, int32_t out_dtype, void *stream);
+
 /* Text of a status code (static storage). */
 const char *kda_status_string(kda_status_t s);
 /* Detail of the last non-OK status returned on this thread (thread-local storage). */

@@ -26,7 +26,7 @@ from typing import Optional
 import torch
 
 __all__ = ["chunk_prefill", "chunk_prefill_workspace_size", "chunk_prepare", "chunk_scan", "recurrent_step",
-           "gated_rmsnorm", "short_conv", "library_path", "load_library", "KdaError", "version"]
+           "gated_rmsnorm", "short_conv", "gated_norm_proj", "out_proj", "library_path", "load_library", "KdaError", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
@@ -84,6 +84,10 @@ def load_library():
     lib.kda_chunk_prepare.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 7 + [ctypes.c_size_t, P]
     lib.kda_chunk_scan.restype = ctypes.c_int
     lib.kda_chunk_scan.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 4 + [ctypes.c_size_t, P, P, P]
+    lib.kda_gated_norm_proj.restype = ctypes.c_int
+    lib.kda_gated_norm_proj.argtypes = [P] * 6 + [i64, i32, i32, i32, f32, i32, P]
+    lib.kda_out_proj.restype = ctypes.c_int
+    lib.kda_out_proj.argtypes = [P, P, P, i64, i32, i32, i32, P]
     lib.kda_short_conv.restype = ctypes.c_int
     lib.kda_short_conv.argtypes = [ctypes.POINTER(KdaConvParams)] + [P] * 8
     lib.kda_recurrent_step.restype = ctypes.c_int
@@ -468,4 +472,56 @@ def short_conv(x: torch.Tensor, weight: torch.Tensor, initial_state: Optional[to
     _check(lib.kda_short_conv(ctypes.byref(p), _ptr(x), _ptr(weight), _ptr(initial_state), _ptr(cu_dev),
                               _ptr(mask_dev), _ptr(y), _ptr(fs), _stream(dev)))
     return (y, fs) if with_final_state else y
+
+
+def out_proj(x: torch.Tensor, weight: torch.Tensor, *, output_dtype: Optional[torch.dtype] = None,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out = x @ weight^T for bf16 x [..., in_features] and weight [out_features,
+    in_features] (a Linear without bias); fp32 accumulation."""
+    lib = load_library()
+    dev = x.device
+    _dev(x, "x", dev)
+    _dev(weight, "weight", dev)
+    if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("x and weight must be bfloat16")
+    K = x.shape[-1]
+    N = weight.shape[0]
+    if weight.shape != (N, K):
+        raise ValueError("weight must be [out_features, in_features]")
+    rows = x.numel() // K if K else 0
+    res = out if out is not None else torch.empty(x.shape[:-1] + (N,), dtype=output_dtype or x.dtype, device=dev)
+    _dev(res, "out", dev)
+    _check(lib.kda_out_proj(_ptr(x), _ptr(weight), _ptr(res), rows, K, N, _dtype_code(res.dtype), _stream(dev)))
+    return res
+
+
+def gated_norm_proj(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tensor, proj_weight: torch.Tensor,
+                    eps: float = 1e-6, *, output_dtype: Optional[torch.dtype] = None,
+                    y: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """The layer's exit: y = gated RMSNorm of each head of o ([..., heads, head_dim], bf16)
+    with sigmoid(gate), then out = y_flat @ proj_weight^T (proj_weight [out_features,
+    heads * head_dim] bf16).  Returns (y [..., heads * head_dim], out [..., out_features])."""
+    lib = load_library()
+    dev = o.device
+    for name, t in (("o", o), ("gate", gate), ("norm_weight", norm_weight), ("proj_weight", proj_weight)):
+        _dev(t, name, dev)
+    if o.dtype != torch.bfloat16 or gate.dtype != torch.bfloat16 or proj_weight.dtype != torch.bfloat16:
+        raise TypeError("o, gate and proj_weight must be bfloat16")
+    if gate.shape != o.shape or o.dim() < 2:
+        raise ValueError("o and gate must be [..., heads, head_dim]")
+    heads, hd = o.shape[-2], o.shape[-1]
+    if norm_weight.dtype != torch.float32 or norm_weight.shape != (hd,):
+        raise ValueError("norm_weight must be float32 [head_dim]")
+    N = proj_weight.shape[0]
+    if proj_weight.shape != (N, heads * hd):
+        raise ValueError("proj_weight must be [out_features, heads * head_dim]")
+    rows = o.numel() // (heads * hd)
+    lead = o.shape[:-2]
+    yy = y if y is not None else torch.empty(lead + (heads * hd,), dtype=torch.bfloat16, device=dev)
+    _dev(yy, "y", dev)
+    res = out if out is not None else torch.empty(lead + (N,), dtype=output_dtype or torch.bfloat16, device=dev)
+    _dev(res, "out", dev)
+    _check(lib.kda_gated_norm_proj(_ptr(o), _ptr(gate), _ptr(norm_weight), _ptr(proj_weight), _ptr(yy), _ptr(res),
+                                   rows, heads, hd, N, float(eps), _dtype_code(res.dtype), _stream(dev)))
+    return yy, res
 

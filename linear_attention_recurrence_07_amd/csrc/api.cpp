@@ -336,6 +336,53 @@ kda_status_t kda_short_conv(const kda_conv_params_t *p, const void *x, const flo
   return KDA_OK;
 }
 
+kda_status_t kda_out_proj(const void *x, const void *weight, void *out, int64_t rows, int32_t in_features,
+                          int32_t out_features, int32_t out_dtype, void *stream) {
+  KDA_TRY(check_ptr(x, "x", true));
+  KDA_TRY(check_ptr(weight, "weight", true));
+  KDA_TRY(check_ptr(out, "out", true));
+  if (rows < 0 || in_features <= 0 || out_features <= 0)
+    return fail(KDA_ERR_SHAPE, "bad sizes rows=%lld in=%d out=%d", static_cast<long long>(rows), in_features,
+                out_features);
+  if (!valid_dtype(out_dtype)) return fail(KDA_ERR_DTYPE, "unknown dtype code %d", out_dtype);
+  if (!kda::out_proj_supports(rows, in_features, out_features))
+    return fail(KDA_ERR_UNSUPPORTED, "in_features %% 256, out_features %% 32 must be 0 and rows <= 65535 * 64");
+  KDA_TRY(hip_status(kda::launch_out_proj(x, weight, out, rows, in_features, out_features, out_dtype == KDA_BF16,
+                                          static_cast<hipStream_t>(stream)),
+                     "output projection"));
+  return KDA_OK;
+}
+
+kda_status_t kda_gated_norm_proj(const void *o, const void *gate, const float *norm_weight,
+                                 const void *proj_weight, void *y, void *out, int64_t rows, int32_t heads,
+                                 int32_t head_dim, int32_t out_features, float eps, int32_t out_dtype,
+                                 void *stream) {
+  KDA_TRY(check_ptr(o, "o", true));
+  KDA_TRY(check_ptr(gate, "gate", true));
+  KDA_TRY(check_ptr(norm_weight, "norm_weight", true));
+  KDA_TRY(check_ptr(proj_weight, "proj_weight", true));
+  KDA_TRY(check_ptr(y, "y", true));
+  KDA_TRY(check_ptr(out, "out", true));
+  if (rows < 0 || heads <= 0 || head_dim <= 0 || out_features <= 0)
+    return fail(KDA_ERR_SHAPE, "bad sizes rows=%lld heads=%d head_dim=%d out=%d", static_cast<long long>(rows),
+                heads, head_dim, out_features);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(KDA_ERR_SHAPE, "eps must be finite and >= 0");
+  if (!valid_dtype(out_dtype)) return fail(KDA_ERR_DTYPE, "unknown dtype code %d", out_dtype);
+  if (head_dim < 8 || head_dim > 512 || (head_dim & (head_dim - 1)) != 0)
+    return fail(KDA_ERR_UNSUPPORTED, "head_dim %d must be a power of two in [8, 512]", head_dim);
+  const int64_t K = static_cast<int64_t>(heads) * head_dim;
+  if (K > 0x7fffffff || !kda::out_proj_supports(rows, static_cast<int>(K), out_features))
+    return fail(KDA_ERR_UNSUPPORTED, "heads * head_dim %% 256, out_features %% 32 must be 0 and rows <= 65535 * 64");
+  if (rows * heads / 256 > 2147483647LL) return fail(KDA_ERR_SHAPE, "too many rows");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  KDA_TRY(hip_status(kda::launch_gated_rmsnorm(o, gate, norm_weight, y, rows * heads, head_dim, eps, 1, 1, 1, st),
+                     "gated norm"));
+  KDA_TRY(hip_status(kda::launch_out_proj(y, proj_weight, out, rows, static_cast<int>(K), out_features,
+                                          out_dtype == KDA_BF16, st),
+                     "output projection"));
+  return KDA_OK;
+}
+
 const char *kda_status_string(kda_status_t s) {
   switch (s) {
     case KDA_OK: return "KDA_OK";

@@ -31,3 +31,9 @@ def gated_norm_proj(o, gate, norm_weight, proj_weight, eps: float):
     y = y.reshape(rows, heads * hd)
     out = y @ np.asarray(proj_weight, dtype=np.float64).T
     return y, out
+
+
+def project(x, proj_weight):
+    """out = x W^T (the output projection alone), fp64."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(proj_weight, dtype=np.float64).T
+

@@ -22,7 +22,7 @@ def _declared_functions():
 
 def test_header_declares_the_three_entry_points():
     names = _declared_functions()
-    for n in ("kda_chunk_prefill", "kda_chunk_prefill_workspace_size", "kda_recurrent_step", "kda_short_conv",
+    for n in ("kda_chunk_prefill", "kda_chunk_prefill_workspace_size", "kda_recurrent_step", "kda_short_conv", "kda_gated_norm_proj", "kda_out_proj",
               "kda_gated_rmsnorm", "kda_status_string", "kda_last_error", "kda_version"):
         assert n in names
 
@@ -235,6 +235,30 @@ def test_conv_validation_codes():
     assert conv(W=1) == 6
     assert conv(B=70000) == 6
     assert conv(cu=A, N=0) == 2
+
+
+def test_out_proj_validation_codes():
+    lib = K.load_library()
+    op = lib.kda_out_proj
+    assert op(None, A, A, 64, 256, 32, 1, None) == 1
+    assert op(A, A, None, 64, 256, 32, 1, None) == 1
+    assert op(A, A, A, -1, 256, 32, 1, None) == 2
+    assert op(A, A, A, 64, 0, 32, 1, None) == 2
+    assert op(A, A, A, 64, 256, 32, 9, None) == 3
+    assert op(MIS, A, A, 64, 256, 32, 1, None) == 4
+    assert op(A, A, A, 64, 300, 32, 1, None) == 6             # in_features % 256
+    assert op(A, A, A, 64, 256, 40, 1, None) == 6             # out_features % 32
+    assert op(A, A, A, 0, 256, 32, 1, None) == 0              # no rows: nothing launched
+    gp = lib.kda_gated_norm_proj
+    args = [A, A, A, A, A, A]
+    assert gp(None, A, A, A, A, A, 64, 96, 128, 7168, 1e-6, 1, None) == 1
+    assert gp(A, A, A, A, None, A, 64, 96, 128, 7168, 1e-6, 1, None) == 1
+    assert gp(*args, 64, 0, 128, 7168, 1e-6, 1, None) == 2
+    assert gp(*args, 64, 96, 128, 7168, -1.0, 1, None) == 2
+    assert gp(*args, 64, 96, 100, 7168, 1e-6, 1, None) == 6   # head_dim not a power of two
+    assert gp(*args, 64, 3, 64, 7168, 1e-6, 1, None) == 6     # heads * head_dim % 256
+    assert gp(*args, 64, 96, 128, 7000, 1e-6, 1, None) == 6   # out_features % 32
+    assert gp(A, MIS, A, A, A, A, 64, 96, 128, 7168, 1e-6, 1, None) == 4
 
 
 def test_status_strings_and_version():
