@@ -190,12 +190,15 @@ def time_layer_exit(kda, rows: int = B_DECODE, N: int = 7168, reps: int = 10) ->
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / reps
-    t = timed(lambda: kda.gated_norm_proj(o, gate, w, W, 1e-6, y=y, out=out))
+    nws = kda.load_library().kda_out_proj_workspace_size(rows, K, N)
+    ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device="cuda")
+    t = timed(lambda: kda.gated_norm_proj(o, gate, w, W, 1e-6, y=y, out=out, workspace=ws))
+    t_proj = timed(lambda: kda.out_proj(y, W, out=out, workspace=ws))
     t_ref = timed(lambda: torch.nn.functional.linear(y, W))
     nbytes = N * K * 2 + rows * K * 2 * 3 + rows * N * 2 + D * 4
     return {"rows": rows, "in_features": K, "out_features": N, "avg_call_us": t * 1e6, "algorithmic_bytes": nbytes,
             "achieved": nbytes / t / 1e9, "unit": "GB/s", "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
-            "torch_linear_us": t_ref * 1e6}
+            "projection_us": t_proj * 1e6, "torch_linear_us": t_ref * 1e6}
 
 
 def _bytes_decode_state(B: int, H: int, d: int) -> int:

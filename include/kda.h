@@ -264,26 +264,36 @@ kda_status_t kda_short_conv(const kda_conv_params_t *p, const void *x, const flo
  *   y            [rows, heads * head_dim]  bf16 output: the gated-normed heads (the
  *                                          projection's input; may alias o)
  *   out          [rows, out_features]      out_dtype: out = y proj_weight^T, fp32 accumulation
+ *   workspace    device scratch of at least kda_out_proj_workspace_size(rows, heads *
+ *                head_dim, out_features) bytes (fp32 partial sums when K is split), 16-byte
+ *                aligned; may be NULL when that size is 0
  * head_dim a power of two in [8, 512]; heads * head_dim a multiple of 256; out_features a
- * multiple of 32; rows <= 65535 * 64.  Two launches: the norm once per row and head, then
- * the projection (a fused per-tile norm would repeat the norm in every output tile).
+ * multiple of 64; rows <= 65535 * 64.  The norm runs once per row and head, then the
+ * projection (a fused per-tile norm would repeat the norm in every output tile); for
+ * rows <= 64 the projection splits K and adds the partial sums in a fixed order.
  * All pointers 16-byte aligned device memory owned by the caller; nothing is allocated.
  * Errors: KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_ALIGN, KDA_ERR_UNSUPPORTED,
- * KDA_ERR_HIP.
+ * KDA_ERR_WORKSPACE, KDA_ERR_HIP.
  */
 kda_status_t kda_gated_norm_proj(const void *o, const void *gate, const float *norm_weight,
                                  const void *proj_weight, void *y, void *out, int64_t rows,
                                  int32_t heads, int32_t head_dim, int32_t out_features, float eps,
-                                 int32_t out_dtype, void *stream);
+                                 int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                                 void *stream);
 
 /*
  * kda_out_proj -- the output projection alone: out[rows, out_features] = x W^T with
  * x [rows, in_features] bf16 and W [out_features, in_features] bf16 (Linear layout, no
  * bias), fp32 accumulation, out in out_dtype.  in_features a multiple of 256,
- * out_features a multiple of 32.  Pointers 16-byte aligned; errors as above.
+ * out_features a multiple of 64.  Pointers 16-byte aligned; workspace and errors as above.
  */
 kda_status_t kda_out_proj(const void *x, const void *weight, void *out, int64_t rows,
-                          int32_t in_features, int32_t out_features, int32_t out_dtype, void *stream);
+                          int32_t in_features, int32_t out_features, int32_t out_dtype,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace kda_out_proj and kda_gated_norm_proj need (0 when K is not split or
+ * the sizes are unsupported). */
+size_t kda_out_proj_workspace_size(int64_t rows, int32_t in_features, int32_t out_features);
 
 /* Text of a status code (static storage). */
 const char *kda_status_string(kda_status_t s);

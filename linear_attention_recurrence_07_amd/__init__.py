@@ -85,9 +85,11 @@ def load_library():
     lib.kda_chunk_scan.restype = ctypes.c_int
     lib.kda_chunk_scan.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 4 + [ctypes.c_size_t, P, P, P]
     lib.kda_gated_norm_proj.restype = ctypes.c_int
-    lib.kda_gated_norm_proj.argtypes = [P] * 6 + [i64, i32, i32, i32, f32, i32, P]
+    lib.kda_gated_norm_proj.argtypes = [P] * 6 + [i64, i32, i32, i32, f32, i32, P, ctypes.c_size_t, P]
     lib.kda_out_proj.restype = ctypes.c_int
-    lib.kda_out_proj.argtypes = [P, P, P, i64, i32, i32, i32, P]
+    lib.kda_out_proj.argtypes = [P, P, P, i64, i32, i32, i32, P, ctypes.c_size_t, P]
+    lib.kda_out_proj_workspace_size.restype = ctypes.c_size_t
+    lib.kda_out_proj_workspace_size.argtypes = [i64, i32, i32]
     lib.kda_short_conv.restype = ctypes.c_int
     lib.kda_short_conv.argtypes = [ctypes.POINTER(KdaConvParams)] + [P] * 8
     lib.kda_recurrent_step.restype = ctypes.c_int
@@ -474,8 +476,17 @@ def short_conv(x: torch.Tensor, weight: torch.Tensor, initial_state: Optional[to
     return (y, fs) if with_final_state else y
 
 
+def _proj_workspace(lib, rows, K, N, dev, workspace):
+    need = lib.kda_out_proj_workspace_size(rows, K, N)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
+    else:
+        _dev(workspace, "workspace", dev)
+    return workspace, 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
 def out_proj(x: torch.Tensor, weight: torch.Tensor, *, output_dtype: Optional[torch.dtype] = None,
-             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out = x @ weight^T for bf16 x [..., in_features] and weight [out_features,
     in_features] (a Linear without bias); fp32 accumulation."""
     lib = load_library()
@@ -491,13 +502,16 @@ def out_proj(x: torch.Tensor, weight: torch.Tensor, *, output_dtype: Optional[to
     rows = x.numel() // K if K else 0
     res = out if out is not None else torch.empty(x.shape[:-1] + (N,), dtype=output_dtype or x.dtype, device=dev)
     _dev(res, "out", dev)
-    _check(lib.kda_out_proj(_ptr(x), _ptr(weight), _ptr(res), rows, K, N, _dtype_code(res.dtype), _stream(dev)))
+    ws, nbytes = _proj_workspace(lib, rows, K, N, dev, workspace)
+    _check(lib.kda_out_proj(_ptr(x), _ptr(weight), _ptr(res), rows, K, N, _dtype_code(res.dtype), _ptr(ws), nbytes,
+                            _stream(dev)))
     return res
 
 
 def gated_norm_proj(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tensor, proj_weight: torch.Tensor,
                     eps: float = 1e-6, *, output_dtype: Optional[torch.dtype] = None,
-                    y: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+                    y: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None):
     """The layer's exit: y = gated RMSNorm of each head of o ([..., heads, head_dim], bf16)
     with sigmoid(gate), then out = y_flat @ proj_weight^T (proj_weight [out_features,
     heads * head_dim] bf16).  Returns (y [..., heads * head_dim], out [..., out_features])."""
@@ -521,7 +535,9 @@ def gated_norm_proj(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tens
     _dev(yy, "y", dev)
     res = out if out is not None else torch.empty(lead + (N,), dtype=output_dtype or torch.bfloat16, device=dev)
     _dev(res, "out", dev)
+    ws, nbytes = _proj_workspace(lib, rows, heads * hd, N, dev, workspace)
     _check(lib.kda_gated_norm_proj(_ptr(o), _ptr(gate), _ptr(norm_weight), _ptr(proj_weight), _ptr(yy), _ptr(res),
-                                   rows, heads, hd, N, float(eps), _dtype_code(res.dtype), _stream(dev)))
+                                   rows, heads, hd, N, float(eps), _dtype_code(res.dtype), _ptr(ws), nbytes,
+                                   _stream(dev)))
     return yy, res
 

@@ -336,8 +336,23 @@ kda_status_t kda_short_conv(const kda_conv_params_t *p, const void *x, const flo
   return KDA_OK;
 }
 
+static kda_status_t check_proj_workspace(int64_t rows, int K, int N, const void *ws, size_t bytes) {
+  const size_t need = kda::out_proj_workspace_bytes(rows, K, N);
+  if (bytes < need || (need > 0 && ws == nullptr))
+    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, bytes,
+                ws == nullptr ? " (NULL)" : "");
+  return check_ptr(ws, "workspace", false);
+}
+
+size_t kda_out_proj_workspace_size(int64_t rows, int32_t in_features, int32_t out_features) {
+  if (rows < 0 || in_features <= 0 || out_features <= 0 || !kda::out_proj_supports(rows, in_features, out_features))
+    return 0;
+  return kda::out_proj_workspace_bytes(rows, in_features, out_features);
+}
+
 kda_status_t kda_out_proj(const void *x, const void *weight, void *out, int64_t rows, int32_t in_features,
-                          int32_t out_features, int32_t out_dtype, void *stream) {
+                          int32_t out_features, int32_t out_dtype, void *workspace, size_t workspace_bytes,
+                          void *stream) {
   KDA_TRY(check_ptr(x, "x", true));
   KDA_TRY(check_ptr(weight, "weight", true));
   KDA_TRY(check_ptr(out, "out", true));
@@ -346,9 +361,10 @@ kda_status_t kda_out_proj(const void *x, const void *weight, void *out, int64_t 
                 out_features);
   if (!valid_dtype(out_dtype)) return fail(KDA_ERR_DTYPE, "unknown dtype code %d", out_dtype);
   if (!kda::out_proj_supports(rows, in_features, out_features))
-    return fail(KDA_ERR_UNSUPPORTED, "in_features %% 256, out_features %% 32 must be 0 and rows <= 65535 * 64");
+    return fail(KDA_ERR_UNSUPPORTED, "in_features %% 256, out_features %% 64 must be 0 and rows <= 65535 * 64");
+  KDA_TRY(check_proj_workspace(rows, in_features, out_features, workspace, workspace_bytes));
   KDA_TRY(hip_status(kda::launch_out_proj(x, weight, out, rows, in_features, out_features, out_dtype == KDA_BF16,
-                                          static_cast<hipStream_t>(stream)),
+                                          workspace, static_cast<hipStream_t>(stream)),
                      "output projection"));
   return KDA_OK;
 }
@@ -356,7 +372,7 @@ kda_status_t kda_out_proj(const void *x, const void *weight, void *out, int64_t 
 kda_status_t kda_gated_norm_proj(const void *o, const void *gate, const float *norm_weight,
                                  const void *proj_weight, void *y, void *out, int64_t rows, int32_t heads,
                                  int32_t head_dim, int32_t out_features, float eps, int32_t out_dtype,
-                                 void *stream) {
+                                 void *workspace, size_t workspace_bytes, void *stream) {
   KDA_TRY(check_ptr(o, "o", true));
   KDA_TRY(check_ptr(gate, "gate", true));
   KDA_TRY(check_ptr(norm_weight, "norm_weight", true));
@@ -372,13 +388,14 @@ kda_status_t kda_gated_norm_proj(const void *o, const void *gate, const float *n
     return fail(KDA_ERR_UNSUPPORTED, "head_dim %d must be a power of two in [8, 512]", head_dim);
   const int64_t K = static_cast<int64_t>(heads) * head_dim;
   if (K > 0x7fffffff || !kda::out_proj_supports(rows, static_cast<int>(K), out_features))
-    return fail(KDA_ERR_UNSUPPORTED, "heads * head_dim %% 256, out_features %% 32 must be 0 and rows <= 65535 * 64");
+    return fail(KDA_ERR_UNSUPPORTED, "heads * head_dim %% 256, out_features %% 64 must be 0 and rows <= 65535 * 64");
   if (rows * heads / 256 > 2147483647LL) return fail(KDA_ERR_SHAPE, "too many rows");
+  KDA_TRY(check_proj_workspace(rows, static_cast<int>(K), out_features, workspace, workspace_bytes));
   const hipStream_t st = static_cast<hipStream_t>(stream);
   KDA_TRY(hip_status(kda::launch_gated_rmsnorm(o, gate, norm_weight, y, rows * heads, head_dim, eps, 1, 1, 1, st),
                      "gated norm"));
   KDA_TRY(hip_status(kda::launch_out_proj(y, proj_weight, out, rows, static_cast<int>(K), out_features,
-                                          out_dtype == KDA_BF16, st),
+                                          out_dtype == KDA_BF16, workspace, st),
                      "output projection"));
   return KDA_OK;
 }

@@ -45,8 +45,9 @@ hipError_t launch_recurrent(const Args &a, hipStream_t s);
 hipError_t launch_short_conv(const ConvArgs &a, hipStream_t s);
 // Output projection out[M, N] = x[M, K] W[N, K]^T, bf16 operands, fp32 accumulation.
 bool out_proj_supports(int64_t M, int K, int N);
+size_t out_proj_workspace_bytes(int64_t M, int K, int N);
 hipError_t launch_out_proj(const void *x, const void *w, void *out, int64_t M, int K, int N, int out_bf16,
-                           hipStream_t s);
+                           void *ws, hipStream_t s);
 hipError_t launch_prefill_valu(const Args &a, hipStream_t s);
 // bf16 chunked prefill, d = 128: the per-chunk preparation (writes one record per
 // (slot, head) into ws), then the state scan that reads them.

@@ -3,11 +3,14 @@
 // enter the output projection, 12,288 -> 7,168 features, no bias).
 //
 // At decode the rows are few (one per sequence) and the 176 MB weight is read once, so
-// the kernel is bound by that stream: a work-group owns 32 output features over the full
-// K for up to 64 rows (224 work-groups at N = 7168), and stages the rows and its weight
-// slice through double-buffered LDS in 256-wide K chunks while the matrix cores work on
-// the previous chunk.  Wave w multiplies rows 16w..16w+15 against both 16-feature halves
-// (MFMA 16x16x32 bf16, fp32 accumulation).  Larger row counts tile over a grid axis.
+// the kernel is bound by that stream.  A work-group owns 64 output features and one of S
+// slices of K for up to 64 rows; its four waves each stream 16 weight rows straight from
+// HBM into registers (loads for the next 256-wide K chunk are in flight while the current
+// one is multiplied), and share the rows, which are staged through double-buffered LDS.
+// Wave w computes features 16w..16w+15 for all 64 rows (MFMA 16x16x32 bf16, fp32
+// accumulation).  With S > 1 each slice writes fp32 partial sums to a workspace and a
+// second launch adds the S partials in a fixed order (deterministic results); S = 4 at
+// the decode shape gives 448 work-groups, enough loads in flight for the weight stream.
 #include "kda_chunk.h"
 #include "kda_launch.h"
 
@@ -16,39 +19,40 @@ namespace {
 using chunk::u32x4;
 
 constexpr int BM = 64;          // rows per work-group
-constexpr int BN = 32;          // output features per work-group
-constexpr int KC = 256;         // K per LDS chunk
+constexpr int BN = 64;          // output features per work-group (16 per wave)
+constexpr int KC = 256;         // K per chunk
 constexpr int NTH = 256;
 constexpr int LDR = KC + 8;     // LDS row stride (bf16): 16 bytes of padding per row
 constexpr int PA = BM * KC / 8 / NTH;   // 16-byte pieces of the row chunk per thread (8)
-constexpr int PB = BN * KC / 8 / NTH;   // pieces of the weight chunk per thread (4)
-
-struct Smem {
-  uint16_t a[2][BM * LDR];
-  uint16_t b[2][BN * LDR];
-};
-static_assert(sizeof(Smem) <= 160 * 1024, "LDS");
+constexpr int KS = KC / 32;     // MFMA K steps per chunk (8)
 
 __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                   0, 0, 0);
 }
 
-template <typename TOut>
+// Rows [m0, m0+64) x features [n0, n0+64) over K range [kb, kb + klen).  dst: out (S = 1,
+// TOut) or this slice's fp32 partial tile.
+template <typename TDst>
 __global__ void __launch_bounds__(NTH)
-out_proj_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, TOut *__restrict__ out,
-                int M, int N, int K) {
-  __shared__ Smem sm;
+out_proj_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, TDst *__restrict__ dst,
+                int M, int N, int K, int klen, size_t slice_stride) {
+  __shared__ uint16_t sa[2][BM * LDR];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
   const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
-  const int nchunks = K / KC;
+  const int slice = blockIdx.y;
+  const int m0 = blockIdx.z * BM;
+  const int kb = slice * klen;
+  const int nchunks = klen / KC;
+  TDst *out = dst + slice * slice_stride;
 
-  u32x4 ra[PA], rb[PB];
+  // this lane's weight row and K offset inside each 32-wide step
+  const uint16_t *wrow = w + static_cast<size_t>(n0 + 16 * wave + l16) * K + kb + 8 * lg;
+  u32x4 ra[PA], wb[KS];
   auto load = [&](int c) {
-    const int k0 = c * KC;
+    const int k0 = kb + c * KC;
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
       const int p = tid + NTH * i, row = p / (KC / 8), col = (p % (KC / 8)) * 8;
@@ -56,54 +60,67 @@ out_proj_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, 
                              : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int i = 0; i < PB; ++i) {
-      const int p = tid + NTH * i, row = p / (KC / 8), col = (p % (KC / 8)) * 8;
-      rb[i] = *reinterpret_cast<const u32x4 *>(w + static_cast<size_t>(n0 + row) * K + k0 + col);
-    }
+    for (int s = 0; s < KS; ++s) wb[s] = *reinterpret_cast<const u32x4 *>(wrow + c * KC + 32 * s);
     __asm__ volatile("" ::: "memory");
   };
   auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
       const int p = tid + NTH * i, row = p / (KC / 8), col = (p % (KC / 8)) * 8;
-      *reinterpret_cast<u32x4 *>(&sm.a[buf][row * LDR + col]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < PB; ++i) {
-      const int p = tid + NTH * i, row = p / (KC / 8), col = (p % (KC / 8)) * 8;
-      *reinterpret_cast<u32x4 *>(&sm.b[buf][row * LDR + col]) = rb[i];
+      *reinterpret_cast<u32x4 *>(&sa[buf][row * LDR + col]) = ra[i];
     }
   };
 
-  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f32x4 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   load(0);
   stage(0);
+  u32x4 wc[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) wc[s] = wb[s];
   sync_lds();
   for (int c = 0; c < nchunks; ++c) {
     const int buf = c & 1;
     if (c + 1 < nchunks) load(c + 1);
-    // lane (lg, r): row r of the tile, K elements 32s + 8lg .. +7 (the same K slots on
-    // both operands)
-    const uint16_t *pa = &sm.a[buf][(16 * wave + l16) * LDR + 8 * lg];
-    const uint16_t *pb0 = &sm.b[buf][l16 * LDR + 8 * lg];
-    const uint16_t *pb1 = &sm.b[buf][(16 + l16) * LDR + 8 * lg];
+    // lane (lg, r): row r of each 16-row tile and K elements 32s + 8lg .. +7, the same
+    // K slots as its weight fragment
 #pragma unroll
-    for (int s = 0; s < KC / 32; ++s) {
-      const u32x4 a = *reinterpret_cast<const u32x4 *>(pa + 32 * s);
-      acc[0] = mma(a, *reinterpret_cast<const u32x4 *>(pb0 + 32 * s), acc[0]);
-      acc[1] = mma(a, *reinterpret_cast<const u32x4 *>(pb1 + 32 * s), acc[1]);
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(&sa[buf][(16 * t + l16) * LDR + 32 * s + 8 * lg]);
+        acc[t] = mma(a, wc[s], acc[t]);
+      }
+    if (c + 1 < nchunks) {
+      stage(buf ^ 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) wc[s] = wb[s];
     }
-    if (c + 1 < nchunks) stage(buf ^ 1);
     sync_lds();
   }
-  // acc[t][i] = out[m0 + 16 wave + 4 lg + i][n0 + 16 t + l16]
+  // acc[t][i] = out[m0 + 16t + 4lg + i][n0 + 16 wave + l16]
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = m0 + 16 * wave + 4 * lg + i;
-      if (row < M) Elem<TOut>::store(out, static_cast<size_t>(row) * N + n0 + 16 * t + l16, acc[t][i]);
+      const int row = m0 + 16 * t + 4 * lg + i;
+      if (row < M) Elem<TDst>::store(out, static_cast<size_t>(row) * N + n0 + 16 * wave + l16, acc[t][i]);
     }
+}
+
+// out = sum over S slices of the fp32 partials, in slice order.
+template <typename TOut>
+__global__ void __launch_bounds__(NTH)
+out_proj_reduce_kernel(const float *__restrict__ part, TOut *__restrict__ out, size_t count, int S) {
+  const size_t i = (static_cast<size_t>(blockIdx.x) * NTH + threadIdx.x) * 4;
+  if (i >= count) return;
+  float4 a = *reinterpret_cast<const float4 *>(part + i);
+  for (int s = 1; s < S; ++s) {
+    const float4 b = *reinterpret_cast<const float4 *>(part + static_cast<size_t>(s) * count + i);
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  Elem<TOut>::store4(out, i, a);
 }
 
 }  // namespace
@@ -112,17 +129,48 @@ bool out_proj_supports(int64_t M, int K, int N) {
   return K > 0 && K % KC == 0 && N > 0 && N % BN == 0 && M >= 0 && (M + BM - 1) / BM <= 65535;
 }
 
+// K slices: 4 (or 2) when the rows fit one tile and K divides evenly, else 1.
+int out_proj_slices(int64_t M, int K) {
+  if (M > BM) return 1;
+  if (K % (4 * KC) == 0) return 4;
+  if (K % (2 * KC) == 0) return 2;
+  return 1;
+}
+
+size_t out_proj_workspace_bytes(int64_t M, int K, int N) {
+  const int S = out_proj_slices(M, K);
+  return S > 1 ? static_cast<size_t>(S) * static_cast<size_t>(M) * N * sizeof(float) : 0;
+}
+
 hipError_t launch_out_proj(const void *x, const void *w, void *out, int64_t M, int K, int N, int out_bf16,
-                           hipStream_t st) {
+                           void *ws, hipStream_t st) {
   if (M == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(N / BN), static_cast<unsigned>((M + BM - 1) / BM));
+  const int S = out_proj_slices(M, K);
+  const dim3 grid(static_cast<unsigned>(N / BN), static_cast<unsigned>(S), static_cast<unsigned>((M + BM - 1) / BM));
   const uint16_t *xx = static_cast<const uint16_t *>(x), *ww = static_cast<const uint16_t *>(w);
+  const int klen = K / S;
+  if (S == 1) {
+    if (out_bf16)
+      hipLaunchKernelGGL((out_proj_kernel<uint16_t>), grid, dim3(NTH), 0, st, xx, ww, static_cast<uint16_t *>(out),
+                         static_cast<int>(M), N, K, klen, size_t(0));
+    else
+      hipLaunchKernelGGL((out_proj_kernel<float>), grid, dim3(NTH), 0, st, xx, ww, static_cast<float *>(out),
+                         static_cast<int>(M), N, K, klen, size_t(0));
+    return hipGetLastError();
+  }
+  float *part = static_cast<float *>(ws);
+  const size_t count = static_cast<size_t>(M) * N;
+  hipLaunchKernelGGL((out_proj_kernel<float>), grid, dim3(NTH), 0, st, xx, ww, part, static_cast<int>(M), N, K,
+                     klen, count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned rb = static_cast<unsigned>((count / 4 + NTH - 1) / NTH);
   if (out_bf16)
-    hipLaunchKernelGGL((out_proj_kernel<uint16_t>), grid, dim3(NTH), 0, st, xx, ww, static_cast<uint16_t *>(out),
-                       static_cast<int>(M), N, K);
+    hipLaunchKernelGGL((out_proj_reduce_kernel<uint16_t>), dim3(rb), dim3(NTH), 0, st, part,
+                       static_cast<uint16_t *>(out), count, S);
   else
-    hipLaunchKernelGGL((out_proj_kernel<float>), grid, dim3(NTH), 0, st, xx, ww, static_cast<float *>(out),
-                       static_cast<int>(M), N, K);
+    hipLaunchKernelGGL((out_proj_reduce_kernel<float>), dim3(rb), dim3(NTH), 0, st, part, static_cast<float *>(out),
+                       count, S);
   return hipGetLastError();
 }
 

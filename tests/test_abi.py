@@ -22,7 +22,7 @@ def _declared_functions():
 
 def test_header_declares_the_three_entry_points():
     names = _declared_functions()
-    for n in ("kda_chunk_prefill", "kda_chunk_prefill_workspace_size", "kda_recurrent_step", "kda_short_conv", "kda_gated_norm_proj", "kda_out_proj",
+    for n in ("kda_chunk_prefill", "kda_chunk_prefill_workspace_size", "kda_recurrent_step", "kda_short_conv", "kda_gated_norm_proj", "kda_out_proj", "kda_out_proj_workspace_size",
               "kda_gated_rmsnorm", "kda_status_string", "kda_last_error", "kda_version"):
         assert n in names
 
@@ -239,26 +239,40 @@ def test_conv_validation_codes():
 
 def test_out_proj_validation_codes():
     lib = K.load_library()
-    op = lib.kda_out_proj
-    assert op(None, A, A, 64, 256, 32, 1, None) == 1
-    assert op(A, A, None, 64, 256, 32, 1, None) == 1
-    assert op(A, A, A, -1, 256, 32, 1, None) == 2
-    assert op(A, A, A, 64, 0, 32, 1, None) == 2
-    assert op(A, A, A, 64, 256, 32, 9, None) == 3
-    assert op(MIS, A, A, 64, 256, 32, 1, None) == 4
-    assert op(A, A, A, 64, 300, 32, 1, None) == 6             # in_features % 256
-    assert op(A, A, A, 64, 256, 40, 1, None) == 6             # out_features % 32
-    assert op(A, A, A, 0, 256, 32, 1, None) == 0              # no rows: nothing launched
-    gp = lib.kda_gated_norm_proj
-    args = [A, A, A, A, A, A]
-    assert gp(None, A, A, A, A, A, 64, 96, 128, 7168, 1e-6, 1, None) == 1
-    assert gp(A, A, A, A, None, A, 64, 96, 128, 7168, 1e-6, 1, None) == 1
-    assert gp(*args, 64, 0, 128, 7168, 1e-6, 1, None) == 2
-    assert gp(*args, 64, 96, 128, 7168, -1.0, 1, None) == 2
-    assert gp(*args, 64, 96, 100, 7168, 1e-6, 1, None) == 6   # head_dim not a power of two
-    assert gp(*args, 64, 3, 64, 7168, 1e-6, 1, None) == 6     # heads * head_dim % 256
-    assert gp(*args, 64, 96, 128, 7000, 1e-6, 1, None) == 6   # out_features % 32
-    assert gp(A, MIS, A, A, A, A, 64, 96, 128, 7168, 1e-6, 1, None) == 4
+    ws = lib.kda_out_proj_workspace_size
+    assert ws(64, 12288, 7168) == 4 * 64 * 7168 * 4          # K split 4 ways: fp32 partials
+    assert ws(64, 512, 64) == 2 * 64 * 64 * 4
+    assert ws(64, 256, 64) == 0                              # one K slice: no partials
+    assert ws(65, 12288, 7168) == 0                          # more than 64 rows: not split
+    assert ws(64, 300, 64) == 0                              # unsupported sizes
+
+    def op(x=A, w=A, out=A, rows=64, K=256, N=64, dt=1, wsp=None, nb=0):
+        return lib.kda_out_proj(x, w, out, rows, K, N, dt, wsp, nb, None)
+
+    assert op(x=None) == 1
+    assert op(out=None) == 1
+    assert op(rows=-1) == 2
+    assert op(K=0) == 2
+    assert op(dt=9) == 3
+    assert op(x=MIS) == 4
+    assert op(K=300) == 6                                    # in_features % 256
+    assert op(N=96) == 6                                     # out_features % 64
+    assert op(K=1024) == 8                                   # split K needs the workspace
+    assert op(K=1024, wsp=MIS, nb=ws(64, 1024, 64)) == 4
+    assert op(rows=0) == 0                                   # no rows: nothing launched
+
+    def gp(o=A, gate=A, w=A, pw=A, y=A, out=A, rows=64, heads=96, hd=128, N=7168, eps=1e-6, dt=1, wsp=None, nb=0):
+        return lib.kda_gated_norm_proj(o, gate, w, pw, y, out, rows, heads, hd, N, eps, dt, wsp, nb, None)
+
+    assert gp(o=None) == 1
+    assert gp(y=None) == 1
+    assert gp(heads=0) == 2
+    assert gp(eps=-1.0) == 2
+    assert gp(hd=100) == 6                                   # head_dim not a power of two
+    assert gp(heads=3, hd=64) == 6                           # heads * head_dim % 256
+    assert gp(N=7000) == 6                                   # out_features % 64
+    assert gp(gate=MIS) == 4
+    assert gp() == 8                                         # the decode shape needs the workspace
 
 
 def test_status_strings_and_version():

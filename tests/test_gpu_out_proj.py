@@ -26,7 +26,8 @@ def _bf16(a):
     return U.to_torch(a, gi.BF16, DEV)
 
 
-@pytest.mark.parametrize("rows,K,N", [(1, 256, 32), (5, 768, 96), (64, 512, 64), (70, 256, 32), (200, 1024, 160)])
+@pytest.mark.parametrize("rows,K,N", [(1, 256, 64), (5, 768, 128), (64, 512, 64), (64, 4096, 192), (70, 1024, 64),
+                                      (200, 1024, 128)])
 def test_projection_alone(rows, K, N):
     import linear_attention_recurrence_07_amd as kda
     rng = np.random.default_rng(rows + K + N)
