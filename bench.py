@@ -40,30 +40,35 @@ D_HEAD = D
 B_DECODE, P_DECODE = 64, 1000
 
 
-def _bytes_prefill(T: int, H: int, d: int, with_init: bool) -> int:
-    """Algorithmic HBM bytes of one prefill launch: q, k, v (bf16), g (fp32), beta (fp32)
-    read, o (bf16) written, final state (fp32) written (+ read when an initial state is
-    given)."""
-    per_tok_head = 3 * d * 2 + d * 4 + 4 + d * 2
+def _bytes_prefill(T: int, H: int, d: int, with_init: bool, norm: bool = False) -> int:
+    """Algorithmic HBM bytes of one prefill: q, k, v (bf16), g (fp32), beta (fp32) read,
+    o (bf16) written, final state (fp32) written (+ read when an initial state is given);
+    with the gated norm also gate (bf16) read and y (bf16) written."""
+    per_tok_head = 3 * d * 2 + d * 4 + 4 + d * 2 + (2 * d * 2 if norm else 0)
     state = H * d * d * 4
     return T * H * per_tok_head + state * (2 if with_init else 1)
 
 
 REC_BYTES = 30224      # one chunk record (per 32-token chunk and head) in the workspace
+XCHG_BYTES = 512       # the scan's norm-exchange words per chunk and head, cleared by the preparation
 CHUNK = 32
 
 
 def _bytes_prep(T: int, H: int, d: int) -> int:
     """Algorithmic bytes of one preparation launch: per chunk and head, q, k (bf16), g
-    (fp32) and beta (fp32) of its 32 tokens read and its record written."""
-    per_chunk = CHUNK * (2 * d * 2 + d * 4 + 4) + REC_BYTES
+    (fp32) and beta (fp32) of its 32 tokens read, its record and cleared exchange words
+    written."""
+    per_chunk = CHUNK * (2 * d * 2 + d * 4 + 4) + REC_BYTES + XCHG_BYTES
     return (T // CHUNK) * H * per_chunk
 
 
-def _bytes_scan(T: int, H: int, d: int, with_init: bool) -> int:
+def _bytes_scan(T: int, H: int, d: int, with_init: bool, norm: bool = False) -> int:
     """Algorithmic bytes of one scan launch: per chunk and head, its record and v (bf16)
-    read, o (bf16) written; the final state (fp32) written (+ read with an initial state)."""
-    per_chunk = REC_BYTES + CHUNK * d * 2 * 2
+    read, o (bf16) written, with the gated norm also gate read and y written (bf16); the
+    final state (fp32) written (+ read with an initial state).  The exchange words of the
+    norm (512 B per chunk and head, written and read once) are the split into two tiles'
+    own traffic and are not counted."""
+    per_chunk = REC_BYTES + CHUNK * d * 2 * (4 if norm else 2)
     state = H * d * d * 4
     return (T // CHUNK) * H * per_chunk + state * (2 if with_init else 1)
 
@@ -199,6 +204,23 @@ def time_layer_exit(kda, rows: int = B_DECODE, N: int = 7168, reps: int = 10) ->
     return {"rows": rows, "in_features": K, "out_features": N, "avg_call_us": t * 1e6, "algorithmic_bytes": nbytes,
             "achieved": nbytes / t / 1e9, "unit": "GB/s", "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
             "projection_us": t_proj * 1e6, "torch_linear_us": t_ref * 1e6}
+
+
+def time_fused_norm_scan(kda, P, ws, o, fs, y, reps: int = 10) -> float:
+    """Average duration of the scan that applies the gated norm itself, over the records
+    the step's preparation left in ws, from HIP events on the current stream."""
+    def call():
+        kda.chunk_scan(P["v"], ws, out=o, final_state=fs, gate=P["gate"], norm_weight=P["w"], norm_eps=P["eps"], y=y)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
 
 
 def _bytes_decode_state(B: int, H: int, d: int) -> int:
@@ -458,6 +480,8 @@ def main():
 
     traffic = measured_traffic()
     mfma = measured_mfma()
+    print("[bench] scan with its own gated norm", file=sys.stderr, flush=True)
+    t_fused = time_fused_norm_scan(kda, P, ws, o, fs, y)
     print("[bench] copy and GEMM ceilings", file=sys.stderr, flush=True)
     ceil = ceilings()
     print("[bench] short convolution", file=sys.stderr, flush=True)
@@ -512,13 +536,18 @@ def main():
         "roofline": r_prep if t_prep >= t_scan else r_scan,
         "roofline_prepare": r_prep,
         "roofline_scan": r_scan,
-        # whole prefill against the bytes it must move (inputs in, o and final state out;
+        # whole prefill against the bytes it must move (inputs in, o, y and final state out;
         # the workspace records are the two-launch design's own traffic)
         "roofline_prefill_path": roof("chunk_prep_kernel + chunk_scan_kernel", b_path, t_prep + t_scan,
                                       algorithmic_tflops=_algorithmic_flops(T_PREFILL, H, D, CHUNK) / (t_prep + t_scan) / 1e12,
                                       algorithmic_flops_per_launch=_algorithmic_flops(T_PREFILL, H, D, CHUNK)),
         "roofline_decode": roof("recurrent_kernel", b_dec_all, t_dec),
         "roofline_norm": roof("gated_rmsnorm_kernel", b_nrm, t_nrm),
+        # the scan applying the gated norm itself (kda_chunk_scan with gate and y), timed on
+        # its own, against the step's scan + separate norm
+        "scan_with_fused_norm": {"avg_call_us": t_fused * 1e6, "scan_plus_norm_us": (t_scan + t_nrm) * 1e6,
+                                 "algorithmic_bytes": _bytes_scan(T_PREFILL, H, D, False, norm=True),
+                                 "achieved_GBps": _bytes_scan(T_PREFILL, H, D, False, norm=True) / t_fused / 1e9},
         "ceilings": ceil,
         # the causal short convolution in front of the kernel, timed on its own (two
         # launches per call: the filter over all tokens, then the carried-input update)

@@ -113,7 +113,9 @@ typedef struct {
  *
  * The bf16 kernel for dk = dv = 128 runs in two launches: a preparation pass over every
  * (sequence, head, chunk) at once, which stores each chunk's intra-chunk products in the
- * workspace (30,224 bytes per chunk and head), then the sequential state scan.
+ * workspace (30,224 bytes per chunk and head, plus 512 bytes that kda_chunk_scan's own
+ * norm uses), then the sequential state scan; with y given, a third launch applies the
+ * gated norm to o.
  */
 kda_status_t kda_chunk_prefill(const kda_params_t *p,
                                const void *q, const void *k, const void *v,
@@ -128,15 +130,16 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p,
  * kda_chunk_prefill_workspace_size -- bytes of workspace kda_chunk_prefill needs for
  * these params; `packed` is nonzero when cu_seqlens will be given (p->num_seqs set).
  * 0 for invalid params or when the chosen kernel needs none.  With packing it is
- * (N + ceil(T / 32)) * H * 30224 bytes, otherwise B * ceil(T / 32) * H * 30224.
+ * (N + ceil(T / 32)) * H * 30736 bytes, otherwise B * ceil(T / 32) * H * 30736.
  */
 size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed);
 
 /*
  * kda_chunk_prepare, kda_chunk_scan -- the two launches of kda_chunk_prefill's bf16,
  * dk = dv = 128 kernel, callable one at a time (same chunked form as kda_chunk_prefill;
- * nnterp Kimi-Linear page, Notes, "Loading").  kda_chunk_prefill without the gated norm
- * is exactly kda_chunk_prepare followed by kda_chunk_scan on the same stream.
+ * nnterp Kimi-Linear page, Notes, "Loading").  kda_chunk_prefill is exactly
+ * kda_chunk_prepare followed by kda_chunk_scan on the same stream (then, with y, the
+ * gated norm over o, as kda_gated_rmsnorm).
  *
  * kda_chunk_prepare reads q, k, g, beta (and cu_seqlens or mask, as in kda_chunk_prefill)
  * and fills the workspace with one record per (sequence, head, chunk): everything about a
@@ -144,7 +147,14 @@ size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed);
  * ahead of the scan that consumes it.
  *
  * kda_chunk_scan reads v, initial_state (or NULL) and the records, and writes o and
- * final_state.  p and cu_seqlens must be those the workspace was prepared with, and the
+ * final_state; with gate, norm_weight and y (all set or all NULL, as in
+ * kda_chunk_prefill; eps is p->norm_eps) it also writes the gated norm y itself, in
+ * the same launch: each head's 128 value columns are scanned by two work-groups of 64,
+ * which exchange per-token sums of squares through the workspace (device-coherent
+ * 64-bit words; a wait for the other work-group is bounded and, if it ever ran out,
+ * would give NaN in y rather than hang).  That saves the second read of o but loads the
+ * scan, so at large T it is slower than the separate norm; kda_chunk_prefill uses the
+ * separate one.  p and cu_seqlens must be those the workspace was prepared with, and the
  * preparation must have completed or be ordered before the scan on the stream; the
  * workspace must not be modified in between.  The records already hold the effect of a
  * mask, so the scan takes none.
@@ -163,7 +173,8 @@ kda_status_t kda_chunk_prepare(const kda_params_t *p,
 kda_status_t kda_chunk_scan(const kda_params_t *p, const void *v,
                             const float *initial_state, const int32_t *cu_seqlens,
                             const void *workspace, size_t workspace_bytes,
-                            void *o, float *final_state, void *stream);
+                            void *o, float *final_state,
+                            const void *gate, const float *norm_weight, void *y, void *stream);
 
 /*
  * kda_recurrent_step -- the decode kernel: the token-by-token form, for one new token

@@ -83,7 +83,7 @@ def load_library():
     lib.kda_chunk_prepare.restype = ctypes.c_int
     lib.kda_chunk_prepare.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 7 + [ctypes.c_size_t, P]
     lib.kda_chunk_scan.restype = ctypes.c_int
-    lib.kda_chunk_scan.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 4 + [ctypes.c_size_t, P, P, P]
+    lib.kda_chunk_scan.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 4 + [ctypes.c_size_t] + [P] * 6
     lib.kda_gated_norm_proj.restype = ctypes.c_int
     lib.kda_gated_norm_proj.argtypes = [P] * 6 + [i64, i32, i32, i32, f32, i32, P, ctypes.c_size_t, P]
     lib.kda_out_proj.restype = ctypes.c_int
@@ -321,9 +321,12 @@ def chunk_prepare(q: torch.Tensor, k: torch.Tensor, g: torch.Tensor, beta: torch
 def chunk_scan(v: torch.Tensor, workspace: torch.Tensor, initial_state: Optional[torch.Tensor] = None, *,
                cu_seqlens: Optional[torch.Tensor] = None, dk: Optional[int] = None,
                output_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
-               final_state: Optional[torch.Tensor] = None):
+               final_state: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
+               norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
+               y: Optional[torch.Tensor] = None):
     """Second launch of the bf16, d = 128 chunked prefill: the state scan over the records
-    chunk_prepare wrote (same shapes and cu_seqlens).  Returns (o, final_state)."""
+    chunk_prepare wrote (same shapes and cu_seqlens).  Returns (o, final_state), or
+    (o, final_state, y) with the gated norm (gate and norm_weight given)."""
     lib = load_library()
     dev = v.device
     B, T, H, dv = v.shape
@@ -340,11 +343,25 @@ def chunk_scan(v: torch.Tensor, workspace: torch.Tensor, initial_state: Optional
     _dev(o, "out", dev)
     fs = final_state if final_state is not None else torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _dev(fs, "final_state", dev)
+    norm = gate is not None or norm_weight is not None
+    yy = None
+    if norm:
+        if gate is None or norm_weight is None:
+            raise ValueError("gate and norm_weight go together")
+        _dev(gate, "gate", dev)
+        _dev(norm_weight, "norm_weight", dev)
+        if gate.shape != v.shape or gate.dtype != v.dtype:
+            raise ValueError("gate must have v's shape and dtype")
+        if norm_weight.dtype != torch.float32 or norm_weight.shape != (dv,):
+            raise ValueError(f"norm_weight must be float32 [{dv}]")
+        yy = y if y is not None else torch.empty_like(o)
+        _dev(yy, "y", dev)
     p = _params(B, T, H, dk, dv, num_seqs=N if cu_dev is not None else 0, in_dtype=_dtype_code(v.dtype),
-                out_dtype=_dtype_code(o.dtype))
+                out_dtype=_dtype_code(o.dtype), norm_eps=norm_eps)
     _check(lib.kda_chunk_scan(ctypes.byref(p), _ptr(v), _ptr(initial_state), _ptr(cu_dev), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _ptr(o), _ptr(fs), _stream(dev)))
-    return o, fs
+                              workspace.numel() * workspace.element_size(), _ptr(o), _ptr(fs), _ptr(gate),
+                              _ptr(norm_weight), _ptr(yy), _stream(dev)))
+    return (o, fs, yy) if norm else (o, fs)
 
 
 def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

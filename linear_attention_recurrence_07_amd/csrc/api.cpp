@@ -162,7 +162,6 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
   a.init = initial_state; a.state = final_state;
   a.cu = cu_seqlens; a.mask = mask; a.o = o;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool norm = y != nullptr;
   const int chunk = p->chunk;
   const bool mfma = use_mfma_prefill(p);
   if (!mfma) {
@@ -172,10 +171,13 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
       return fail(KDA_ERR_UNSUPPORTED, "chunk 32 needs bf16 inputs with dk = dv = 128 and T * H * 128 < 2^31");
   }
   if (mfma) {
+    // The gated norm runs as its own launch over o: the scan can apply it itself
+    // (kda_chunk_scan with gate and y), but on the scan's 2 work-groups per head that
+    // costs more than a separate pass at full HBM bandwidth on every CU.
     KDA_TRY(check_workspace(p, cu_seqlens, workspace, workspace_bytes));
     KDA_TRY(hip_status(kda::launch_chunk_prep(a, workspace, st), "prefill (chunk preparation)"));
     KDA_TRY(hip_status(kda::launch_chunk_scan(a, workspace, st), "prefill (state scan)"));
-    if (norm) {
+    if (y != nullptr) {
       const int64_t rows = static_cast<int64_t>(p->B) * p->T * p->H;
       KDA_TRY(hip_status(kda::launch_gated_rmsnorm(o, gate, norm_weight, y, rows, p->dv, p->norm_eps,
                                                    a.out_bf16, a.in_bf16, a.out_bf16, st),
@@ -216,19 +218,22 @@ kda_status_t kda_chunk_prepare(const kda_params_t *p, const void *q, const void 
 
 kda_status_t kda_chunk_scan(const kda_params_t *p, const void *v, const float *initial_state,
                             const int32_t *cu_seqlens, const void *workspace, size_t workspace_bytes,
-                            void *o, float *final_state, void *stream) {
+                            void *o, float *final_state, const void *gate, const float *norm_weight,
+                            void *y, void *stream) {
   KDA_TRY(check_params(p, true));
   KDA_TRY(check_ptr(v, "v", true));
   KDA_TRY(check_ptr(o, "o", true));
   KDA_TRY(check_ptr(final_state, "final_state", true));
   KDA_TRY(check_ptr(initial_state, "initial_state", false));
   KDA_TRY(check_layout(p, cu_seqlens, nullptr));
+  KDA_TRY(check_norm(gate, norm_weight, y, p->dv));
   KDA_TRY(check_stage_kernel(p));
   KDA_TRY(check_workspace(p, cu_seqlens, workspace, workspace_bytes));
   kda::Args a = make_args(p);
   a.N = cu_seqlens ? p->num_seqs : p->B;
   a.v = v; a.init = initial_state; a.state = final_state;
   a.cu = cu_seqlens; a.o = o;
+  a.gate = gate; a.norm_w = norm_weight; a.y = y;
   KDA_TRY(hip_status(kda::launch_chunk_scan(a, workspace, static_cast<hipStream_t>(stream)), "state scan"));
   return KDA_OK;
 }

@@ -93,7 +93,8 @@ __global__ void __launch_bounds__(NT)
 chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const float *__restrict__ g, const float *__restrict__ beta,
                   const int32_t *__restrict__ cu, const uint8_t *__restrict__ mask,
-                  Rec *__restrict__ ws, int T, int H, int N, float scale, int use_l2) {
+                  Rec *__restrict__ ws, uint64_t *__restrict__ xs, int T, int H, int N, float scale,
+                  int use_l2) {
   __shared__ Shared sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int m = __builtin_amdgcn_readfirstlane(tid >> 6);   // sub-block of this wave
@@ -125,6 +126,8 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
   if (c < 0 || c * C >= t_end - t_begin) return;   // no chunk in this slot (whole work-group)
   const int c0 = t_begin + c * C;
   Rec *rec = ws + static_cast<size_t>(slot) * H + h;
+  // clear the chunk's words of the scan's norm exchange (2 tiles x 32 tokens)
+  if (tid < 32) reinterpret_cast<u32x4 *>(xs + (static_cast<size_t>(slot) * H + h) * 64)[tid] = u32x4{0u, 0u, 0u, 0u};
   const size_t row0 = static_cast<size_t>(b) * T;
 
   // ---------------------------------------------------------------- load (operand order)
@@ -393,9 +396,15 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
 
 }  // namespace
 
-// Workspace records for the bf16 chunked prefill: one per (slot, head).
+// Workspace of the bf16 chunked prefill: one record per (slot, head), then the scan's
+// norm-exchange words, 64 per (slot, head).
 size_t chunk_prep_workspace_bytes(long long B, long long T, long long H, long long N, bool packed) {
-  return static_cast<size_t>(num_slots(B, T, N, packed) * H) * kRecBytes;
+  return static_cast<size_t>(num_slots(B, T, N, packed) * H) * (kRecBytes + kExchangeBytes);
+}
+
+uint64_t *chunk_exchange_words(const void *ws, long long B, long long T, long long H, long long N, bool packed) {
+  const size_t rec_bytes = static_cast<size_t>(num_slots(B, T, N, packed) * H) * kRecBytes;
+  return reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(const_cast<void *>(ws)) + rec_bytes);
 }
 
 hipError_t launch_chunk_prep(const Args &a, void *ws, hipStream_t st) {
@@ -405,21 +414,22 @@ hipError_t launch_chunk_prep(const Args &a, void *ws, hipStream_t st) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k);
   Rec *rec = static_cast<Rec *>(ws);
+  uint64_t *xs = chunk_exchange_words(ws, a.B, a.T, a.H, a.N, a.cu != nullptr);
   const dim3 grid(static_cast<unsigned>(blocks));
   if (a.g_head) {
     if (a.mask)
       hipLaunchKernelGGL((chunk_prep_kernel<true, true>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                         rec, a.T, a.H, a.N, a.scale, a.use_l2);
+                         rec, xs, a.T, a.H, a.N, a.scale, a.use_l2);
     else
       hipLaunchKernelGGL((chunk_prep_kernel<false, true>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                         rec, a.T, a.H, a.N, a.scale, a.use_l2);
+                         rec, xs, a.T, a.H, a.N, a.scale, a.use_l2);
   } else {
     if (a.mask)
       hipLaunchKernelGGL((chunk_prep_kernel<true, false>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                         rec, a.T, a.H, a.N, a.scale, a.use_l2);
+                         rec, xs, a.T, a.H, a.N, a.scale, a.use_l2);
     else
       hipLaunchKernelGGL((chunk_prep_kernel<false, false>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                         rec, a.T, a.H, a.N, a.scale, a.use_l2);
+                         rec, xs, a.T, a.H, a.N, a.scale, a.use_l2);
   }
   return hipGetLastError();
 }

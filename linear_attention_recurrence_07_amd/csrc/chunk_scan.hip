@@ -24,6 +24,23 @@
 // One work-group barrier per step.  The two tiles of a head get work-group ids 8 apart,
 // so they land on the same XCD and share its L2 for the record reads.
 //
+// Gated norm epilogue (nnterp Kimi-Linear page and Kimi-K3 atlas, gate-project page:
+// y = w * o / sqrt(mean(o^2) + eps) * sigmoid(gate) over the 128 channels of a head).
+// The mean needs both 64-column tiles of a head, which live in two work-groups.  When a
+// helper writes chunk c's output rows (step c+1) it also publishes, per token, the sum of
+// squares of its 64 columns as one 64-bit word (a flag in the high half, the float in
+// the low half) in the workspace.  Compute wave 0 reads the partner tile's words for
+// chunk c: it issues the device-coherent read (which bypasses the XCD's L2 and takes
+// about a step) at step c+3, two steps after the partner published them, and at step
+// c+4 passes the sums to the helpers through LDS; the helpers write y of chunk c at step
+// c+5.  The compute waves issue no other global loads, so waiting for that read never
+// waits for the helpers' prefetches.  The tiles therefore do not wait on each other in
+// lockstep; the output tiles of the last six chunks stay in LDS.  A wait is bounded, and
+// a word that never arrives gives a NaN output instead of a hang.  The reader clears each
+// word after use, and the preparation kernel clears them all, so no call sees another
+// call's words.  The two tiles of a head are consecutive work-groups of one XCD's
+// dispatch order, so a tile never waits for a partner that cannot start.
+//
 // Precision: fp16 operands for the state, the decayed keys/queries and V - K S0; W and U
 // as fp16 hi + lo parts; fp32 accumulation.  The fp16 state operand limits |S| to well
 // inside fp16 range.
@@ -43,6 +60,13 @@ constexpr int NHT = NT - NCW * 64;  // helper threads (256)
 constexpr int LDV = DVT + 8;      // value tile row stride (bf16)
 constexpr int LDO = DVT + 4;      // fp32 output tile row stride
 constexpr int REC_PIECES = static_cast<int>(sizeof(Rec) / 16);
+constexpr int kSpinLimit = 1 << 18;   // polls of a partner's word before giving up (~0.3 s)
+
+// x of another lane of the same row, chosen by a DPP control code.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 constexpr int PPT = (REC_PIECES + NHT - 1) / NHT;   // record pieces per helper thread (8)
 static_assert(NCW == 4 && NHT == 256, "thread mappings");
 
@@ -50,18 +74,26 @@ struct alignas(16) Hand {
   Rec rec;
   uint16_t vt[C * LDV];        // bf16 value tile [token][column]
 };
+template <int NOST>
 struct alignas(16) Smem {
   Hand hand[2];
-  float ost[2][C * LDO];       // fp32 output tiles
+  float ost[NOST][C * LDO];    // fp32 output tiles: chunk c in ost[c % NOST]
+  float pss[2][C];             // NORM: the partner tile's sums of squares, chunk c in pss[c & 1]
 };
-static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+constexpr int kNormLag = 5;          // y of chunk c is written at step c + kNormLag
+static_assert(sizeof(Smem<kNormLag + 1>) <= 160 * 1024, "LDS budget");
 static_assert(sizeof(Hand) % 16 == 0 && (LDV * 2) % 16 == 0 && (LDO * 4) % 16 == 0, "16-byte LDS access");
 
-template <typename TOut, bool HAS_INIT>
+// NORM: also write y (gated norm over the head's 128 channels); xs holds the exchanged
+// partial sums of squares, 2 tiles x 32 tokens per (slot, head).
+template <typename TOut, bool HAS_INIT, bool NORM>
 __global__ void __launch_bounds__(NT, 1)
 chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, const float *init,
-                  float *fin, const int32_t *__restrict__ cu, TOut *__restrict__ o, int T, int H, int units) {
-  __shared__ Smem sm;
+                  float *fin, const int32_t *__restrict__ cu, TOut *__restrict__ o,
+                  const uint16_t *__restrict__ gate, const float *__restrict__ norm_w, TOut *__restrict__ y,
+                  uint64_t *xs, float eps, int T, int H, int units) {
+  constexpr int NOST = NORM ? kNormLag + 1 : 2;
+  __shared__ Smem<NOST> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: branches stay scalar
   const int l16 = lane & 15, lg = lane >> 4;
@@ -108,6 +140,7 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     u32x4 v;
     uint32_t valid;            // the chunk's token flags
   };
+  const uint8_t *grow = reinterpret_cast<const uint8_t *>(gate + row0 * tok_stride);
   uint32_t vzero;              // 0 in a vector register: keeps the flag load a per-lane load
   __asm__ volatile("v_mov_b32 %0, 0" : "=v"(vzero));
   auto load = [&](Pre &pre, int cidx) {
@@ -133,22 +166,101 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     *reinterpret_cast<u32x4 *>(hd.vt + hr * LDV + hc8) = keep ? pre.v : u32x4{0u, 0u, 0u, 0u};
   };
   // Token ht/8 of chunk cidx, columns (ht%8)*8..+7 of the tile.
-  auto emit = [&](int cidx, const float *ost) {
+  auto store_row = [&](TOut *dst, int t, float4 x0, float4 x1) {
+    const size_t off = row0 * tok_stride + (piece + static_cast<uint32_t>(t) * tok_bytes) / 2u;
+    if constexpr (sizeof(TOut) == 2) {
+      uint4 w;
+      w.x = pack_bf16x2(x0.x, x0.y); w.y = pack_bf16x2(x0.z, x0.w);
+      w.z = pack_bf16x2(x1.x, x1.y); w.w = pack_bf16x2(x1.z, x1.w);
+      *reinterpret_cast<uint4 *>(dst + off) = w;
+    } else {
+      reinterpret_cast<float4 *>(dst + off)[0] = x0;
+      reinterpret_cast<float4 *>(dst + off)[1] = x1;
+    }
+  };
+  // Writes the output rows of chunk cidx; returns the token's sum of squares over the
+  // tile's 64 columns (NORM), the same in the 8 lanes of the token.
+  auto emit = [&](int cidx, const float *ost) -> float {
     const int t = t_begin + cidx * C + hr;
     const float4 x0 = *reinterpret_cast<const float4 *>(ost + hr * LDO + hc8);
     const float4 x1 = *reinterpret_cast<const float4 *>(ost + hr * LDO + hc8 + 4);
-    if (t < t_end) {
-      const size_t off = row0 * tok_stride + (piece + static_cast<uint32_t>(t) * tok_bytes) / 2u;
-      if constexpr (sizeof(TOut) == 2) {
-        uint4 w;
-        w.x = pack_bf16x2(x0.x, x0.y); w.y = pack_bf16x2(x0.z, x0.w);
-        w.z = pack_bf16x2(x1.x, x1.y); w.w = pack_bf16x2(x1.z, x1.w);
-        *reinterpret_cast<uint4 *>(o + off) = w;
-      } else {
-        reinterpret_cast<float4 *>(o + off)[0] = x0;
-        reinterpret_cast<float4 *>(o + off)[1] = x1;
-      }
+    if (t < t_end) store_row(o, t, x0, x1);
+    if constexpr (NORM) {
+      float ss = x0.x * x0.x + x0.y * x0.y + x0.z * x0.z + x0.w * x0.w;
+      ss += x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w;
+      // over the 8 lanes of the token: quad swaps, then lane i + lane 7-i of each 8
+      ss += dpp_f32<0xB1>(ss);                 // quad_perm [1, 0, 3, 2]
+      ss += dpp_f32<0x4E>(ss);                 // quad_perm [2, 3, 0, 1]
+      ss += dpp_f32<0x141>(ss);                // row_half_mirror
+      return ss;
     }
+    return 0.f;
+  };
+
+  // ================================================================ gated norm (helpers)
+  // Exchange word of (chunk, tile, token).
+  auto xword = [&](int cidx, int tl, int tok) {
+    return xs + ((static_cast<size_t>(slot0 + cidx) * H + h) * NTILE + tl) * C + tok;
+  };
+  auto publish = [&](int cidx, float ss) {
+    if ((ht & 7) == 0)
+      __hip_atomic_store(xword(cidx, tile, hr), (uint64_t{1} << 32) | __float_as_uint(ss), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto fetch = [&](int cidx, int tok) -> uint64_t {
+    return __hip_atomic_load(xword(cidx, tile ^ 1, tok), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // The partner's sum for (chunk, token), given a first read of its word; the caller
+  // clears the word.  After one wait has run out, the later ones give up at once.
+  bool lost = false;
+  auto partner = [&](int cidx, int tok, uint64_t w) -> float {
+    for (int n = 0; (w >> 32) != 1u; ++n) {
+      if (lost || n == kSpinLimit) {
+        lost = true;
+        return __builtin_nanf("");
+      }
+      __builtin_amdgcn_s_sleep(2);
+      w = fetch(cidx, tok);
+    }
+    return __uint_as_float(static_cast<uint32_t>(w));
+  };
+  auto clear = [&](int cidx, int tok) {
+    __hip_atomic_store(xword(cidx, tile ^ 1, tok), uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // gate piece of token hr of chunk cidx and the chunk's token flags
+  auto load_gate = [&](int cidx, u32x4 &gt, uint32_t &valid) {
+    const uint32_t tv = static_cast<uint32_t>(min(t_begin + cidx * C + hr, t_end - 1));
+    gt = *reinterpret_cast<const u32x4 *>(grow + (piece + tv * tok_bytes));
+    valid = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(rp0 + static_cast<size_t>(cidx) * H) +
+                                                offsetof(Rec, valid) + vzero);
+  };
+  float wn[8];                 // norm weights of this thread's 8 columns
+  if constexpr (NORM) {
+    if (helper) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wn[i] = norm_w[col0 + hc8 + i];
+    }
+  }
+  // y of token hr of chunk cidx from its output rows, the two tiles' sums of squares,
+  // the gate piece and the chunk's token flags (padding gives 0).
+  auto emit_y = [&](int cidx, const float *ost, float ss, u32x4 gt, uint32_t valid) {
+    const int t = t_begin + cidx * C + hr;
+    if (t >= t_end) return;
+    const float rn = rsqrtf(ss * (1.f / DV) + eps);
+    const bool keep = (valid >> hr) & 1u;
+    float xv[8];
+    *reinterpret_cast<float4 *>(xv) = *reinterpret_cast<const float4 *>(ost + hr * LDO + hc8);
+    *reinterpret_cast<float4 *>(xv + 4) = *reinterpret_cast<const float4 *>(ost + hr * LDO + hc8 + 4);
+    float yv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t gw = gt[i >> 1];
+      const float gv = (i & 1) ? hi_bf16(gw) : lo_bf16(gw);
+      // sigmoid from the hardware exp2 and reciprocal (each about 1 ulp)
+      const float sg = __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * gv));
+      yv[i] = keep ? wn[i] * (xv[i] * rn) * sg : 0.f;
+    }
+    store_row(y, t, make_float4(yv[0], yv[1], yv[2], yv[3]), make_float4(yv[4], yv[5], yv[6], yv[7]));
   };
 
   // ================================================================ compute side
@@ -268,24 +380,79 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
       load(pre1, min(1, last));
       stage(sm.hand[0], pre0);
       load(pre0, min(2, last));
+      // NORM: the gate pieces and flags of chunk s-5 in the set of step s's parity
+      // (loaded at step s-2); at the start of step s, this tile's sums of squares of
+      // chunks s-5 .. s-2
+      u32x4 gA{}, gB{};
+      uint32_t fA = 0, fB = 0;
+      float ssr[kNormLag - 1] = {};
       sync_lds();
-      auto hstep = [&](int s, Pre &from) {
+      auto hstep = [&](int s, Pre &from, u32x4 &gs, uint32_t &fs) {
         stage(sm.hand[(s + 1) & 1], from);
         load(from, min(s + 3, last));
-        if (s >= 1) emit(s - 1, sm.ost[(s + 1) & 1]);
+        float ss = 0.f;
+        if (s >= 1) {
+          ss = emit(s - 1, sm.ost[(s - 1) % NOST]);
+          if constexpr (NORM) publish(s - 1, ss);
+        }
+        if constexpr (NORM) {
+          if (s >= kNormLag) {
+            const int c = s - kNormLag;
+            emit_y(c, sm.ost[c % NOST], ssr[0] + sm.pss[c & 1][hr], gs, fs);
+          }
+          load_gate(max(s - (kNormLag - 2), 0), gs, fs);   // unconditional: the load is waited for by count
+#pragma unroll
+          for (int i = 0; i < kNormLag - 2; ++i) ssr[i] = ssr[i + 1];
+          ssr[kNormLag - 2] = ss;
+        }
         sync_lds();
       };
       int s = 0;
       for (; s + 1 < nchunks; s += 2) {
-        hstep(s, pre1);                          // chunk s+1 is in pre1, s+2 in pre0
-        hstep(s + 1, pre0);
+        hstep(s, pre1, gA, fA);                  // chunk s+1 is in pre1, s+2 in pre0
+        hstep(s + 1, pre0, gB, fB);
       }
-      if (s < nchunks) hstep(s, pre1);
-      emit(last, sm.ost[last & 1]);
+      if (s < nchunks) hstep(s, pre1, gA, fA);
+      const float ssl = emit(last, sm.ost[last % NOST]);
+      if constexpr (NORM) {
+        // y of chunks last-4 .. last.  The partner's sums of chunk last-4 are in LDS
+        // (compute wave 0 read them at the last step); the later ones are read here.
+        publish(last, ssl);
+#pragma unroll
+        for (int i = 0; i < kNormLag; ++i) {
+          const int c = last - (kNormLag - 1) + i;
+          if (c < 0) continue;
+          const float own = (i < kNormLag - 1) ? ssr[i] : ssl;
+          float other;
+          if (i == 0) {
+            other = sm.pss[c & 1][hr];
+          } else {
+            other = partner(c, hr, fetch(c, hr));
+            if ((ht & 7) == 0) clear(c, hr);
+          }
+          u32x4 gt;
+          uint32_t fl;
+          load_gate(c, gt, fl);
+          emit_y(c, sm.ost[c % NOST], own + other, gt, fl);
+        }
+      }
     } else {
       sync_lds();
+      int oi = 0;
+      uint64_t xw = 0;                           // NORM, wave 0: the partner's word of chunk s-4
       for (int s = 0; s < nchunks; ++s) {
-        products(sm.hand[s & 1], sm.ost[s & 1]);
+        if constexpr (NORM) {
+          if (wave == 0 && lane < C) {
+            if (s >= kNormLag - 1) {
+              const int c = s - (kNormLag - 1);
+              sm.pss[c & 1][lane] = partner(c, lane, xw);
+              clear(c, lane);
+            }
+            if (s >= kNormLag - 2) xw = fetch(s - (kNormLag - 2), lane);
+          }
+        }
+        products(sm.hand[s & 1], sm.ost[oi]);
+        oi = (oi + 1 == NOST) ? 0 : oi + 1;
         sync_lds();
       }
     }
@@ -299,19 +466,25 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
   }
 }
 
-template <typename TOut, bool HAS_INIT>
-hipError_t launch2(const Args &a, const void *ws, hipStream_t st) {
+template <typename TOut, bool HAS_INIT, bool NORM>
+hipError_t launch3(const Args &a, const void *ws, uint64_t *xs, hipStream_t st) {
   const int units = a.N * a.H;
   const unsigned grid = static_cast<unsigned>((units + 7) / 8) * 8 * NTILE;
-  hipLaunchKernelGGL((chunk_scan_kernel<TOut, HAS_INIT>), dim3(grid), dim3(NT), 0, st,
+  hipLaunchKernelGGL((chunk_scan_kernel<TOut, HAS_INIT, NORM>), dim3(grid), dim3(NT), 0, st,
                      static_cast<const uint16_t *>(a.v), static_cast<const Rec *>(ws), a.init, a.state, a.cu,
-                     static_cast<TOut *>(a.o), a.T, a.H, units);
+                     static_cast<TOut *>(a.o), static_cast<const uint16_t *>(a.gate), a.norm_w,
+                     static_cast<TOut *>(a.y), xs, a.eps, a.T, a.H, units);
   return hipGetLastError();
 }
 
+template <typename TOut, bool HAS_INIT>
+hipError_t launch2(const Args &a, const void *ws, uint64_t *xs, hipStream_t st) {
+  return a.y ? launch3<TOut, HAS_INIT, true>(a, ws, xs, st) : launch3<TOut, HAS_INIT, false>(a, ws, xs, st);
+}
+
 template <typename TOut>
-hipError_t launch1(const Args &a, const void *ws, hipStream_t st) {
-  return a.init ? launch2<TOut, true>(a, ws, st) : launch2<TOut, false>(a, ws, st);
+hipError_t launch1(const Args &a, const void *ws, uint64_t *xs, hipStream_t st) {
+  return a.init ? launch2<TOut, true>(a, ws, xs, st) : launch2<TOut, false>(a, ws, xs, st);
 }
 
 }  // namespace
@@ -323,7 +496,8 @@ bool prefill_mfma_fits(long long T, long long H) { return T * H * DK < (1LL << 3
 
 hipError_t launch_chunk_scan(const Args &a, const void *ws, hipStream_t st) {
   if (a.N * static_cast<long long>(a.H) <= 0) return hipSuccess;
-  return a.out_bf16 ? launch1<uint16_t>(a, ws, st) : launch1<float>(a, ws, st);
+  uint64_t *xs = chunk_exchange_words(ws, a.B, a.T, a.H, a.N, a.cu != nullptr);
+  return a.out_bf16 ? launch1<uint16_t>(a, ws, xs, st) : launch1<float>(a, ws, xs, st);
 }
 
 }  // namespace kda

@@ -51,6 +51,9 @@ struct alignas(16) Rec {
 };
 static_assert(sizeof(Rec) == 30224, "record layout");
 constexpr size_t kRecBytes = sizeof(Rec);
+// Per (slot, head): the scan's gated-norm exchange, 2 tiles x 32 tokens of 64-bit words,
+// stored after all records.
+constexpr size_t kExchangeBytes = 2 * 32 * 8;
 // K index (0..31) of slot e (0..7) of lane group lg, and the inverse.
 __host__ __device__ constexpr int kidx(int lg, int e) { return (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4); }
 __host__ __device__ constexpr int kidx_lg(int x) { return (x & 15) >> 2; }

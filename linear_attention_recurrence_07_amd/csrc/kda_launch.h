@@ -52,7 +52,9 @@ hipError_t launch_prefill_valu(const Args &a, hipStream_t s);
 // bf16 chunked prefill, d = 128: the per-chunk preparation (writes one record per
 // (slot, head) into ws), then the state scan that reads them.
 size_t chunk_prep_workspace_bytes(long long B, long long T, long long H, long long N, bool packed);
+uint64_t *chunk_exchange_words(const void *ws, long long B, long long T, long long H, long long N, bool packed);
 hipError_t launch_chunk_prep(const Args &a, void *ws, hipStream_t s);
+// With a.y set the scan also applies the gated norm (a.gate, a.norm_w, a.eps).
 hipError_t launch_chunk_scan(const Args &a, const void *ws, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const void *x, const void *gate, const float *w, void *y,
                                 int64_t rows, int width, float eps, int x_bf16, int gate_bf16,

@@ -106,7 +106,7 @@ def test_prefill_validation_codes():
 def test_prefill_workspace_size_and_checks():
     lib = K.load_library()
     size = lambda p, packed=0: lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), packed)
-    rec = 30224                                            # bytes per (chunk, head)
+    rec = 30224 + 512                                      # bytes per (chunk, head): record + norm exchange
     assert size(_p(B=1, T=64, H=2)) == 1 * 2 * 2 * rec      # B * ceil(T/32) * H records
     assert size(_p(B=3, T=65, H=2)) == 3 * 3 * 2 * rec
     assert size(_p(B=1, T=64, H=2, num_seqs=3), 1) == (3 + 2) * 2 * rec   # (N + ceil(T/32)) * H
@@ -133,10 +133,10 @@ def test_stage_validation_codes():
                                      *[d[n] for n in ("q", "k", "g", "beta", "cu", "mask")], ws, nbytes, None)
 
     def scan(p, ws=A, nbytes=need, **ptrs):
-        d = dict(v=A, init=None, cu=None, o=A, fs=A)
+        d = dict(v=A, init=None, cu=None, o=A, fs=A, gate=None, w=None, y=None)
         d.update(ptrs)
         return lib.kda_chunk_scan(None if p is None else ctypes.byref(p), d["v"], d["init"], d["cu"],
-                                  ws, nbytes, d["o"], d["fs"], None)
+                                  ws, nbytes, d["o"], d["fs"], d["gate"], d["w"], d["y"], None)
 
     for f in (prep, scan):
         assert f(None) == 1
@@ -154,6 +154,9 @@ def test_stage_validation_codes():
     assert scan(_p(), v=None) == 1
     assert scan(_p(), fs=None) == 1
     assert scan(_p(), init=MIS) == 4
+    assert scan(_p(), y=A) == 5                             # gate, norm_weight, y: all or none
+    assert scan(_p(), gate=A, w=A) == 5
+    assert scan(_p(), gate=A, w=A, y=MIS) == 4
 
 
 def test_recurrent_and_norm_validation_codes():

@@ -247,6 +247,50 @@ def test_two_stage_prefill_equals_one_call():
         U.assert_close(f"two-stage {name} state", U.to_numpy64(f2), rfs, U.BF16_TOL)
 
 
+def test_scan_with_fused_norm():
+    """kda_chunk_scan applying the gated norm itself (the two tiles of a head exchange
+    per-token sums of squares): o and state identical to chunk_prefill's, y within 1e-5
+    (of rms) of chunk_prefill's separate norm over the same fp32 o and within tolerance of
+    the oracle; a second scan over the same prepared workspace repeats y exactly (the
+    exchange words are cleared after use); bf16 outputs are the exact rounding of the
+    fp32 ones; padding gives y = 0 even where its gate is NaN."""
+    import linear_attention_recurrence_07_amd as kda
+    x = gi.varlen_packed((100, 0, 37, 64, 129, 1, 33), H=3, d=128)
+    cases = [("packed", x), ("left-padded", gi.padded_from_packed(x, left=True)),
+             ("plain+init", gi.make_inputs("stages_norm", B=2, T=77, H=2, dk=128, dv=128, in_dtype=gi.BF16,
+                                           seed=31, initial_state_std=0.02, norm=True))]
+    f32 = torch.float32
+    for name, c in cases:
+        U.log(f"scan with fused norm {name}")
+        d = U.device_inputs(c, DEV)
+        vm = U.valid_token_mask(c)
+        m = torch.from_numpy(vm).to(DEV)
+        o1, f1, y1 = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                                       cu_seqlens=d["cu_seqlens"], attention_mask=d["mask"], gate=d["gate"],
+                                       norm_weight=d["norm_weight"], norm_eps=c.norm_eps, output_dtype=f32)
+        if d["mask"] is not None:
+            d["gate"][~m] = float("nan")
+        ws = kda.chunk_prepare(d["q"], d["k"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                               attention_mask=d["mask"])
+        kw = dict(cu_seqlens=d["cu_seqlens"], gate=d["gate"], norm_weight=d["norm_weight"], norm_eps=c.norm_eps)
+        outs = [kda.chunk_scan(d["v"], ws, d["initial_state"], output_dtype=f32, **kw) for _ in range(2)]
+        ob, fb, yb = kda.chunk_scan(d["v"], ws, d["initial_state"], **kw)
+        torch.cuda.synchronize()
+        o2, f2, y2 = outs[0]
+        for o3, f3, y3 in outs:
+            assert torch.equal(o1[m], o3[m]), name
+            assert torch.equal(f1, f3), name
+            assert torch.equal(y2[m], y3[m]), name
+        assert torch.equal(ob[m], o2[m].to(torch.bfloat16)), name
+        assert torch.equal(yb[m], y2[m].to(torch.bfloat16)), name
+        assert torch.equal(fb, f2), name
+        if d["mask"] is not None:
+            assert torch.all(y2[~m] == 0) and torch.all(yb[~m] == 0), name
+        U.assert_close(f"fused norm {name} y vs separate norm", U.to_numpy64(y2)[vm], U.to_numpy64(y1)[vm], 1e-5)
+        _, _, ry = U.oracle(c)
+        U.assert_close(f"fused norm {name} y", U.to_numpy64(y2)[vm], ry[vm], U.BF16_TOL)
+
+
 @pytest.mark.parametrize("case", ["mfma_init_norm", "mfma_packed", "mfma_masked", "valu_f32", "valu_bf16_chunk16"])
 def test_per_head_decay(case):
     """One decay per (token, head) (g [B,T,H], the gated DeltaNet's scalar decay) through
