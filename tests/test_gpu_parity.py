@@ -291,6 +291,35 @@ def test_scan_with_fused_norm():
         U.assert_close(f"fused norm {name} y", U.to_numpy64(y2)[vm], ry[vm], U.BF16_TOL)
 
 
+def test_scan_with_fused_norm_more_work_groups_than_cus():
+    """The fused-norm scan when its work-groups (2 per sequence and head) outnumber the
+    CUs: 5 packed sequences (one empty) x 48 heads = 480 work-groups, dispatched in two
+    rounds, so some tiles start only after others finish.  o and state identical to
+    chunk_prefill's, y within 1e-5 of its separate norm, and within tolerance of the
+    oracle on sampled heads."""
+    import linear_attention_recurrence_07_amd as kda
+    c = gi.varlen_packed((300, 0, 129, 64, 1), H=48, d=128)
+    U.log("scan with fused norm: 480 work-groups")
+    d = U.device_inputs(c, DEV)
+    vm = U.valid_token_mask(c)
+    m = torch.from_numpy(vm).to(DEV)
+    f32 = torch.float32
+    o1, f1, y1 = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                                   cu_seqlens=d["cu_seqlens"], gate=d["gate"], norm_weight=d["norm_weight"],
+                                   norm_eps=c.norm_eps, output_dtype=f32)
+    ws = kda.chunk_prepare(d["q"], d["k"], d["g"], d["beta"], cu_seqlens=d["cu_seqlens"])
+    o2, f2, y2 = kda.chunk_scan(d["v"], ws, d["initial_state"], cu_seqlens=d["cu_seqlens"], gate=d["gate"],
+                                norm_weight=d["norm_weight"], norm_eps=c.norm_eps, output_dtype=f32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[m], o2[m])
+    assert torch.equal(f1, f2)
+    U.assert_close("fused norm 480 WGs y vs separate norm", U.to_numpy64(y2)[vm], U.to_numpy64(y1)[vm], 1e-5)
+    heads = [0, 17, 47]
+    _, _, ry = U.oracle(c, heads=heads)
+    got = U.to_numpy64(y2)[:, :, heads]
+    U.assert_close("fused norm 480 WGs y (sampled heads)", got[vm], ry[vm], U.BF16_TOL)
+
+
 @pytest.mark.parametrize("case", ["mfma_init_norm", "mfma_packed", "mfma_masked", "valu_f32", "valu_bf16_chunk16"])
 def test_per_head_decay(case):
     """One decay per (token, head) (g [B,T,H], the gated DeltaNet's scalar decay) through
