@@ -87,6 +87,32 @@ __device__ __forceinline__ float lane_sum(float x) {
   return x;
 }
 
+// Sums over lanes without LDS round trips, by DPP moves within 16-lane rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Sum over the N consecutive lanes of each aligned group (N = 2, 4, 8 or 16), in every
+// lane of the group: quad swaps, then the half-row mirror (exact once the quads hold
+// their sums), then a rotate by 8 within the row.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "group of 2, 4, 8 or 16 lanes");
+  x += dpp_move<0xB1>(x);                              // quad_perm [1, 0, 3, 2]
+  if constexpr (N >= 4) x += dpp_move<0x4E>(x);        // quad_perm [2, 3, 0, 1]
+  if constexpr (N >= 8) x += dpp_move<0x141>(x);       // row_half_mirror
+  if constexpr (N >= 16) x += dpp_move<0x128>(x);      // row_ror:8
+  return x;
+}
+// Sum over the 64 lanes of the wave (all active), wave-uniform.
+__device__ __forceinline__ float wave_sum(float x) {
+  const int r = __builtin_bit_cast(int, group_sum<16>(x));
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 48)));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 

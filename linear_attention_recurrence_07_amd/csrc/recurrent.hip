@@ -9,46 +9,59 @@
 //     o  = S^T q = S'^T q + u (k . q)        one pass: both reductions read S'
 // with k, q L2-normalised and q scaled by 1/sqrt(dk).
 //
-// Layout: one work-group per (batch row, head) slab.  Thread (cg, rg) owns the four
-// value columns 4cg..4cg+3 of key rows rg, rg+RG, rg+2RG, ... so a wave's float4 loads
-// cover whole 512-byte state rows (coalesced) and the slab lives in registers.  The two
-// column reductions (S'^T k, S'^T q) run over lanes with cross-lane adds, then over
-// waves through LDS.  This kernel is HBM-bound: at B=64, H=96, d=128 it moves 805 MB
-// of state per step and does 0.86 flop per byte.
+// Layout: one work-group per (batch row, head) slab, or with few slabs per DVW-column
+// tile of one (value columns are independent in the recurrence: each column's update
+// needs only k, q and its own column).  Thread (cg, rg) owns the four value columns
+// 4cg..4cg+3 of the tile, key rows rg, rg+RG, rg+2RG, ... so a wave's float4 loads cover
+// whole state row pieces (coalesced) and the slab lives in registers.  The two column
+// reductions (S'^T k, S'^T q) run over lanes with cross-lane adds, then over waves
+// through LDS.  The next token's inputs are loaded while the current one is processed.
+// This kernel is HBM-bound: at B=64, H=96, d=128 it moves 805 MB of state per step and
+// does 0.86 flop per byte.
 //
 // With `states` set it also stores the state after every token ([B, T, H, dk, dv]; a
 // padding token stores the carried state): the per-token states that the pages read by
 // running a prompt through the token-by-token kernel (nnterp Kimi-Linear page, support()
 // table, the 'states' row, and Notes, "Loading").
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 namespace {
 
-template <int D, int RPT, typename TIn, typename TOut, bool NORM>
-__global__ void __launch_bounds__((D / RPT) * (D / 4))
+// DVW: value columns per work-group (D: whole slab; the fused norm needs whole rows).
+// STATES: also store the state after every token into `states`.
+template <int D, int DVW, int RPT, typename TIn, typename TOut, bool NORM, bool STATES>
+__global__ void __launch_bounds__((D / RPT) * (DVW / 4))
 recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
                  const float *__restrict__ g, const float *__restrict__ beta,
                  float *__restrict__ state, const uint8_t *__restrict__ mask,
                  TOut *__restrict__ o, const TIn *__restrict__ gate,
                  const float *__restrict__ norm_w, TOut *__restrict__ y,
                  int T, int H, float scale, int use_l2, float eps, int g_head, float *__restrict__ states) {
-  constexpr int CG = D / 4;          // column groups (float4 each)
+  constexpr int CG = DVW / 4;        // column groups (float4 each)
   constexpr int RG = D / RPT;        // row groups
   constexpr int NT = RG * CG;
   constexpr int NW = NT / 64;
-  static_assert(NT % 64 == 0 && 64 % CG == 0, "thread layout");
-  constexpr int RED_MASK = 63 & ~(CG - 1);   // lanes sharing a column group within a wave
+  constexpr int NTILE = D / DVW;     // work-groups per slab
+  static_assert(NT % 64 == 0 && 64 % CG == 0 && D % DVW == 0, "thread layout");
+  static_assert(!NORM || DVW == D, "the fused norm needs whole rows");
+  constexpr int RL = 64 / CG;        // consecutive lanes of a wave sharing a column group
+  constexpr int EPL = (D + 63) / 64;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cg = tid % CG, rg = tid / CG;
-  const int slab = blockIdx.x;
+  // Lane l of wave w: column group l / RL, row group w * RL + l % RL, so a column's
+  // partial sums over a wave's rows meet in RL consecutive lanes (DPP reach).
+  const int cg = lane / RL, rg = wave * RL + lane % RL;
+  const int slab = blockIdx.x / NTILE;
+  const int col0 = (blockIdx.x % NTILE) * DVW;
   const int b = slab / H, h = slab % H;
-  float *S = state + static_cast<size_t>(slab) * D * D;
+  float *S = state + static_cast<size_t>(slab) * D * D + col0;
 
   __shared__ float s_k[D], s_q[D], s_e[D];
-  __shared__ float s_red[NW][2][D];
+  __shared__ float s_red[NW][2][DVW];
   __shared__ float s_scal[4];
 
   float4 s[RPT];
@@ -56,10 +69,41 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
   for (int m = 0; m < RPT; ++m)
     s[m] = *reinterpret_cast<const float4 *>(S + static_cast<size_t>(rg + RG * m) * D + 4 * cg);
 
-  for (int t = 0; t < T; ++t) {
+  // Inputs of token t: wave 0 holds k, q, g, beta and the mask flag, every thread its
+  // four columns of v.  Column tiles (few work-groups, each walking its tokens) load them
+  // during token t-1; whole slabs (many work-groups per CU hide the latency, and the
+  // extra registers would cost occupancy) at the start of token t.
+  constexpr bool PF = DVW < D;
+  struct In {
+    float k[EPL], q[EPL], g[EPL], bt;
+    uint32_t mk;
+    float4 v;
+  };
+  auto fetch = [&](int t, In &in) {
     const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
     if (wave == 0) {
-      constexpr int EPL = (D + 63) / 64;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        if (e < D) {
+          in.k[j] = Elem<TIn>::load(k, tok * D + e);
+          in.q[j] = Elem<TIn>::load(q, tok * D + e);
+          in.g[j] = g_head ? g[tok] : g[tok * D + e];
+        }
+      }
+      in.bt = beta[tok];
+      in.mk = mask == nullptr ? 1u : mask[static_cast<size_t>(b) * T + t];
+    }
+    in.v = Elem<TIn>::load4(v, tok * D + col0 + 4 * cg);
+  };
+
+  // One token; `cur` holds its inputs (PF), loaded two tokens earlier, and is refilled
+  // with those of token t+2.
+  auto token = [&](int t, In &cur) {
+    const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
+    float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (PF) vv = cur.v;
+    if (wave == 0) {
       float kk[EPL], qq[EPL], ee[EPL];
       float sk = 0.f, sq = 0.f;
 #pragma unroll
@@ -68,15 +112,21 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
         kk[j] = qq[j] = 0.f;
         ee[j] = 1.f;
         if (e < D) {
-          kk[j] = Elem<TIn>::load(k, tok * D + e);
-          qq[j] = Elem<TIn>::load(q, tok * D + e);
-          ee[j] = fast_exp2((g_head ? g[tok] : g[tok * D + e]) * kLog2e);
+          if constexpr (PF) {
+            kk[j] = cur.k[j];
+            qq[j] = cur.q[j];
+            ee[j] = fast_exp2(cur.g[j] * kLog2e);
+          } else {
+            kk[j] = Elem<TIn>::load(k, tok * D + e);
+            qq[j] = Elem<TIn>::load(q, tok * D + e);
+            ee[j] = fast_exp2((g_head ? g[tok] : g[tok * D + e]) * kLog2e);
+          }
           sk += kk[j] * kk[j];
           sq += qq[j] * qq[j];
         }
       }
-      sk = lane_sum<63>(sk);
-      sq = lane_sum<63>(sq);
+      sk = wave_sum(sk);
+      sq = wave_sum(sq);
       const float kn = use_l2 ? rsqrtf(sk + kL2Eps) : 1.f;
       const float qn = (use_l2 ? rsqrtf(sq + kL2Eps) : 1.f) * scale;
       float kq = 0.f;
@@ -90,13 +140,19 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
           kq += (kk[j] * kn) * (qq[j] * qn);
         }
       }
-      kq = lane_sum<63>(kq);
+      kq = wave_sum(kq);
       if (lane == 0) {
         s_scal[0] = kq;
-        s_scal[1] = beta[tok];
-        s_scal[2] = (mask == nullptr || mask[static_cast<size_t>(b) * T + t] != 0) ? 1.f : 0.f;
+        if constexpr (PF) {
+          s_scal[1] = cur.bt;
+          s_scal[2] = cur.mk != 0 ? 1.f : 0.f;
+        } else {
+          s_scal[1] = beta[tok];
+          s_scal[2] = (mask == nullptr || mask[static_cast<size_t>(b) * T + t] != 0) ? 1.f : 0.f;
+        }
       }
     }
+    if constexpr (PF) fetch(min(t + 2, T - 1), cur);   // (the last token again near the end)
     sync_lds();
     const bool valid = s_scal[2] != 0.f;
     if (valid) {
@@ -109,11 +165,11 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
         r.x += kv * s[m].x; r.y += kv * s[m].y; r.z += kv * s[m].z; r.w += kv * s[m].w;
         p.x += qv * s[m].x; p.y += qv * s[m].y; p.z += qv * s[m].z; p.w += qv * s[m].w;
       }
-      r.x = lane_sum<RED_MASK>(r.x); r.y = lane_sum<RED_MASK>(r.y);
-      r.z = lane_sum<RED_MASK>(r.z); r.w = lane_sum<RED_MASK>(r.w);
-      p.x = lane_sum<RED_MASK>(p.x); p.y = lane_sum<RED_MASK>(p.y);
-      p.z = lane_sum<RED_MASK>(p.z); p.w = lane_sum<RED_MASK>(p.w);
-      if (lane < CG) {
+      r.x = group_sum<RL>(r.x); r.y = group_sum<RL>(r.y);
+      r.z = group_sum<RL>(r.z); r.w = group_sum<RL>(r.w);
+      p.x = group_sum<RL>(p.x); p.y = group_sum<RL>(p.y);
+      p.z = group_sum<RL>(p.z); p.w = group_sum<RL>(p.w);
+      if (lane % RL == 0) {
         *reinterpret_cast<float4 *>(&s_red[wave][0][4 * cg]) = r;
         *reinterpret_cast<float4 *>(&s_red[wave][1][4 * cg]) = p;
       }
@@ -131,7 +187,7 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
         pp.x += p2.x; pp.y += p2.y; pp.z += p2.z; pp.w += p2.w;
       }
       const float bt = s_scal[1], kq = s_scal[0];
-      const float4 vv = Elem<TIn>::load4(v, tok * D + 4 * cg);
+      if constexpr (!PF) vv = Elem<TIn>::load4(v, tok * D + col0 + 4 * cg);
       float4 u;
       u.x = bt * (vv.x - rr.x); u.y = bt * (vv.y - rr.y);
       u.z = bt * (vv.z - rr.z); u.w = bt * (vv.w - rr.w);
@@ -143,29 +199,54 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
         s[m].x += kv * u.x; s[m].y += kv * u.y; s[m].z += kv * u.z; s[m].w += kv * u.w;
       }
     }
-    if (states) {
-      float *St = states + tok * D * D;
+    if constexpr (STATES) {
+      float *St = states + tok * D * D + col0;
 #pragma unroll
       for (int m = 0; m < RPT; ++m)
         *reinterpret_cast<float4 *>(St + static_cast<size_t>(rg + RG * m) * D + 4 * cg) = s[m];
     }
-    if (rg == 0) {   // the first CG threads (wave 0) hold one full output row
-      Elem<TOut>::store4(o, tok * D + 4 * cg, out);
+    if constexpr (PF) {
+      // Every thread holds `out` of its columns; every wave stores the tile's row (the
+      // same values to the same addresses), so each wave issues the same memory
+      // operations every token and the wait for the prefetched inputs counts past the
+      // stores instead of waiting for them.
+      Elem<TOut>::store4(o, tok * D + col0 + 4 * cg, out);   // 0 for a padding token
+    } else if (wave == 0) {
+      // Every lane of wave 0 holds `out` of its column group, each group in RL lanes:
+      // the row's sum of squares is the wave's sum over RL.
+      float rn = 0.f;
       if constexpr (NORM) {
-        float ss = out.x * out.x + out.y * out.y + out.z * out.z + out.w * out.w;
-        ss = lane_sum<CG - 1>(ss);
-        const float rn = rsqrtf(ss / D + eps);
-        const float4 gt = Elem<TIn>::load4(gate, tok * D + 4 * cg);
-        const float4 w = *reinterpret_cast<const float4 *>(norm_w + 4 * cg);
-        float4 yy;
-        yy.x = w.x * out.x * rn * sigmoidf_(gt.x);
-        yy.y = w.y * out.y * rn * sigmoidf_(gt.y);
-        yy.z = w.z * out.z * rn * sigmoidf_(gt.z);
-        yy.w = w.w * out.w * rn * sigmoidf_(gt.w);
-        Elem<TOut>::store4(y, tok * D + 4 * cg, yy);
+        const float ss = wave_sum(out.x * out.x + out.y * out.y + out.z * out.z + out.w * out.w) * (1.f / RL);
+        rn = rsqrtf(ss / D + eps);
+      }
+      if (rg == 0) {   // one lane per column group stores the row
+        Elem<TOut>::store4(o, tok * D + col0 + 4 * cg, out);
+        if constexpr (NORM) {
+          const float4 gt = Elem<TIn>::load4(gate, tok * D + 4 * cg);
+          const float4 w = *reinterpret_cast<const float4 *>(norm_w + 4 * cg);
+          float4 yy;
+          yy.x = w.x * out.x * rn * sigmoidf_(gt.x);
+          yy.y = w.y * out.y * rn * sigmoidf_(gt.y);
+          yy.z = w.z * out.z * rn * sigmoidf_(gt.z);
+          yy.w = w.w * out.w * rn * sigmoidf_(gt.w);
+          Elem<TOut>::store4(y, tok * D + 4 * cg, yy);
+        }
       }
     }
     sync_lds();   // s_k / s_q / s_e / s_red are rewritten by the next token
+  };
+  In inA, inB;
+  if constexpr (PF) {
+    if (T > 0) fetch(0, inA);
+    if (T > 1) fetch(1, inB);
+    int t = 0;
+    for (; t + 1 < T; t += 2) {
+      token(t, inA);
+      token(t + 1, inB);
+    }
+    if (t < T) token(t, inA);
+  } else {
+    for (int t = 0; t < T; ++t) token(t, inA);
   }
 
 #pragma unroll
@@ -173,31 +254,55 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
     *reinterpret_cast<float4 *>(S + static_cast<size_t>(rg + RG * m) * D + 4 * cg) = s[m];
 }
 
-template <int D, int RPT, typename TIn, typename TOut>
+template <int D, int DVW, int RPT, typename TIn, typename TOut>
 hipError_t launch_typed(const Args &a, hipStream_t st) {
-  constexpr int NT = (D / RPT) * (D / 4);
-  const dim3 grid(static_cast<unsigned>(a.B) * a.H), block(NT);
+  constexpr int NT = (D / RPT) * (DVW / 4);
+  const dim3 grid(static_cast<unsigned>(a.B) * a.H * (D / DVW)), block(NT);
   const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k),
             *v = static_cast<const TIn *>(a.v), *gate = static_cast<const TIn *>(a.gate);
   TOut *o = static_cast<TOut *>(a.o), *y = static_cast<TOut *>(a.y);
-  if (a.y)
-    hipLaunchKernelGGL((recurrent_kernel<D, RPT, TIn, TOut, true>), grid, block, 0, st, q, k, v,
-                       a.g, a.beta, a.state, a.mask, o, gate, a.norm_w, y, a.T, a.H, a.scale,
-                       a.use_l2, a.eps, a.g_head, a.states_out);
-  else
-    hipLaunchKernelGGL((recurrent_kernel<D, RPT, TIn, TOut, false>), grid, block, 0, st, q, k, v,
-                       a.g, a.beta, a.state, a.mask, o, gate, a.norm_w, y, a.T, a.H, a.scale,
-                       a.use_l2, a.eps, a.g_head, a.states_out);
-  return hipGetLastError();
+  auto go = [&](auto norm, auto with_states) {
+    hipLaunchKernelGGL((recurrent_kernel<D, DVW, RPT, TIn, TOut, decltype(norm)::value, decltype(with_states)::value>),
+                       grid, block, 0, st, q, k, v, a.g, a.beta, a.state, a.mask, o, gate, a.norm_w, y, a.T, a.H,
+                       a.scale, a.use_l2, a.eps, a.g_head, a.states_out);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  const bool norm = DVW == D && a.y != nullptr;
+  if (a.states_out) {
+    if constexpr (DVW == D) {
+      if (norm) go(T_{}, T_{});
+      else go(F_{}, T_{});
+    } else {
+      go(F_{}, T_{});
+    }
+  } else {
+    if constexpr (DVW == D) {
+      if (norm) go(T_{}, F_{});
+      else go(F_{}, F_{});
+    } else {
+      go(F_{}, F_{});
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || DVW == D || a.y == nullptr) return e;
+  // column tiles: the gated norm over whole rows as its own pass
+  return launch_gated_rmsnorm(a.o, a.gate, a.norm_w, a.y, static_cast<int64_t>(a.B) * a.T * a.H, D, a.eps,
+                              a.out_bf16, a.in_bf16, a.out_bf16, st);
 }
 
-template <int D, int RPT>
+template <int D, int DVW, int RPT>
 hipError_t launch_d(const Args &a, hipStream_t st) {
-  if (a.in_bf16 && a.out_bf16) return launch_typed<D, RPT, uint16_t, uint16_t>(a, st);
-  if (a.in_bf16) return launch_typed<D, RPT, uint16_t, float>(a, st);
-  if (a.out_bf16) return launch_typed<D, RPT, float, uint16_t>(a, st);
-  return launch_typed<D, RPT, float, float>(a, st);
+  if (a.in_bf16 && a.out_bf16) return launch_typed<D, DVW, RPT, uint16_t, uint16_t>(a, st);
+  if (a.in_bf16) return launch_typed<D, DVW, RPT, uint16_t, float>(a, st);
+  if (a.out_bf16) return launch_typed<D, DVW, RPT, float, uint16_t>(a, st);
+  return launch_typed<D, DVW, RPT, float, float>(a, st);
 }
+
+// Slabs below which a d = 128 slab is split into 4 work-groups of 32 columns when the
+// call walks more than one token (a single token is one latency either way, and the
+// split needs a separate norm pass).
+constexpr long long kSplitSlabs = 512;
 
 }  // namespace
 
@@ -207,10 +312,12 @@ bool recurrent_supports(int dk, int dv) {
 
 hipError_t launch_recurrent(const Args &a, hipStream_t st) {
   switch (a.dk) {
-    case 16: return launch_d<16, 1>(a, st);
-    case 32: return launch_d<32, 4>(a, st);
-    case 64: return launch_d<64, 8>(a, st);
-    case 128: return launch_d<128, 16>(a, st);
+    case 16: return launch_d<16, 16, 1>(a, st);
+    case 32: return launch_d<32, 32, 4>(a, st);
+    case 64: return launch_d<64, 64, 8>(a, st);
+    case 128:
+      if (a.T > 1 && static_cast<long long>(a.B) * a.H < kSplitSlabs) return launch_d<128, 32, 4>(a, st);
+      return launch_d<128, 128, 16>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

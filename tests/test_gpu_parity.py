@@ -364,6 +364,33 @@ def test_per_head_decay_decode_steps():
     U.assert_close("per-head g decode state", U.to_numpy64(st), rfs, U.BF16_TOL)
 
 
+@pytest.mark.parametrize("B,T,H,masked", [(2, 41, 3, True), (6, 3, 96, False)])
+def test_multi_token_decode_with_norm(B, T, H, masked):
+    """kda_recurrent_step over several tokens with the gated norm, d = 128.  Few slabs
+    (B * H < 512) take the 32-column tiles with the norm as its own pass; many take whole
+    slabs with the norm fused.  o, y and the final state against the oracle."""
+    import linear_attention_recurrence_07_amd as kda
+    m = None
+    if masked:
+        m = np.ones((B, T), dtype=np.uint8)
+        m[0, :5] = 0                       # left padding
+        m[1, 20:23] = 0                    # a gap inside the row
+    x = gi.make_inputs(f"multi_dec_B{B}_T{T}", B=B, T=T, H=H, dk=128, dv=128, in_dtype=gi.BF16, seed=53 + T,
+                       initial_state_std=0.05, norm=True, mask=m)
+    d = U.device_inputs(x, DEV)
+    U.log(f"multi-token decode B={B} T={T} H={H} masked={masked}")
+    st = d["initial_state"].clone()
+    o, y = kda.recurrent_step(d["q"], d["k"], d["v"], d["g"], d["beta"], st, attention_mask=d["mask"],
+                              gate=d["gate"], norm_weight=d["norm_weight"], norm_eps=x.norm_eps,
+                              output_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rfs, ry = U.oracle(x)
+    vm = U.valid_token_mask(x)
+    U.assert_close(f"multi-token decode B{B} o", U.to_numpy64(o)[vm], ro[vm], U.BF16_TOL)
+    U.assert_close(f"multi-token decode B{B} y", U.to_numpy64(y)[vm], ry[vm], U.BF16_TOL)
+    U.assert_close(f"multi-token decode B{B} state", U.to_numpy64(st), rfs, U.BF16_TOL)
+
+
 @pytest.mark.parametrize("case", ["bf16_mask", "f32_tiny", "bf16_per_head"])
 def test_per_token_states(case):
     """kda_recurrent_states: the state after every token against the oracle's per-token
