@@ -10,10 +10,12 @@
 //
 // Memory-bound: every input is read once (plus a W-1 token halo per tile) and every
 // output written once.  A thread owns 8 consecutive channels (one 16-byte bf16 vector)
-// over a tile of 64 tokens of one batch row, so a wave reads 1 KB of one token row per
+// over a tile of 16 tokens of one batch row, so a wave reads 1 KB of one token row per
 // load; it rebuilds the window at its tile start from the preceding tokens of the same
-// sequence (or the carried state) and then slides it, loading 8 tokens ahead.  When every
-// row fits one tile (T <= 64, no packing: a decode step) the same thread writes the row's
+// sequence (or the carried state) and then slides it, loading 4 tokens ahead (small tiles
+// give many work-groups, which measured faster than deeper loads per thread).  A tile of
+// padding only writes zeros and skips the window.  When every row fits one tile (T <= 16,
+// no packing: a decode step) the same thread writes the row's
 // new carried state after its last token, having read the old one first.  Otherwise a
 // second launch writes each sequence's new carried state with the same window rule at the
 // sequence end; running after the first launch, it may overwrite the state the first one
@@ -25,9 +27,9 @@ namespace kda {
 namespace {
 
 constexpr int CPT = 8;          // channels per thread
-constexpr int TT = 64;          // tokens per tile
+constexpr int TT = 16;          // tokens per tile
 constexpr int NTH = 256;        // threads per work-group
-constexpr int PF = 8;           // tokens loaded ahead
+constexpr int PF = 4;           // tokens loaded ahead
 
 typedef float f8 __attribute__((ext_vector_type(8)));
 
@@ -40,6 +42,28 @@ __device__ __forceinline__ f8 load8(const float *p) {
   const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
   return f8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 }
+// Inputs as loaded: 8 bf16 in one 16-byte vector (half the registers of fp32), or 8 fp32.
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+template <typename TIn>
+struct Raw;
+template <>
+struct Raw<uint16_t> {
+  typedef u4 type;
+  __device__ __forceinline__ static type load(const uint16_t *p) { return *reinterpret_cast<const u4 *>(p); }
+  __device__ __forceinline__ static f8 cvt(type w) {
+    return f8{lo_bf16(w[0]), hi_bf16(w[0]), lo_bf16(w[1]), hi_bf16(w[1]),
+              lo_bf16(w[2]), hi_bf16(w[2]), lo_bf16(w[3]), hi_bf16(w[3])};
+  }
+  __device__ __forceinline__ static type zero() { return u4{0u, 0u, 0u, 0u}; }
+};
+template <>
+struct Raw<float> {
+  typedef f8 type;
+  __device__ __forceinline__ static type load(const float *p) { return load8(p); }
+  __device__ __forceinline__ static f8 cvt(type v) { return v; }
+  __device__ __forceinline__ static type zero() { return f8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}; }
+};
+
 __device__ __forceinline__ void store8(uint16_t *p, f8 v) {
   uint4 w;
   w.x = pack_bf16x2(v[0], v[1]); w.y = pack_bf16x2(v[2], v[3]);
@@ -70,7 +94,7 @@ __device__ __forceinline__ Seq find_seq(const int32_t *cu, int N, int T, int row
 // The W-1 inputs that precede token t0 in sequence q (oldest first): the latest
 // non-padding tokens in [q.s, t0), then the newest entries of the carried state.
 template <typename TIn, int W, bool HAS_MASK>
-__device__ __forceinline__ void window_before(f8 (&h)[W - 1], const TIn *xrow, const TIn *init,
+__device__ __forceinline__ void window_before(typename Raw<TIn>::type (&h)[W - 1], const TIn *xrow, const TIn *init,
                                               const uint8_t *mrow, const Seq &q, int t0, int D, int c0) {
   int found[W - 1];
 #pragma unroll
@@ -87,17 +111,17 @@ __device__ __forceinline__ void window_before(f8 (&h)[W - 1], const TIn *xrow, c
   for (int j = 0; j < W - 1; ++j) {
     const int slot = W - 2 - j;        // h[slot] takes the j-th newest input
     if (found[j] >= 0) {
-      h[slot] = load8(xrow + static_cast<size_t>(found[j]) * D + c0);
+      h[slot] = Raw<TIn>::load(xrow + static_cast<size_t>(found[j]) * D + c0);
     } else if (init) {
       // the (j - cnt)-th newest carried input: state slot W-2-(j-cnt)
-      h[slot] = load8(init + (static_cast<size_t>(q.n) * (W - 1) + (W - 2 - (j - cnt))) * D + c0);
+      h[slot] = Raw<TIn>::load(init + (static_cast<size_t>(q.n) * (W - 1) + (W - 2 - (j - cnt))) * D + c0);
     } else {
-      h[slot] = f8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      h[slot] = Raw<TIn>::zero();
     }
   }
 }
 
-__device__ __forceinline__ void store_state(uint16_t *p, f8 v) { store8(p, v); }
+__device__ __forceinline__ void store_state(uint16_t *p, u4 v) { *reinterpret_cast<u4 *>(p) = v; }
 __device__ __forceinline__ void store_state(float *p, f8 v) { store8(p, v); }
 
 // FUSED: one tile per row and no packing; the thread also writes the row's carried state
@@ -126,28 +150,40 @@ short_conv_kernel(const TIn *__restrict__ x, const float *__restrict__ w, const 
   if (t0 >= q.e) {                     // past the last packed sequence: nothing here
     if (!cu || q.n == N - 1) return;
   }
-  f8 h[W - 1];
+  using R = Raw<TIn>;
+  if constexpr (HAS_MASK && !FUSED) {
+    // a tile of padding only: zeros, and no window to rebuild (which would scan back
+    // over the padded stretch before it)
+    bool any = false;
+    for (int t = t0; t < t1; ++t) any = any || mrow[t] != 0;
+    if (!any) {
+      for (int t = t0; t < t1; ++t)
+        store8(yrow + static_cast<size_t>(t) * D + c0, f8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f});
+      return;
+    }
+  }
+  typename R::type h[W - 1];
   window_before<TIn, W, HAS_MASK>(h, xrow, init, mrow, q, t0, D, c0);
 
   for (int tb = t0; tb < t1; tb += PF) {
-    f8 xin[PF];
+    typename R::type xin[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int t = min(tb + i, t1 - 1);
-      xin[i] = load8(xrow + static_cast<size_t>(t) * D + c0);
+      xin[i] = R::load(xrow + static_cast<size_t>(t) * D + c0);
     }
     if (!HAS_MASK && tb + PF <= t1 && tb + PF <= q.e) {
       // whole batch inside one sequence, no padding: token i's window is win[i .. i+W-1]
-      f8 win[W - 1 + PF];
+      typename R::type win[W - 1 + PF];
 #pragma unroll
       for (int j = 0; j < W - 1; ++j) win[j] = h[j];
 #pragma unroll
       for (int i = 0; i < PF; ++i) win[W - 1 + i] = xin[i];
 #pragma unroll
       for (int i = 0; i < PF; ++i) {
-        f8 z = tap[W - 1] * win[i + W - 1];
+        f8 z = tap[W - 1] * R::cvt(win[i + W - 1]);
 #pragma unroll
-        for (int j = 0; j < W - 1; ++j) z += tap[j] * win[i + j];
+        for (int j = 0; j < W - 1; ++j) z += tap[j] * R::cvt(win[i + j]);
         if (silu) {                    // z * sigmoid(z); 1 + e^-z = inf gives -0 for very negative z
 #pragma unroll
           for (int c = 0; c < CPT; ++c) z[c] = z[c] * __builtin_amdgcn_rcpf(1.f + __expf(-z[c]));
@@ -170,14 +206,13 @@ short_conv_kernel(const TIn *__restrict__ x, const float *__restrict__ w, const 
         if (t >= q.e) return;
 #pragma unroll
         for (int j = 0; j < W - 1; ++j)
-          h[j] = init ? load8(init + (static_cast<size_t>(q.n) * (W - 1) + j) * D + c0)
-                      : f8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          h[j] = init ? R::load(init + (static_cast<size_t>(q.n) * (W - 1) + j) * D + c0) : R::zero();
       }
       f8 out = f8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       if (!HAS_MASK || mrow[t] != 0) {
-        f8 z = tap[W - 1] * xin[i];
+        f8 z = tap[W - 1] * R::cvt(xin[i]);
 #pragma unroll
-        for (int j = 0; j < W - 1; ++j) z += tap[j] * h[j];
+        for (int j = 0; j < W - 1; ++j) z += tap[j] * R::cvt(h[j]);
         if (silu) {
 #pragma unroll
           for (int c = 0; c < CPT; ++c) z[c] = z[c] * __builtin_amdgcn_rcpf(1.f + __expf(-z[c]));
@@ -217,14 +252,10 @@ short_conv_state_kernel(const TIn *__restrict__ x, const TIn *init, const int32_
     row = n;
   }
   const uint8_t *mrow = HAS_MASK ? mask + static_cast<size_t>(row) * T : nullptr;
-  f8 h[W - 1];
+  typename Raw<TIn>::type h[W - 1];
   window_before<TIn, W, HAS_MASK>(h, x + static_cast<size_t>(row) * T * D, init, mrow, q, q.e, D, c0);
 #pragma unroll
-  for (int j = 0; j < W - 1; ++j) {
-    TIn *p = fin + (static_cast<size_t>(n) * (W - 1) + j) * D + c0;
-    if constexpr (sizeof(TIn) == 2) store8(reinterpret_cast<uint16_t *>(p), h[j]);
-    else store8(reinterpret_cast<float *>(p), h[j]);
-  }
+  for (int j = 0; j < W - 1; ++j) store_state(fin + (static_cast<size_t>(n) * (W - 1) + j) * D + c0, h[j]);
 }
 
 template <typename TIn, typename TOut, int W>
