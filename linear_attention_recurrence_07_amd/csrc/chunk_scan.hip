@@ -19,13 +19,14 @@
 //     (16-byte reads, no bank conflicts).
 //   helper waves 4-7: stage the record and value tile of chunk c+1 (loaded two steps
 //     earlier into registers) into the other half of a double-buffered LDS hand-over
-//     area, issue the loads of chunk c+3, and write chunk c-1's output rows from the
-//     other of two output tiles, while the compute waves work on chunk c.
+//     area, issue the loads of chunk c+3, and write chunk c-1's output rows from a ring
+//     of output tiles, while the compute waves work on chunk c.
 // One work-group barrier per step.  The two tiles of a head get work-group ids 8 apart,
 // so they land on the same XCD and share its L2 for the record reads.
 //
-// Gated norm epilogue (nnterp Kimi-Linear page and Kimi-K3 atlas, gate-project page:
-// y = w * o / sqrt(mean(o^2) + eps) * sigmoid(gate) over the 128 channels of a head).
+// Gated norm epilogue, when y is given (nnterp Kimi-Linear page and Kimi-K3 atlas,
+// gate-project page: y = w * o / sqrt(mean(o^2) + eps) * sigmoid(gate) over the 128
+// channels of a head).
 // The mean needs both 64-column tiles of a head, which live in two work-groups.  When a
 // helper writes chunk c's output rows (step c+1) it also publishes, per token, the sum of
 // squares of its 64 columns as one 64-bit word (a flag in the high half, the float in
@@ -62,11 +63,6 @@ constexpr int LDO = DVT + 4;      // fp32 output tile row stride
 constexpr int REC_PIECES = static_cast<int>(sizeof(Rec) / 16);
 constexpr int kSpinLimit = 1 << 18;   // polls of a partner's word before giving up (~0.3 s)
 
-// x of another lane of the same row, chosen by a DPP control code.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
 constexpr int PPT = (REC_PIECES + NHT - 1) / NHT;   // record pieces per helper thread (8)
 static_assert(NCW == 4 && NHT == 256, "thread mappings");
 
@@ -188,11 +184,7 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     if constexpr (NORM) {
       float ss = x0.x * x0.x + x0.y * x0.y + x0.z * x0.z + x0.w * x0.w;
       ss += x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w;
-      // over the 8 lanes of the token: quad swaps, then lane i + lane 7-i of each 8
-      ss += dpp_f32<0xB1>(ss);                 // quad_perm [1, 0, 3, 2]
-      ss += dpp_f32<0x4E>(ss);                 // quad_perm [2, 3, 0, 1]
-      ss += dpp_f32<0x141>(ss);                // row_half_mirror
-      return ss;
+      return group_sum<8>(ss);                 // over the 8 lanes of the token
     }
     return 0.f;
   };

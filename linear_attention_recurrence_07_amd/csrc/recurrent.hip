@@ -9,15 +9,15 @@
 //     o  = S^T q = S'^T q + u (k . q)        one pass: both reductions read S'
 // with k, q L2-normalised and q scaled by 1/sqrt(dk).
 //
-// Layout: one work-group per (batch row, head) slab, or with few slabs per DVW-column
-// tile of one (value columns are independent in the recurrence: each column's update
-// needs only k, q and its own column).  Thread (cg, rg) owns the four value columns
-// 4cg..4cg+3 of the tile, key rows rg, rg+RG, rg+2RG, ... so a wave's float4 loads cover
-// whole state row pieces (coalesced) and the slab lives in registers.  The two column
-// reductions (S'^T k, S'^T q) run over lanes with cross-lane adds, then over waves
-// through LDS.  The next token's inputs are loaded while the current one is processed.
-// This kernel is HBM-bound: at B=64, H=96, d=128 it moves 805 MB of state per step and
-// does 0.86 flop per byte.
+// Layout: one work-group per (batch row, head) slab, or, with few slabs and several
+// tokens, per 32-column tile of one (value columns are independent in the recurrence:
+// each column's update needs only k, q and its own column).  Thread (cg, rg) owns the
+// four value columns 4cg..4cg+3 of the tile, key rows rg, rg+RG, rg+2RG, ... so a wave's
+// float4 loads cover whole state row pieces (coalesced) and the slab lives in registers.
+// The two column reductions (S'^T k, S'^T q) run over lanes with DPP moves, then over
+// waves through LDS.  Column tiles load each token's inputs two tokens ahead.  This
+// kernel is HBM-bound: at B=64, H=96, d=128 it moves 805 MB of state per step and does
+// 0.86 flop per byte.
 //
 // With `states` set it also stores the state after every token ([B, T, H, dk, dv]; a
 // padding token stores the carried state): the per-token states that the pages read by
@@ -71,7 +71,7 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
 
   // Inputs of token t: wave 0 holds k, q, g, beta and the mask flag, every thread its
   // four columns of v.  Column tiles (few work-groups, each walking its tokens) load them
-  // during token t-1; whole slabs (many work-groups per CU hide the latency, and the
+  // two tokens ahead; whole slabs (many work-groups per CU hide the latency, and the
   // extra registers would cost occupancy) at the start of token t.
   constexpr bool PF = DVW < D;
   struct In {
