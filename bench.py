@@ -394,10 +394,28 @@ def cpu_baseline(seed: int = 0, tokens: int = T_PREFILL, min_seconds: float = 10
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
+    # one thread on a short cut of the same prompt, for the per-core rate
+    cut = 256
+    t1 = time.perf_counter()
+    cref.recurrence(x.q[:, :cut], x.k[:, :cut], x.v[:, :cut], x.g[:, :cut], x.beta[:, :cut], in_dtype="bf16",
+                    num_threads=1)
+    one = cut / (time.perf_counter() - t1)
     return {"value": passes * tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{passes} pass(es) over the first {tokens} tokens of the T={T_PREFILL} prompt, "
                       f"all {H} heads (fp64 token-by-token recurrence, {dt:.1f} s)",
-            "cpu": platform.processor() or platform.machine()}
+            "one_thread_tokens_per_s": one, "one_thread_sample": f"first {cut} tokens, all {H} heads",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def main():
