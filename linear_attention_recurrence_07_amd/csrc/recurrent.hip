@@ -60,9 +60,14 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
   const int b = slab / H, h = slab % H;
   float *S = state + static_cast<size_t>(slab) * D * D + col0;
 
-  __shared__ float s_k[D], s_q[D], s_e[D];
-  __shared__ float s_red[NW][2][DVW];
-  __shared__ float s_scal[4];
+  // Token inputs (normalised k, q, decay factors; k.q, beta, the valid flag) and the
+  // waves' partial column sums.  Column tiles keep three input sets and two sum sets in
+  // flight (see the token loop below); whole slabs one of each.
+  constexpr bool PF = DVW < D;
+  constexpr int NB = PF ? 3 : 1, NR = PF ? 2 : 1;
+  __shared__ float s_k[NB][D], s_q[NB][D], s_e[NB][D];
+  __shared__ float s_red[NR][NW][2][DVW];
+  __shared__ float s_scal[NB][4];
 
   float4 s[RPT];
 #pragma unroll
@@ -73,11 +78,22 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
   // four columns of v.  Column tiles (few work-groups, each walking its tokens) load them
   // two tokens ahead; whole slabs (many work-groups per CU hide the latency, and the
   // extra registers would cost occupancy) at the start of token t.
-  constexpr bool PF = DVW < D;
+  // Raw as loaded (bf16 stays 16-bit): converting right after a load would make the
+  // compiler wait for it there instead of at the use a token or two later.
+  typedef typename std::conditional<sizeof(TIn) == 2, uint2, float4>::type RawV;
   struct In {
-    float k[EPL], q[EPL], g[EPL], bt;
+    TIn k[EPL], q[EPL];
+    float g[EPL], bt;
     uint32_t mk;
-    float4 v;
+    RawV v;
+  };
+  auto f32_of = [](TIn x) -> float {
+    if constexpr (sizeof(TIn) == 2) return bf16_to_f32(x);
+    else return x;
+  };
+  auto f32x4_of = [](RawV x) -> float4 {
+    if constexpr (sizeof(TIn) == 2) return make_float4(lo_bf16(x.x), hi_bf16(x.x), lo_bf16(x.y), hi_bf16(x.y));
+    else return x;
   };
   auto fetch = [&](int t, In &in) {
     const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
@@ -86,107 +102,106 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
       for (int j = 0; j < EPL; ++j) {
         const int e = lane + 64 * j;
         if (e < D) {
-          in.k[j] = Elem<TIn>::load(k, tok * D + e);
-          in.q[j] = Elem<TIn>::load(q, tok * D + e);
+          in.k[j] = k[tok * D + e];
+          in.q[j] = q[tok * D + e];
           in.g[j] = g_head ? g[tok] : g[tok * D + e];
         }
       }
       in.bt = beta[tok];
       in.mk = mask == nullptr ? 1u : mask[static_cast<size_t>(b) * T + t];
     }
-    in.v = Elem<TIn>::load4(v, tok * D + col0 + 4 * cg);
+    in.v = *reinterpret_cast<const RawV *>(v + tok * D + col0 + 4 * cg);
   };
 
-  // One token; `cur` holds its inputs (PF), loaded two tokens earlier, and is refilled
-  // with those of token t+2.
-  auto token = [&](int t, In &cur) {
+  // Wave 0: normalise token t's k and q, its decay factors, k.q, beta and the valid flag
+  // into input set `nb` (from `in` for column tiles, else loaded here).
+  auto prologue = [&](int t, const In &in, int nb) {
     const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
-    float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if constexpr (PF) vv = cur.v;
-    if (wave == 0) {
-      float kk[EPL], qq[EPL], ee[EPL];
-      float sk = 0.f, sq = 0.f;
+    float kk[EPL], qq[EPL], ee[EPL];
+    float sk = 0.f, sq = 0.f;
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) {
-        const int e = lane + 64 * j;
-        kk[j] = qq[j] = 0.f;
-        ee[j] = 1.f;
-        if (e < D) {
-          if constexpr (PF) {
-            kk[j] = cur.k[j];
-            qq[j] = cur.q[j];
-            ee[j] = fast_exp2(cur.g[j] * kLog2e);
-          } else {
-            kk[j] = Elem<TIn>::load(k, tok * D + e);
-            qq[j] = Elem<TIn>::load(q, tok * D + e);
-            ee[j] = fast_exp2((g_head ? g[tok] : g[tok * D + e]) * kLog2e);
-          }
-          sk += kk[j] * kk[j];
-          sq += qq[j] * qq[j];
-        }
-      }
-      sk = wave_sum(sk);
-      sq = wave_sum(sq);
-      const float kn = use_l2 ? rsqrtf(sk + kL2Eps) : 1.f;
-      const float qn = (use_l2 ? rsqrtf(sq + kL2Eps) : 1.f) * scale;
-      float kq = 0.f;
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) {
-        const int e = lane + 64 * j;
-        if (e < D) {
-          s_k[e] = kk[j] * kn;
-          s_q[e] = qq[j] * qn;
-          s_e[e] = ee[j];
-          kq += (kk[j] * kn) * (qq[j] * qn);
-        }
-      }
-      kq = wave_sum(kq);
-      if (lane == 0) {
-        s_scal[0] = kq;
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      kk[j] = qq[j] = 0.f;
+      ee[j] = 1.f;
+      if (e < D) {
         if constexpr (PF) {
-          s_scal[1] = cur.bt;
-          s_scal[2] = cur.mk != 0 ? 1.f : 0.f;
+          kk[j] = f32_of(in.k[j]);
+          qq[j] = f32_of(in.q[j]);
+          ee[j] = fast_exp2(in.g[j] * kLog2e);
         } else {
-          s_scal[1] = beta[tok];
-          s_scal[2] = (mask == nullptr || mask[static_cast<size_t>(b) * T + t] != 0) ? 1.f : 0.f;
+          kk[j] = Elem<TIn>::load(k, tok * D + e);
+          qq[j] = Elem<TIn>::load(q, tok * D + e);
+          ee[j] = fast_exp2((g_head ? g[tok] : g[tok * D + e]) * kLog2e);
         }
+        sk += kk[j] * kk[j];
+        sq += qq[j] * qq[j];
       }
     }
-    if constexpr (PF) fetch(min(t + 2, T - 1), cur);   // (the last token again near the end)
-    sync_lds();
-    const bool valid = s_scal[2] != 0.f;
-    if (valid) {
-      float4 r = make_float4(0.f, 0.f, 0.f, 0.f), p = r;
+    sk = wave_sum(sk);
+    sq = wave_sum(sq);
+    const float kn = use_l2 ? rsqrtf(sk + kL2Eps) : 1.f;
+    const float qn = (use_l2 ? rsqrtf(sq + kL2Eps) : 1.f) * scale;
+    float kq = 0.f;
 #pragma unroll
-      for (int m = 0; m < RPT; ++m) {
-        const int i = rg + RG * m;
-        const float a = s_e[i], kv = s_k[i], qv = s_q[i];
-        s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;
-        r.x += kv * s[m].x; r.y += kv * s[m].y; r.z += kv * s[m].z; r.w += kv * s[m].w;
-        p.x += qv * s[m].x; p.y += qv * s[m].y; p.z += qv * s[m].z; p.w += qv * s[m].w;
-      }
-      r.x = group_sum<RL>(r.x); r.y = group_sum<RL>(r.y);
-      r.z = group_sum<RL>(r.z); r.w = group_sum<RL>(r.w);
-      p.x = group_sum<RL>(p.x); p.y = group_sum<RL>(p.y);
-      p.z = group_sum<RL>(p.z); p.w = group_sum<RL>(p.w);
-      if (lane % RL == 0) {
-        *reinterpret_cast<float4 *>(&s_red[wave][0][4 * cg]) = r;
-        *reinterpret_cast<float4 *>(&s_red[wave][1][4 * cg]) = p;
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      if (e < D) {
+        s_k[nb][e] = kk[j] * kn;
+        s_q[nb][e] = qq[j] * qn;
+        s_e[nb][e] = ee[j];
+        kq += (kk[j] * kn) * (qq[j] * qn);
       }
     }
-    sync_lds();
+    kq = wave_sum(kq);
+    if (lane == 0) {
+      s_scal[nb][0] = kq;
+      if constexpr (PF) {
+        s_scal[nb][1] = in.bt;
+        s_scal[nb][2] = in.mk != 0 ? 1.f : 0.f;
+      } else {
+        s_scal[nb][1] = beta[tok];
+        s_scal[nb][2] = (mask == nullptr || mask[static_cast<size_t>(b) * T + t] != 0) ? 1.f : 0.f;
+      }
+    }
+  };
+  // Every wave: decay its rows with input set nb and put its partial S'^T k, S'^T q
+  // column sums in sum set nr.
+  auto partials = [&](int nb, int nr) {
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f), p = r;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      const int i = rg + RG * m;
+      const float a = s_e[nb][i], kv = s_k[nb][i], qv = s_q[nb][i];
+      s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;
+      r.x += kv * s[m].x; r.y += kv * s[m].y; r.z += kv * s[m].z; r.w += kv * s[m].w;
+      p.x += qv * s[m].x; p.y += qv * s[m].y; p.z += qv * s[m].z; p.w += qv * s[m].w;
+    }
+    r.x = group_sum<RL>(r.x); r.y = group_sum<RL>(r.y);
+    r.z = group_sum<RL>(r.z); r.w = group_sum<RL>(r.w);
+    p.x = group_sum<RL>(p.x); p.y = group_sum<RL>(p.y);
+    p.z = group_sum<RL>(p.z); p.w = group_sum<RL>(p.w);
+    if (lane % RL == 0) {
+      *reinterpret_cast<float4 *>(&s_red[nr][wave][0][4 * cg]) = r;
+      *reinterpret_cast<float4 *>(&s_red[nr][wave][1][4 * cg]) = p;
+    }
+  };
+  // Every thread: the delta-rule update of its rows and token t's output for its
+  // columns, then the stores.
+  auto finish = [&](int t, int nb, int nr, bool valid, float4 vv) {
+    const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
     float4 out = make_float4(0.f, 0.f, 0.f, 0.f);
     if (valid) {
-      float4 rr = *reinterpret_cast<const float4 *>(&s_red[0][0][4 * cg]);
-      float4 pp = *reinterpret_cast<const float4 *>(&s_red[0][1][4 * cg]);
+      float4 rr = *reinterpret_cast<const float4 *>(&s_red[nr][0][0][4 * cg]);
+      float4 pp = *reinterpret_cast<const float4 *>(&s_red[nr][0][1][4 * cg]);
 #pragma unroll
       for (int w = 1; w < NW; ++w) {
-        const float4 r2 = *reinterpret_cast<const float4 *>(&s_red[w][0][4 * cg]);
-        const float4 p2 = *reinterpret_cast<const float4 *>(&s_red[w][1][4 * cg]);
+        const float4 r2 = *reinterpret_cast<const float4 *>(&s_red[nr][w][0][4 * cg]);
+        const float4 p2 = *reinterpret_cast<const float4 *>(&s_red[nr][w][1][4 * cg]);
         rr.x += r2.x; rr.y += r2.y; rr.z += r2.z; rr.w += r2.w;
         pp.x += p2.x; pp.y += p2.y; pp.z += p2.z; pp.w += p2.w;
       }
-      const float bt = s_scal[1], kq = s_scal[0];
+      const float bt = s_scal[nb][1], kq = s_scal[nb][0];
       if constexpr (!PF) vv = Elem<TIn>::load4(v, tok * D + col0 + 4 * cg);
       float4 u;
       u.x = bt * (vv.x - rr.x); u.y = bt * (vv.y - rr.y);
@@ -195,15 +210,23 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
       out.z = pp.z + u.z * kq; out.w = pp.w + u.w * kq;
 #pragma unroll
       for (int m = 0; m < RPT; ++m) {
-        const float kv = s_k[rg + RG * m];
+        const float kv = s_k[nb][rg + RG * m];
         s[m].x += kv * u.x; s[m].y += kv * u.y; s[m].z += kv * u.z; s[m].w += kv * u.w;
       }
     }
     if constexpr (STATES) {
       float *St = states + tok * D * D + col0;
 #pragma unroll
-      for (int m = 0; m < RPT; ++m)
-        *reinterpret_cast<float4 *>(St + static_cast<size_t>(rg + RG * m) * D + 4 * cg) = s[m];
+      for (int m = 0; m < RPT; ++m) {
+        // store from a copy: the next token's decay may then rewrite s[m] without first
+        // waiting for this store to complete
+        float4 c;
+        __asm__ volatile("v_mov_b32 %0, %1" : "=v"(c.x) : "v"(s[m].x));
+        __asm__ volatile("v_mov_b32 %0, %1" : "=v"(c.y) : "v"(s[m].y));
+        __asm__ volatile("v_mov_b32 %0, %1" : "=v"(c.z) : "v"(s[m].z));
+        __asm__ volatile("v_mov_b32 %0, %1" : "=v"(c.w) : "v"(s[m].w));
+        *reinterpret_cast<float4 *>(St + static_cast<size_t>(rg + RG * m) * D + 4 * cg) = c;
+      }
     }
     if constexpr (PF) {
       // Every thread holds `out` of its columns; every wave stores the tile's row (the
@@ -233,20 +256,57 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
         }
       }
     }
-    sync_lds();   // s_k / s_q / s_e / s_red are rewritten by the next token
   };
+
   In inA, inB;
   if constexpr (PF) {
-    if (T > 0) fetch(0, inA);
-    if (T > 1) fetch(1, inB);
+    // Column tiles: one work-group barrier per token.  During token t's partial sums,
+    // wave 0 already prepares token t+1's inputs in set (t+1) % 3; after the barrier every
+    // thread finishes token t.  Set (t+1) % 3 was last read by token t-2, which every
+    // thread finished before token t-1's barrier; token t-1's set is still being read
+    // by threads finishing it, hence three sets.  Sum set t & 1 is next written at token
+    // t+2, after token t+1's barrier.
+    // The state's loads complete here, once (an empty asm that reads them), on every path
+    // into the token loop: otherwise their waits sit at the first use inside the loop,
+    // where every token would also wait for the previous one's memory operations.
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) __asm__ volatile("" ::"v"(s[m].x), "v"(s[m].y), "v"(s[m].z), "v"(s[m].w));
+    if (T > 0) {
+      fetch(0, inA);
+      if (T > 1) fetch(1, inB);
+      if (wave == 0) prologue(0, inA, 0);
+      sync_lds();
+    }
+    // token t: `cur` holds its inputs (v used here), `nxt` those of t+1 (prepared here);
+    // `cur` is refilled with token t+2's.
+    auto step = [&](int t, In &cur, In &nxt) {
+      const int nb = t % 3, nr = t & 1;
+      const bool valid = s_scal[nb][2] != 0.f;
+      if (valid) partials(nb, nr);
+      if (wave == 0 && t + 1 < T) prologue(t + 1, nxt, (t + 1) % 3);
+      sync_lds();
+      // refill `cur` with token t+2's inputs before this token's stores, so that waiting
+      // for those loads later does not wait for the stores (one in-order counter)
+      const RawV vv = cur.v;
+      fetch(min(t + 2, T - 1), cur);          // (the last token again near the end)
+      finish(t, nb, nr, valid, f32x4_of(vv));
+    };
     int t = 0;
     for (; t + 1 < T; t += 2) {
-      token(t, inA);
-      token(t + 1, inB);
+      step(t, inA, inB);
+      step(t + 1, inB, inA);
     }
-    if (t < T) token(t, inA);
+    if (t < T) step(t, inA, inB);
   } else {
-    for (int t = 0; t < T; ++t) token(t, inA);
+    for (int t = 0; t < T; ++t) {
+      if (wave == 0) prologue(t, inA, 0);
+      sync_lds();
+      const bool valid = s_scal[0][2] != 0.f;
+      if (valid) partials(0, 0);
+      sync_lds();
+      finish(t, 0, 0, valid, make_float4(0.f, 0.f, 0.f, 0.f));
+      sync_lds();   // the input and sum sets are rewritten by the next token
+    }
   }
 
 #pragma unroll
