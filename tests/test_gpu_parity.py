@@ -391,7 +391,7 @@ def test_multi_token_decode_with_norm(B, T, H, masked):
     U.assert_close(f"multi-token decode B{B} state", U.to_numpy64(st), rfs, U.BF16_TOL)
 
 
-@pytest.mark.parametrize("case", ["bf16_mask", "f32_tiny", "bf16_per_head"])
+@pytest.mark.parametrize("case", ["bf16_mask", "f32_tiny", "bf16_per_head", "f32_d128_odd_T"])
 def test_per_token_states(case):
     """kda_recurrent_states: the state after every token against the oracle's per-token
     states (padding tokens repeat the carried state), plus o and the final state."""
@@ -405,6 +405,11 @@ def test_per_token_states(case):
         tol = U.BF16_TOL
     elif case == "f32_tiny":
         x = gi.make_inputs("states_tiny", B=1, T=64, H=2, dk=16, dv=16, chunk=16, in_dtype=gi.F32, seed=52)
+        tol = U.F32_TOL
+    elif case == "f32_d128_odd_T":
+        # fp32 inputs through the 32-column tiles (few slabs, several tokens), odd T
+        x = gi.make_inputs("states_f32", B=1, T=21, H=3, dk=128, dv=128, in_dtype=gi.F32, seed=54,
+                           initial_state_std=0.05)
         tol = U.F32_TOL
     else:
         x = gi.make_inputs("states_ph", B=1, T=20, H=2, dk=128, dv=128, in_dtype=gi.BF16, seed=53,
