@@ -23,7 +23,7 @@ template <> struct Vec8<uint16_t> {
     uint4 w;
     w.x = pack_bf16x2(x[0], x[1]); w.y = pack_bf16x2(x[2], x[3]);
     w.z = pack_bf16x2(x[4], x[5]); w.w = pack_bf16x2(x[6], x[7]);
-    *reinterpret_cast<uint4 *>(p) = w;
+    store_nt(p, w);
   }
 };
 template <> struct Vec8<float> {
@@ -32,8 +32,8 @@ template <> struct Vec8<float> {
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
   }
   __device__ __forceinline__ static void store(float *p, const float (&x)[8]) {
-    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4 *>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    store_nt(p, make_float4(x[0], x[1], x[2], x[3]));
+    store_nt(p + 4, make_float4(x[4], x[5], x[6], x[7]));
   }
 };
 

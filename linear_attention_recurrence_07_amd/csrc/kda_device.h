@@ -113,6 +113,20 @@ __device__ __forceinline__ float wave_sum(float x) {
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(r, 48)));
 }
 
+// ------------------------------------------------------------------ streaming stores
+// Non-temporal stores, for data that a kernel writes once and does not read back (the
+// state after a step, per-token states, normalised and filtered outputs).  On MI355X
+// they shorten the B = 64 decode step's state write-back by about a fifth and the
+// per-token state stream by about 30% for the same bytes.  Loads stay ordinary: the
+// same hint on the decode step's state loads made it slower.
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt(float *p, float4 v) {
+  __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4 *>(p));
+}
+__device__ __forceinline__ void store_nt(uint16_t *p, uint4 w) {
+  __builtin_nontemporal_store(u32x4_nt{w.x, w.y, w.z, w.w}, reinterpret_cast<u32x4_nt *>(p));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 

@@ -225,7 +225,7 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
         __asm__ volatile("v_mov_b32 %0, %1" : "=v"(c.y) : "v"(s[m].y));
         __asm__ volatile("v_mov_b32 %0, %1" : "=v"(c.z) : "v"(s[m].z));
         __asm__ volatile("v_mov_b32 %0, %1" : "=v"(c.w) : "v"(s[m].w));
-        *reinterpret_cast<float4 *>(St + static_cast<size_t>(rg + RG * m) * D + 4 * cg) = c;
+        store_nt(St + static_cast<size_t>(rg + RG * m) * D + 4 * cg, c);
       }
     }
     if constexpr (PF) {
@@ -311,7 +311,7 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
 
 #pragma unroll
   for (int m = 0; m < RPT; ++m)
-    *reinterpret_cast<float4 *>(S + static_cast<size_t>(rg + RG * m) * D + 4 * cg) = s[m];
+    store_nt(S + static_cast<size_t>(rg + RG * m) * D + 4 * cg, s[m]);
 }
 
 template <int D, int DVW, int RPT, typename TIn, typename TOut>

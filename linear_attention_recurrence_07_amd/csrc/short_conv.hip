@@ -68,11 +68,11 @@ __device__ __forceinline__ void store8(uint16_t *p, f8 v) {
   uint4 w;
   w.x = pack_bf16x2(v[0], v[1]); w.y = pack_bf16x2(v[2], v[3]);
   w.z = pack_bf16x2(v[4], v[5]); w.w = pack_bf16x2(v[6], v[7]);
-  *reinterpret_cast<uint4 *>(p) = w;
+  store_nt(p, w);
 }
 __device__ __forceinline__ void store8(float *p, f8 v) {
-  reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-  reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  store_nt(p, make_float4(v[0], v[1], v[2], v[3]));
+  store_nt(p + 4, make_float4(v[4], v[5], v[6], v[7]));
 }
 
 // The sequence of batch row `row` that holds token t: [s, e) and its index n.
