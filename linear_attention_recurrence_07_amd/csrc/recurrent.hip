@@ -10,7 +10,7 @@
 // with k, q L2-normalised and q scaled by 1/sqrt(dk).
 //
 // Layout: one work-group per (batch row, head) slab, or, with few slabs and several
-// tokens, per 32-column tile of one (value columns are independent in the recurrence:
+// tokens, per 16-column tile of one (value columns are independent in the recurrence:
 // each column's update needs only k, q and its own column).  Thread (cg, rg) owns the
 // four value columns 4cg..4cg+3 of the tile, key rows rg, rg+RG, rg+2RG, ... so a wave's
 // float4 loads cover whole state row pieces (coalesced) and the slab lives in registers.
@@ -359,7 +359,7 @@ hipError_t launch_d(const Args &a, hipStream_t st) {
   return launch_typed<D, DVW, RPT, float, float>(a, st);
 }
 
-// Slabs below which a d = 128 slab is split into 4 work-groups of 32 columns when the
+// Slabs below which a d = 128 slab is split into 8 work-groups of 16 columns when the
 // call walks more than one token (a single token is one latency either way, and the
 // split needs a separate norm pass).
 constexpr long long kSplitSlabs = 512;
@@ -376,7 +376,7 @@ hipError_t launch_recurrent(const Args &a, hipStream_t st) {
     case 32: return launch_d<32, 32, 4>(a, st);
     case 64: return launch_d<64, 64, 8>(a, st);
     case 128:
-      if (a.T > 1 && static_cast<long long>(a.B) * a.H < kSplitSlabs) return launch_d<128, 32, 4>(a, st);
+      if (a.T > 1 && static_cast<long long>(a.B) * a.H < kSplitSlabs) return launch_d<128, 16, 4>(a, st);
       return launch_d<128, 128, 16>(a, st);
     default: return hipErrorInvalidValue;
   }
