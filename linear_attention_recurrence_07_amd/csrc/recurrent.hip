@@ -187,8 +187,9 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
     }
   };
   // Every thread: the delta-rule update of its rows and token t's output for its
-  // columns, then the stores.
-  auto finish = [&](int t, int nb, int nr, bool valid, float4 vv) {
+  // columns, then the stores.  vv: token t's v of the thread's columns; graw: its gate
+  // as loaded (read by wave 0 with the fused norm).
+  auto finish = [&](int t, int nb, int nr, bool valid, float4 vv, RawV graw) {
     const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
     float4 out = make_float4(0.f, 0.f, 0.f, 0.f);
     if (valid) {
@@ -202,7 +203,6 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
         pp.x += p2.x; pp.y += p2.y; pp.z += p2.z; pp.w += p2.w;
       }
       const float bt = s_scal[nb][1], kq = s_scal[nb][0];
-      if constexpr (!PF) vv = Elem<TIn>::load4(v, tok * D + col0 + 4 * cg);
       float4 u;
       u.x = bt * (vv.x - rr.x); u.y = bt * (vv.y - rr.y);
       u.z = bt * (vv.z - rr.z); u.w = bt * (vv.w - rr.w);
@@ -245,7 +245,7 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
       if (rg == 0) {   // one lane per column group stores the row
         Elem<TOut>::store4(o, tok * D + col0 + 4 * cg, out);
         if constexpr (NORM) {
-          const float4 gt = Elem<TIn>::load4(gate, tok * D + 4 * cg);
+          const float4 gt = f32x4_of(graw);
           const float4 w = *reinterpret_cast<const float4 *>(norm_w + 4 * cg);
           float4 yy;
           yy.x = w.x * out.x * rn * sigmoidf_(gt.x);
@@ -289,7 +289,7 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
       // for those loads later does not wait for the stores (one in-order counter)
       const RawV vv = cur.v;
       fetch(min(t + 2, T - 1), cur);          // (the last token again near the end)
-      finish(t, nb, nr, valid, f32x4_of(vv));
+      finish(t, nb, nr, valid, f32x4_of(vv), vv);
     };
     int t = 0;
     for (; t + 1 < T; t += 2) {
@@ -299,12 +299,21 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
     if (t < T) step(t, inA, inB);
   } else {
     for (int t = 0; t < T; ++t) {
+      // v of this thread's columns and the gate (wave 0, which writes y) are loaded
+      // before the prologue: their latency overlaps the prologue and the partial sums
+      // instead of following them.
+      const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
+      const RawV vraw = *reinterpret_cast<const RawV *>(v + tok * D + col0 + 4 * cg);
+      RawV graw{};
+      if constexpr (NORM) {
+        if (wave == 0) graw = *reinterpret_cast<const RawV *>(gate + tok * D + 4 * cg);
+      }
       if (wave == 0) prologue(t, inA, 0);
       sync_lds();
       const bool valid = s_scal[0][2] != 0.f;
       if (valid) partials(0, 0);
       sync_lds();
-      finish(t, 0, 0, valid, make_float4(0.f, 0.f, 0.f, 0.f));
+      finish(t, 0, 0, valid, f32x4_of(vraw), graw);
       sync_lds();   // the input and sum sets are rewritten by the next token
     }
   }
