@@ -364,19 +364,25 @@ def test_per_head_decay_decode_steps():
     U.assert_close("per-head g decode state", U.to_numpy64(st), rfs, U.BF16_TOL)
 
 
-@pytest.mark.parametrize("B,T,H,masked", [(2, 41, 3, True), (6, 3, 96, False)])
-def test_multi_token_decode_with_norm(B, T, H, masked):
+@pytest.mark.parametrize("B,T,H,masked,in_dtype", [(2, 41, 3, True, gi.BF16), (6, 3, 96, False, gi.BF16),
+                                                    (6, 4, 96, True, gi.BF16), (6, 2, 96, True, gi.F32)])
+def test_multi_token_decode_with_norm(B, T, H, masked, in_dtype):
     """kda_recurrent_step over several tokens with the gated norm, d = 128.  Few slabs
-    (B * H < 512) take the 32-column tiles with the norm as its own pass; many take whole
-    slabs with the norm fused.  o, y and the final state against the oracle."""
+    (B * H < 512) take the 16-column tiles with the norm as its own pass; many take whole
+    slabs with the norm fused, which load each token's v and gate before its reductions
+    (masked tokens too: their values are loaded and unused).  With T <= 5 the mask below
+    pads the whole of row 0 (its state must come back unchanged).  o, y and the final
+    state against the oracle."""
     import linear_attention_recurrence_07_amd as kda
     m = None
     if masked:
         m = np.ones((B, T), dtype=np.uint8)
         m[0, :5] = 0                       # left padding
         m[1, 20:23] = 0                    # a gap inside the row
-    x = gi.make_inputs(f"multi_dec_B{B}_T{T}", B=B, T=T, H=H, dk=128, dv=128, in_dtype=gi.BF16, seed=53 + T,
-                       initial_state_std=0.05, norm=True, mask=m)
+        if T < 23:
+            m[1, T - 1] = 0                # right padding
+    x = gi.make_inputs(f"multi_dec_B{B}_T{T}_{in_dtype}", B=B, T=T, H=H, dk=128, dv=128, in_dtype=in_dtype,
+                       seed=53 + T, initial_state_std=0.05, norm=True, mask=m)
     d = U.device_inputs(x, DEV)
     U.log(f"multi-token decode B={B} T={T} H={H} masked={masked}")
     st = d["initial_state"].clone()
@@ -386,9 +392,13 @@ def test_multi_token_decode_with_norm(B, T, H, masked):
     torch.cuda.synchronize()
     ro, rfs, ry = U.oracle(x)
     vm = U.valid_token_mask(x)
-    U.assert_close(f"multi-token decode B{B} o", U.to_numpy64(o)[vm], ro[vm], U.BF16_TOL)
-    U.assert_close(f"multi-token decode B{B} y", U.to_numpy64(y)[vm], ry[vm], U.BF16_TOL)
-    U.assert_close(f"multi-token decode B{B} state", U.to_numpy64(st), rfs, U.BF16_TOL)
+    tol = U.BF16_TOL if in_dtype == gi.BF16 else U.F32_TOL
+    U.assert_close(f"multi-token decode B{B} o", U.to_numpy64(o)[vm], ro[vm], tol)
+    U.assert_close(f"multi-token decode B{B} y", U.to_numpy64(y)[vm], ry[vm], tol)
+    U.assert_close(f"multi-token decode B{B} state", U.to_numpy64(st), rfs, tol)
+    if masked:
+        # padding tokens write zeros
+        assert not np.any(U.to_numpy64(o)[~vm]) and not np.any(U.to_numpy64(y)[~vm])
 
 
 @pytest.mark.parametrize("case", ["bf16_mask", "f32_tiny", "bf16_per_head", "f32_d128_odd_T"])
