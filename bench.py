@@ -223,6 +223,28 @@ def time_fused_norm_scan(kda, P, ws, o, fs, y, reps: int = 10) -> float:
     return e0.elapsed_time(e1) * 1e-3 / reps
 
 
+def time_prefill_y_only(kda, P, ws, fs, y, reps: int = 10) -> dict:
+    """The T=8192 prefill with the gated norm when the caller wants y alone (no head
+    outputs): the preparation, then the scan applying the norm itself and writing no o.
+    Timed on its own with HIP events; not part of the step."""
+    def call():
+        kda.chunk_prefill(P["q"], P["k"], P["v"], P["g"], P["beta"], gate=P["gate"], norm_weight=P["w"],
+                          norm_eps=P["eps"], head_outputs=False, final_state=fs, y=y, workspace=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    nbytes = _bytes_prefill(T_PREFILL, H, D, False, norm=True) - T_PREFILL * H * D * 2   # no o written
+    return {"avg_call_us": t * 1e6, "tokens_per_s": T_PREFILL / t, "algorithmic_bytes": nbytes,
+            "achieved_GBps": nbytes / t / 1e9}
+
+
 def _bytes_decode_state(B: int, H: int, d: int) -> int:
     return 2 * B * H * d * d * 4               # state read + written (fp32)
 
@@ -500,6 +522,9 @@ def main():
     mfma = measured_mfma()
     print("[bench] scan with its own gated norm", file=sys.stderr, flush=True)
     t_fused = time_fused_norm_scan(kda, P, ws, o, fs, y)
+    print("[bench] prefill with y alone", file=sys.stderr, flush=True)
+    y_only = time_prefill_y_only(kda, P, ws, fs, y)
+    y_only["step_prepare_scan_norm_us"] = (t_prep + t_scan + t_nrm) * 1e6
     print("[bench] copy and GEMM ceilings", file=sys.stderr, flush=True)
     ceil = ceilings()
     print("[bench] short convolution", file=sys.stderr, flush=True)
@@ -566,6 +591,9 @@ def main():
         "scan_with_fused_norm": {"avg_call_us": t_fused * 1e6, "scan_plus_norm_us": (t_scan + t_nrm) * 1e6,
                                  "algorithmic_bytes": _bytes_scan(T_PREFILL, H, D, False, norm=True),
                                  "achieved_GBps": _bytes_scan(T_PREFILL, H, D, False, norm=True) / t_fused / 1e9},
+        # the prefill + norm when only y is wanted (the scan applies the norm, no o is
+        # written), timed on its own against the step's preparation + scan + norm
+        "prefill_y_only": y_only,
         "ceilings": ceil,
         # the causal short convolution in front of the kernel, timed on its own (two
         # launches per call: the filter over all tokens, then the carried-input update)

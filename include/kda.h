@@ -99,7 +99,8 @@ typedef struct {
  *                                 requires B == 1 and p->num_seqs = N
  *   mask          [B, T]          uint8, 1 = token, 0 = padding (skipped: state unchanged,
  *                                 output 0), or NULL; not together with cu_seqlens
- *   o             [B, T, H, dv]   out_dtype head outputs (before the gated norm)
+ *   o             [B, T, H, dv]   out_dtype head outputs (before the gated norm); may be
+ *                                 NULL when y is given (only y is then written)
  *   final_state   [N, H, dk, dv]  fp32; may be the same buffer as initial_state
  *   gate          [B, T, H, dv]   in_dtype, norm_weight [dv] fp32, y [B, T, H, dv]
  *                                 out_dtype: the gated norm y = w * o / rms(o) *
@@ -114,8 +115,10 @@ typedef struct {
  * The bf16 kernel for dk = dv = 128 runs in two launches: a preparation pass over every
  * (sequence, head, chunk) at once, which stores each chunk's intra-chunk products in the
  * workspace (30,224 bytes per chunk and head, plus 512 bytes that kda_chunk_scan's own
- * norm uses), then the sequential state scan; with y given, a third launch applies the
- * gated norm to o.
+ * norm uses), then the sequential state scan; with y and o given, a third launch applies
+ * the gated norm to o.  With y given and o NULL the scan applies the norm itself and
+ * writes no o (as kda_chunk_scan with gate, norm_weight and y), which saves writing o
+ * and reading it back.  The other kernels apply the norm in the same launch either way.
  */
 kda_status_t kda_chunk_prefill(const kda_params_t *p,
                                const void *q, const void *k, const void *v,
@@ -147,14 +150,15 @@ size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed);
  * ahead of the scan that consumes it.
  *
  * kda_chunk_scan reads v, initial_state (or NULL) and the records, and writes o and
- * final_state; with gate, norm_weight and y (all set or all NULL, as in
+ * final_state (o may be NULL when y is given); with gate, norm_weight and y (all set or
+ * all NULL, as in
  * kda_chunk_prefill; eps is p->norm_eps) it also writes the gated norm y itself, in
  * the same launch: each head's 128 value columns are scanned by two work-groups of 64,
  * which exchange per-token sums of squares through the workspace (device-coherent
  * 64-bit words; a wait for the other work-group is bounded and, if it ever ran out,
  * would give NaN in y rather than hang).  That saves the second read of o but loads the
- * scan, so at large T it is slower than the separate norm; kda_chunk_prefill uses the
- * separate one.  p and cu_seqlens must be those the workspace was prepared with, and the
+ * scan, so at large T it is slower than writing o and running the separate norm;
+ * kda_chunk_prefill uses the separate one when o is wanted.  p and cu_seqlens must be those the workspace was prepared with, and the
  * preparation must have completed or be ordered before the scan on the stream; the
  * workspace must not be modified in between.  The records already hold the effect of a
  * mask, so the scan takes none.

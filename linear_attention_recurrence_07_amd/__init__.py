@@ -175,9 +175,12 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   use_qk_l2norm_in_kernel: bool = True, chunk: int = 0,
                   output_dtype: Optional[torch.dtype] = None,
                   out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-                  y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+                  y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  head_outputs: bool = True):
     """Chunked prefill.  Returns (o, final_state), or (o, final_state, y) with the fused
-    sigmoid-gated RMSNorm when gate and norm_weight are given.
+    sigmoid-gated RMSNorm when gate and norm_weight are given.  With the norm and
+    head_outputs=False the head outputs are not written (o is None): the bf16 d = 128
+    kernel then applies the norm inside its state scan.
 
     cu_seqlens ([N+1] int32; a CPU tensor is validated then copied to the GPU) packs N
     sequences into B = 1; attention_mask ([B, T], nonzero = token) marks padding.
@@ -222,11 +225,15 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         _dev(initial_state, "initial_state", dev)
         if initial_state.dtype != torch.float32 or initial_state.shape != (N, H, dk, dv):
             raise ValueError(f"initial_state must be float32 [{N},{H},{dk},{dv}]")
-    o = out if out is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
-    _dev(o, "out", dev)
+    norm = gate is not None or norm_weight is not None
+    if not head_outputs and not norm:
+        raise ValueError("head_outputs=False needs the gated norm (gate and norm_weight)")
+    o = None
+    if head_outputs:
+        o = out if out is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
+        _dev(o, "out", dev)
     fs = final_state if final_state is not None else torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _dev(fs, "final_state", dev)
-    norm = gate is not None or norm_weight is not None
     if norm:
         if gate is None or norm_weight is None:
             raise ValueError("the gated norm needs both gate and norm_weight")
@@ -323,10 +330,11 @@ def chunk_scan(v: torch.Tensor, workspace: torch.Tensor, initial_state: Optional
                output_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
                final_state: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None,
                norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
-               y: Optional[torch.Tensor] = None):
+               y: Optional[torch.Tensor] = None, head_outputs: bool = True):
     """Second launch of the bf16, d = 128 chunked prefill: the state scan over the records
     chunk_prepare wrote (same shapes and cu_seqlens).  Returns (o, final_state), or
-    (o, final_state, y) with the gated norm (gate and norm_weight given)."""
+    (o, final_state, y) with the gated norm (gate and norm_weight given); with the norm
+    and head_outputs=False, o is not written (None)."""
     lib = load_library()
     dev = v.device
     B, T, H, dv = v.shape
@@ -339,11 +347,16 @@ def chunk_scan(v: torch.Tensor, workspace: torch.Tensor, initial_state: Optional
         if initial_state.dtype != torch.float32 or initial_state.shape != (N, H, dk, dv):
             raise ValueError(f"initial_state must be float32 [{N},{H},{dk},{dv}]")
     out_dt = output_dtype or v.dtype
-    o = out if out is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
-    _dev(o, "out", dev)
+    norm = gate is not None or norm_weight is not None
+    if not head_outputs and not norm:
+        raise ValueError("head_outputs=False needs the gated norm (gate and norm_weight)")
+    o = None
+    if head_outputs:
+        o = out if out is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
+        _dev(o, "out", dev)
+        out_dt = o.dtype
     fs = final_state if final_state is not None else torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _dev(fs, "final_state", dev)
-    norm = gate is not None or norm_weight is not None
     yy = None
     if norm:
         if gate is None or norm_weight is None:
@@ -354,10 +367,12 @@ def chunk_scan(v: torch.Tensor, workspace: torch.Tensor, initial_state: Optional
             raise ValueError("gate must have v's shape and dtype")
         if norm_weight.dtype != torch.float32 or norm_weight.shape != (dv,):
             raise ValueError(f"norm_weight must be float32 [{dv}]")
-        yy = y if y is not None else torch.empty_like(o)
+        yy = y if y is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
         _dev(yy, "y", dev)
+        if yy.dtype != out_dt:
+            raise TypeError(f"y dtype {yy.dtype} differs from the output dtype {out_dt}")
     p = _params(B, T, H, dk, dv, num_seqs=N if cu_dev is not None else 0, in_dtype=_dtype_code(v.dtype),
-                out_dtype=_dtype_code(o.dtype), norm_eps=norm_eps)
+                out_dtype=_dtype_code(out_dt), norm_eps=norm_eps)
     _check(lib.kda_chunk_scan(ctypes.byref(p), _ptr(v), _ptr(initial_state), _ptr(cu_dev), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _ptr(o), _ptr(fs), _ptr(gate),
                               _ptr(norm_weight), _ptr(yy), _stream(dev)))

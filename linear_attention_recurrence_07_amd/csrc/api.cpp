@@ -151,7 +151,7 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
   KDA_TRY(check_ptr(v, "v", true));
   KDA_TRY(check_ptr(g, "g", true, p->decay_per_head ? 4u : 16u));
   KDA_TRY(check_ptr(beta, "beta", true, 4));
-  KDA_TRY(check_ptr(o, "o", true));
+  KDA_TRY(check_ptr(o, "o", y == nullptr));   // optional when y is wanted
   KDA_TRY(check_ptr(final_state, "final_state", true));
   KDA_TRY(check_ptr(initial_state, "initial_state", false));
   KDA_TRY(check_layout(p, cu_seqlens, mask));
@@ -171,13 +171,17 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
       return fail(KDA_ERR_UNSUPPORTED, "chunk 32 needs bf16 inputs with dk = dv = 128 and T * H * 128 < 2^31");
   }
   if (mfma) {
-    // The gated norm runs as its own launch over o: the scan can apply it itself
-    // (kda_chunk_scan with gate and y), but on the scan's 2 work-groups per head that
-    // costs more than a separate pass at full HBM bandwidth on every CU.
+    // With o wanted, the gated norm runs as its own launch over o: the scan can apply it
+    // itself, but on the scan's 2 work-groups per head that costs more than a separate
+    // pass at full HBM bandwidth on every CU.  With y alone, the scan applies it and
+    // writes no o.
     KDA_TRY(check_workspace(p, cu_seqlens, workspace, workspace_bytes));
     KDA_TRY(hip_status(kda::launch_chunk_prep(a, workspace, st), "prefill (chunk preparation)"));
+    if (o == nullptr) {
+      a.gate = gate; a.norm_w = norm_weight; a.y = y;
+    }
     KDA_TRY(hip_status(kda::launch_chunk_scan(a, workspace, st), "prefill (state scan)"));
-    if (y != nullptr) {
+    if (y != nullptr && o != nullptr) {
       const int64_t rows = static_cast<int64_t>(p->B) * p->T * p->H;
       KDA_TRY(hip_status(kda::launch_gated_rmsnorm(o, gate, norm_weight, y, rows, p->dv, p->norm_eps,
                                                    a.out_bf16, a.in_bf16, a.out_bf16, st),
@@ -222,7 +226,7 @@ kda_status_t kda_chunk_scan(const kda_params_t *p, const void *v, const float *i
                             void *y, void *stream) {
   KDA_TRY(check_params(p, true));
   KDA_TRY(check_ptr(v, "v", true));
-  KDA_TRY(check_ptr(o, "o", true));
+  KDA_TRY(check_ptr(o, "o", y == nullptr));   // optional when y is wanted
   KDA_TRY(check_ptr(final_state, "final_state", true));
   KDA_TRY(check_ptr(initial_state, "initial_state", false));
   KDA_TRY(check_layout(p, cu_seqlens, nullptr));

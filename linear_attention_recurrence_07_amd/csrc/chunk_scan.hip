@@ -81,8 +81,9 @@ static_assert(sizeof(Smem<kNormLag + 1>) <= 160 * 1024, "LDS budget");
 static_assert(sizeof(Hand) % 16 == 0 && (LDV * 2) % 16 == 0 && (LDO * 4) % 16 == 0, "16-byte LDS access");
 
 // NORM: also write y (gated norm over the head's 128 channels); xs holds the exchanged
-// partial sums of squares, 2 tiles x 32 tokens per (slot, head).
-template <typename TOut, bool HAS_INIT, bool NORM>
+// partial sums of squares, 2 tiles x 32 tokens per (slot, head).  WRITE_O: store the head
+// outputs o (only NORM may leave them out: the caller then wants y alone).
+template <typename TOut, bool HAS_INIT, bool NORM, bool WRITE_O>
 __global__ void __launch_bounds__(NT, 1)
 chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, const float *init,
                   float *fin, const int32_t *__restrict__ cu, TOut *__restrict__ o,
@@ -180,7 +181,9 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     const int t = t_begin + cidx * C + hr;
     const float4 x0 = *reinterpret_cast<const float4 *>(ost + hr * LDO + hc8);
     const float4 x1 = *reinterpret_cast<const float4 *>(ost + hr * LDO + hc8 + 4);
-    if (t < t_end) store_row(o, t, x0, x1);
+    if constexpr (WRITE_O) {
+      if (t < t_end) store_row(o, t, x0, x1);
+    }
     if constexpr (NORM) {
       float ss = x0.x * x0.x + x0.y * x0.y + x0.z * x0.z + x0.w * x0.w;
       ss += x1.x * x1.x + x1.y * x1.y + x1.z * x1.z + x1.w * x1.w;
@@ -458,11 +461,12 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
   }
 }
 
-template <typename TOut, bool HAS_INIT, bool NORM>
+template <typename TOut, bool HAS_INIT, bool NORM, bool WRITE_O>
 hipError_t launch3(const Args &a, const void *ws, uint64_t *xs, hipStream_t st) {
+  static_assert(WRITE_O || NORM, "without the norm the head outputs are the only output");
   const int units = a.N * a.H;
   const unsigned grid = static_cast<unsigned>((units + 7) / 8) * 8 * NTILE;
-  hipLaunchKernelGGL((chunk_scan_kernel<TOut, HAS_INIT, NORM>), dim3(grid), dim3(NT), 0, st,
+  hipLaunchKernelGGL((chunk_scan_kernel<TOut, HAS_INIT, NORM, WRITE_O>), dim3(grid), dim3(NT), 0, st,
                      static_cast<const uint16_t *>(a.v), static_cast<const Rec *>(ws), a.init, a.state, a.cu,
                      static_cast<TOut *>(a.o), static_cast<const uint16_t *>(a.gate), a.norm_w,
                      static_cast<TOut *>(a.y), xs, a.eps, a.T, a.H, units);
@@ -471,7 +475,8 @@ hipError_t launch3(const Args &a, const void *ws, uint64_t *xs, hipStream_t st) 
 
 template <typename TOut, bool HAS_INIT>
 hipError_t launch2(const Args &a, const void *ws, uint64_t *xs, hipStream_t st) {
-  return a.y ? launch3<TOut, HAS_INIT, true>(a, ws, xs, st) : launch3<TOut, HAS_INIT, false>(a, ws, xs, st);
+  if (!a.y) return launch3<TOut, HAS_INIT, false, true>(a, ws, xs, st);
+  return a.o ? launch3<TOut, HAS_INIT, true, true>(a, ws, xs, st) : launch3<TOut, HAS_INIT, true, false>(a, ws, xs, st);
 }
 
 template <typename TOut>

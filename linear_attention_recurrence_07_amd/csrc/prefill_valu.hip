@@ -169,7 +169,7 @@ prefill_valu_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
       if (r < L) {
         for (int col = part; col < D; col += 16) {
           const float ov = sV[r][col];
-          Elem<TOut>::store(o, base + col, ov);
+          if (o != nullptr) Elem<TOut>::store(o, base + col, ov);   // null: y alone is wanted
           if constexpr (NORM) {
             const float gt = Elem<TIn>::load(gate, base + col);
             Elem<TOut>::store(y, base + col, norm_w[col] * (ov * rn) * sigmoidf_(gt));

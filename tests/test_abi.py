@@ -84,6 +84,9 @@ def test_prefill_validation_codes():
     assert _prefill(None) == 1
     assert _prefill(_p(), q=None) == 1
     assert _prefill(_p(), o=None) == 1
+    # o may be NULL when y is wanted: these get past the o check and stop at a later one
+    assert _prefill(_p(), o=None, gate=A, w=A, y=A) == 8                   # the workspace check
+    assert _prefill(_p(chunk=16), o=None, gate=A, w=A, y=MIS) == 4         # y's alignment
     assert _prefill(_p(B=0)) == 2
     assert _prefill(_p(T=-1)) == 2
     assert _prefill(_p(in_dtype=7)) == 3
@@ -153,6 +156,8 @@ def test_stage_validation_codes():
     assert prep(_p(B=1, num_seqs=1), cu=A, mask=A) == 5
     assert scan(_p(), v=None) == 1
     assert scan(_p(), fs=None) == 1
+    assert scan(_p(), o=None) == 1                          # o is required without y
+    assert scan(_p(), o=None, gate=A, w=A, y=A, nbytes=need - 1) == 8   # ... and optional with it
     assert scan(_p(), init=MIS) == 4
     assert scan(_p(), y=A) == 5                             # gate, norm_weight, y: all or none
     assert scan(_p(), gate=A, w=A) == 5

@@ -291,6 +291,50 @@ def test_scan_with_fused_norm():
         U.assert_close(f"fused norm {name} y", U.to_numpy64(y2)[vm], ry[vm], U.BF16_TOL)
 
 
+def test_prefill_y_only():
+    """kda_chunk_prefill with the gated norm and no head outputs (o = NULL): the bf16
+    d = 128 kernel applies the norm inside its scan and writes y alone; the vector-ALU
+    kernel skips its o stores.  y within 1e-5 (of rms) of the call that also writes o
+    (bitwise for the vector-ALU kernel), the final state bitwise the same, y within
+    tolerance of the oracle, padding rows of y zero, and the y buffer's packed tail
+    untouched."""
+    import linear_attention_recurrence_07_amd as kda
+    x = gi.varlen_packed((100, 0, 37, 64, 129, 1, 33), H=3, d=128)
+    cases = [("mfma packed", x, 0), ("mfma right-padded", gi.padded_from_packed(x, left=False), 0),
+             ("mfma plain+init", gi.make_inputs("y_only", B=2, T=77, H=2, dk=128, dv=128, in_dtype=gi.BF16,
+                                                seed=37, initial_state_std=0.02, norm=True), 0),
+             ("valu f32 tiny", gi.tiny(), 0),
+             ("valu bf16 chunk16", gi.make_inputs("y_only_valu", B=2, T=45, H=2, dk=128, dv=128,
+                                                  in_dtype=gi.BF16, seed=38, norm=True), 16)]
+    f32 = torch.float32
+    for name, c, chunk in cases:
+        U.log(f"prefill y only: {name}")
+        d = U.device_inputs(c, DEV)
+        vm = U.valid_token_mask(c)
+        m = torch.from_numpy(vm).to(DEV)
+        kw = dict(cu_seqlens=d["cu_seqlens"], attention_mask=d["mask"], gate=d["gate"],
+                  norm_weight=d["norm_weight"], norm_eps=c.norm_eps, output_dtype=f32, chunk=chunk)
+        _, f1, y1 = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], **kw)
+        y_buf = torch.full_like(y1, 7.0)
+        o2, f2, y2 = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                                       head_outputs=False, y=y_buf, **kw)
+        torch.cuda.synchronize()
+        assert o2 is None and y2 is y_buf, name
+        assert torch.equal(f1, f2), name
+        if name.startswith("valu"):
+            assert torch.equal(y1[m], y2[m]), name
+        U.assert_close(f"y only {name} vs y with o", U.to_numpy64(y2)[vm], U.to_numpy64(y1)[vm], 1e-5)
+        _, _, ry = U.oracle(c)
+        tol = U.F32_TOL if c.in_dtype == gi.F32 else U.BF16_TOL
+        U.assert_close(f"y only {name} y", U.to_numpy64(y2)[vm], ry[vm], tol)
+        if d["mask"] is not None:
+            assert torch.all(y2[~m] == 0), name
+        if d["cu_seqlens"] is not None:
+            assert torch.all(y2[~m] == 7.0), name           # tokens past the last sequence
+    with pytest.raises(ValueError):
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], head_outputs=False)
+
+
 def test_scan_with_fused_norm_more_work_groups_than_cus():
     """The fused-norm scan when its work-groups (2 per sequence and head) outnumber the
     CUs: 5 packed sequences (one empty) x 48 heads = 480 work-groups, dispatched in two
