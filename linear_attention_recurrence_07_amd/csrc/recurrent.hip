@@ -289,7 +289,7 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
       // for those loads later does not wait for the stores (one in-order counter)
       const RawV vv = cur.v;
       fetch(min(t + 2, T - 1), cur);          // (the last token again near the end)
-      finish(t, nb, nr, valid, f32x4_of(vv), vv);
+      finish(t, nb, nr, valid, f32x4_of(vv), RawV{});   // column tiles: no fused norm, no gate
     };
     int t = 0;
     for (; t + 1 < T; t += 2) {
