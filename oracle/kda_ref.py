@@ -22,7 +22,7 @@ Per head, with S of shape [dk, dv], one token does, in this order:
     o_t = S^T q_t                                (read the updated state)
 with k_t = k/||k||, q_t = q/||q|| / sqrt(dk).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   decay before the update and the read after the write; g is a natural log; the L2
   norm is x / sqrt(sum x^2 + 1e-6); a padding-mask zero leaves the state untouched
   and gives a zero output; cu_seqlens restarts the recurrence per sequence with that

@@ -20,7 +20,7 @@ where x before the first token of a sequence comes from its carried state (the W
 inputs that preceded it, oldest first) or is zero when no state is given.  The state
 after the call holds the last W-1 inputs of each sequence, oldest first.
 
-Readings where the pages are silent (each listed in the design doc): the carried state holds
+Readings taken where the pages are silent: the carried state holds
 raw inputs, not activations; a padding-mask zero skips the token (output 0, the window
 does not advance, so padding never enters the window), matching the recurrence's mask;
 cu_seqlens restarts the window per sequence from that sequence's state.
