@@ -14,8 +14,9 @@
 // state carry.
 //
 // Work-group: one (sequence, head, chunk), two waves; wave m owns the 16-token sub-block
-// m.  Each lane loads its token's channels directly in MFMA operand order (lane 16 lg + r:
-// token r of the sub-block, channels 32 s + kidx(lg, e) of K block s), so
+// m.  Each lane holds its token's channels in MFMA operand order (lane 16 lg + r: token r
+// of the sub-block, channels 32 s + kidx(lg, e) of K block s): g is loaded that way, q and
+// k as 16 contiguous bytes per K block that one row swap puts in that order, so
 //   * G is a prefix sum over the 16 lanes of a row (DPP row shifts), in log2 units, and
 //     every decay factor is one exp2 of a difference of running sums;
 //   * the decayed key and query fragments go from registers straight to the record;
@@ -80,6 +81,17 @@ __device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
   lo = u32x2{l.x, l.y};
 }
 __device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
+// w holds 8 channels 8L .. 8L+7 of a K block (L = (0, 2, 1, 3)[lg]); one row swap of its
+// halves (odd rows of the first with even rows of the second) leaves channels 4lg .. 4lg+3
+// in lo and 16 + 4lg .. 16 + 4lg + 3 in hi, the MFMA operand order.
+__device__ __forceinline__ void operand_halves(u32x4 w, u32x2 &lo, u32x2 &hi) {
+  const auto a = __builtin_amdgcn_permlane16_swap(w[0], w[2], false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(w[1], w[3], false, false);
+  uint32_t a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+  __asm__("" : "+v"(a1), "+v"(b1));   // keep the optimiser from merging the swap's two outputs
+  lo = u32x2{a0, b0};
+  hi = u32x2{a1, b1};
+}
 __device__ __forceinline__ f32x4 mma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
@@ -136,17 +148,24 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
   bool valid = tok < t_end;
   if constexpr (HAS_MASK) valid = valid && mask[row0 + tcl] != 0;
   const int off = tcl * (H * DK) + h * DK + 4 * lg;
-  const uint16_t *kp = k + row0 * H * DK + off;
-  const uint16_t *qp = q + row0 * H * DK + off;
+  // q and k: one 16-byte load per K block, lane group lg reading channels 32 s + 8 L ..
+  // 32 s + 8 L + 7 with L = (0, 2, 1, 3)[lg], then a row swap (operand_halves)
+  const int off16 = tcl * (H * DK) + h * DK + 8 * (((lg & 1) << 1) | (lg >> 1));
+  const uint16_t *kp = k + row0 * H * DK + off16;
+  const uint16_t *qp = q + row0 * H * DK + off16;
   const float *gp = G_HEAD ? g + (row0 + tcl) * H + h : g + row0 * H * DK + off;
   u32x2 kr[4][2], qr[4][2];
+  u32x4 kw[4], qw[4];
   f32x4 G[4][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    kw[s] = *reinterpret_cast<const u32x4 *>(kp + 32 * s);
+    qw[s] = *reinterpret_cast<const u32x4 *>(qp + 32 * s);
+  }
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      kr[s][hh] = *reinterpret_cast<const u32x2 *>(kp + 32 * s + 16 * hh);
-      qr[s][hh] = *reinterpret_cast<const u32x2 *>(qp + 32 * s + 16 * hh);
       if constexpr (G_HEAD) {
         const float gs = *gp;
         G[s][hh] = f32x4{gs, gs, gs, gs};
@@ -155,6 +174,11 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
       }
     }
   const float bt = beta[(row0 + tcl) * H + h];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    operand_halves(kw[s], kr[s][0], kr[s][1]);
+    operand_halves(qw[s], qr[s][0], qr[s][1]);
+  }
 
   // ---------------------------------------------------------------- norms, running sums
   // Padding and tokens past the end act as no-ops: zero key, query, beta and decay.
