@@ -515,6 +515,18 @@ def test_config3_varlen_full():
         U.assert_close(f"padded vs packed o seq{n}", po[n, :ln], qo[0, cu[n]:cu[n + 1]], 1e-6)
         U.assert_close(f"padded vs packed y seq{n}", py[n, :ln], qy[0, cu[n]:cu[n + 1]], 1e-6)
     U.assert_close("padded vs packed state", pfs, qfs, 1e-6)
+    del po, pfs, py
+    # y alone (no head outputs: the scan applies the norm itself) at the full config
+    import linear_attention_recurrence_07_amd as kda
+    U.log("config 3 packed, y alone, against the run that writes o (all heads)")
+    d = U.device_inputs(x, DEV)
+    none, yfs, yy = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                                      cu_seqlens=d["cu_seqlens"], gate=d["gate"], norm_weight=d["norm_weight"],
+                                      norm_eps=x.norm_eps, output_dtype=torch.float32, head_outputs=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert np.array_equal(U.to_numpy64(yfs), qfs)
+    U.assert_close("y alone vs y with o", U.to_numpy64(yy), qy, 1e-5)
 
 
 def test_config4_decode_B64():
