@@ -184,7 +184,9 @@ kda_status_t kda_chunk_scan(const kda_params_t *p, const void *v,
  * kda_recurrent_step -- the decode kernel: the token-by-token form, for one new token
  * per row (T = 1) or a few tokens (T >= 1, applied in order).  The state is read and
  * written in place: state [B, H, dk, dv] fp32 holds S before the call and S after the
- * last token on return.  Other arguments as for kda_chunk_prefill (no cu_seqlens).
+ * last token on return.  Other arguments as for kda_chunk_prefill (no cu_seqlens), except
+ * that o is always required (with few slabs and several tokens the gated norm runs as its
+ * own pass over o): NULL o is KDA_ERR_NULL.
  */
 kda_status_t kda_recurrent_step(const kda_params_t *p,
                                 const void *q, const void *k, const void *v,

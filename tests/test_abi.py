@@ -174,6 +174,7 @@ def test_recurrent_and_norm_validation_codes():
         return lib.kda_recurrent_step(ctypes.byref(p), *[d[n] for n in names], None)
 
     assert rec(_p(), state=None) == 1
+    assert rec(_p(), o=None, gate=A, w=A, y=A) == 1           # o is required here, even with y
     assert rec(_p(dk=128, dv=64)) == 6
     assert rec(_p(), y=A) == 5
     assert rec(_p(), g=MIS) == 4
