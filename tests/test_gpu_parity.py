@@ -331,6 +331,14 @@ def test_prefill_y_only():
             assert torch.all(y2[~m] == 0), name
         if d["cu_seqlens"] is not None:
             assert torch.all(y2[~m] == 7.0), name           # tokens past the last sequence
+        if c.in_dtype == gi.BF16:
+            # bf16 y alone: the exact rounding of the fp32 y (same kernel, other store)
+            kw16 = dict(kw, output_dtype=None)
+            _, f3, y3 = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                                          head_outputs=False, **kw16)
+            torch.cuda.synchronize()
+            assert y3.dtype == torch.bfloat16 and torch.equal(f3, f2), name
+            assert torch.equal(y3[m], y2[m].to(torch.bfloat16)), name
     with pytest.raises(ValueError):
         kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], head_outputs=False)
 
