@@ -113,7 +113,8 @@ def _draw(rng: np.random.Generator, shape, kind: str, dtype=np.float32, **kw) ->
 
 
 def _sigmoid_f32(x: np.ndarray) -> np.ndarray:
-    # beta is the sigmoid of a normal draw (the pages: "the sigmoid of b_proj's output").
+    # beta is a logistic function of a normal draw: the write strengths reach the kernel
+    # already squashed into (0, 1) (nnterp Kimi-Linear page, Notes, KDA paragraph).
     return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
 
 
@@ -137,10 +138,13 @@ def make_inputs(
     cu_seqlens: Optional[Sequence[int]] = None,
     mask: Optional[np.ndarray] = None,
     normalize_qk: bool = True,
+    qk_scale_by_head: Optional[Sequence[float]] = None,
     decay_per_head: bool = False,
 ) -> KdaInputs:
     """Draw one problem in the fixed order q, k, v, g, beta-logits, initial_state, gate, w.
 
+    q and k are N(0, 1) rows scaled to unit length (normalize_qk), then multiplied per head
+    by qk_scale_by_head (k takes the factors in reverse head order) when given.
     g is uniform in [low, high) per element (log decay, <= 0); with g_ranges_by_head each
     head h gets its own range.  beta = sigmoid(N(0,1)).  initial_state ~ N(0, std) when a
     std is given.  gate ~ N(0,1) and w ~ 1 + N(0, 0.1) when norm is set.
@@ -151,6 +155,12 @@ def make_inputs(
     if normalize_qk:
         q = _unit_rows_f32(q)
         k = _unit_rows_f32(k)
+    if qk_scale_by_head is not None:
+        # raw (not unit) queries and keys: head h's rows are multiplied by the factor
+        # qk_scale_by_head[h % len], so the in-kernel L2 norm has work to do
+        f = np.asarray([qk_scale_by_head[h % len(qk_scale_by_head)] for h in range(H)], np.float32)
+        q = (q * f[None, None, :, None]).astype(np.float32)
+        k = (k * f[::-1][None, None, :, None]).astype(np.float32)
     v = _draw(rng, (B, T, H, dv), "normal")
     if decay_per_head:        # one decay per (token, head): the gated DeltaNet's scalar decay
         g = _draw(rng, (B, T, H), "uniform", low=g_range[0], high=g_range[1])

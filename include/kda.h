@@ -35,6 +35,14 @@
  *    linear_attn_config.gate_lower_bound).  The bf16 chunked kernel factors
  *    within-chunk decays with 16-token reference points and stays finite for
  *    g >= -5.4; the other kernels accept any g <= 0.
+ *  - Precondition of the bf16 chunked kernel for dk = dv = 128 (not checked,
+ *    documented): its state-side matrix-core products take fp16 operands (largest
+ *    finite value 65504).  Every |v| entry, and the Euclidean norm of every value column
+ *    S[:, j] of the initial state and of every state the sequence reaches, must stay
+ *    at or below 2^14 = 16384; the operands (S, v - k^T S and the corrected values) then
+ *    stay below 2^15.  Outside that range this kernel may return inf or NaN where the
+ *    fp32 token-by-token kernels stay finite.  With unit keys, beta in (0, 1) and g <= 0
+ *    a state's column norms grow by at most |beta (v - k^T S)| per token.
  *  - Padded tokens (mask == 0), and tokens of a packed batch, must hold finite values.
  */
 #ifndef KDA_H_
@@ -56,9 +64,10 @@ typedef enum {
   KDA_ERR_DTYPE = 3,        /* unknown dtype code                                           */
   KDA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned                             */
   KDA_ERR_CONFLICT = 5,     /* mutually exclusive arguments given together                  */
-  KDA_ERR_UNSUPPORTED = 6,  /* a valid combination this build has no kernel for             */
-  KDA_ERR_HIP = 7,          /* the HIP runtime reported an error at launch                  */
-  KDA_ERR_WORKSPACE = 8     /* the workspace is missing or smaller than required            */
+  KDA_ERR_WORKSPACE = 6,    /* the workspace is missing or smaller than required            */
+  KDA_ERR_UNSUPPORTED = 7,  /* a valid combination this build has no kernel for             */
+  KDA_ERR_HIP = 8,          /* the HIP runtime reported an error at launch                  */
+  KDA_ERR_TIMEOUT = 9       /* a bounded wait inside a kernel ran out (kda_chunk_prefill_status) */
 } kda_status_t;
 
 /* Problem description shared by the prefill and recurrent entry points. */
@@ -69,8 +78,11 @@ typedef struct {
   int32_t dk;            /* key_dim   (16, 32, 64 or 128)                                  */
   int32_t dv;            /* value_dim (== dk in this build)                                */
   int32_t num_seqs;      /* sequences: len(cu_seqlens)-1 with cu_seqlens, else ignored (=B) */
-  int32_t chunk;         /* prefill chunk length: 0 = kernel's choice; 32 (bf16, d = 128: the
-                            matrix-core kernel) or 16 (the vector-ALU kernel, any dtype)    */
+  int32_t chunk;         /* prefill chunk length: 0 = kernel's choice; 64 or 32 (bf16, d = 128:
+                            the matrix-core kernel, whose blocks are 32 tokens; a 64-token
+                            chunk is carried as its two halves, the same chunked form
+                            regrouped) or 16 (the vector-ALU kernel, any dtype).  The result
+                            does not depend on it beyond rounding.                          */
   float scale;           /* query scale; 0 = 1/sqrt(dk)                                    */
   int32_t use_qk_l2norm; /* 1: q, k are L2-normalised in the kernel (x / sqrt(sum x^2 + 1e-6)) */
   int32_t in_dtype;      /* kda_dtype_t of q, k, v and gate                                */
@@ -86,7 +98,7 @@ typedef struct {
  * kda_chunk_prefill -- the prompt kernel: runs the recurrence over whole sequences,
  * carrying the state from one chunk of tokens to the next without storing it per token
  * (nnterp Kimi-Linear page, Notes, "Loading", which names 64-token chunks; the chunked
- * form is exact for any chunk length, and these kernels use 32 or 16).  Results equal
+ * form is exact for any chunk length; these kernels work in blocks of 32 or 16).  Results equal
  * the token-by-token recurrence up to rounding.
  *
  *   q, k          [B, T, H, dk]   in_dtype
@@ -133,9 +145,27 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p,
  * kda_chunk_prefill_workspace_size -- bytes of workspace kda_chunk_prefill needs for
  * these params; `packed` is nonzero when cu_seqlens will be given (p->num_seqs set).
  * 0 for invalid params or when the chosen kernel needs none.  With packing it is
- * (N + ceil(T / 32)) * H * 30736 bytes, otherwise B * ceil(T / 32) * H * 30736.
+ * (N + ceil(T / 32)) * H * 30736 + 256 bytes, otherwise B * ceil(T / 32) * H * 30736 + 256
+ * (a record and the norm-exchange words per chunk and head, then a status word).
  */
 size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed);
+
+/*
+ * kda_chunk_prefill_status -- whether every wait between the two column tiles of a head
+ * in the scans run on this workspace since its last preparation completed normally.
+ * Only the scan that applies the gated norm itself (kda_chunk_scan with y, and
+ * kda_chunk_prefill with y and o == NULL) has such waits: the two work-groups of a head
+ * exchange per-token sums of squares.  A wait always ends, since partner work-groups
+ * are consecutive in one XCD's dispatch order, but it is bounded (seconds); if other work
+ * held the GPU's CUs longer than that, the wait gives up, the tokens after it get NaN in
+ * y, and the workspace's status word is set.  This call waits for `stream`, reads that
+ * word, and returns KDA_OK or KDA_ERR_TIMEOUT.  p and packed as for
+ * kda_chunk_prefill_workspace_size; workspace as given to the prefill.  Errors:
+ * KDA_ERR_NULL, KDA_ERR_WORKSPACE, KDA_ERR_UNSUPPORTED (p does not select the
+ * matrix-core kernel), KDA_ERR_HIP.  Nothing is allocated; it synchronises the stream.
+ */
+kda_status_t kda_chunk_prefill_status(const kda_params_t *p, int32_t packed, const void *workspace,
+                                      size_t workspace_bytes, void *stream);
 
 /*
  * kda_chunk_prepare, kda_chunk_scan -- the two launches of kda_chunk_prefill's bf16,
@@ -166,7 +196,7 @@ size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed);
  * Arguments have the meaning, layout and alignment given for kda_chunk_prefill; the
  * workspace is at least kda_chunk_prefill_workspace_size(p, cu_seqlens != NULL) bytes.
  * Both return KDA_ERR_UNSUPPORTED unless p selects the bf16, dk = dv = 128 kernel
- * (in_dtype bf16, chunk 0 or 32, T * H * 128 < 2^31).  Ownership: all buffers stay the
+ * (in_dtype bf16, chunk 0, 32 or 64, T * H * 128 < 2^31).  Ownership: all buffers stay the
  * caller's; nothing is allocated.  Errors: as for kda_chunk_prefill.
  */
 kda_status_t kda_chunk_prepare(const kda_params_t *p,

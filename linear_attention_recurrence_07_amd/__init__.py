@@ -25,15 +25,20 @@ from typing import Optional
 
 import torch
 
-__all__ = ["chunk_prefill", "chunk_prefill_workspace_size", "chunk_prepare", "chunk_scan", "recurrent_step",
+__all__ = ["chunk_prefill", "chunk_prefill_workspace_size", "chunk_prefill_status", "chunk_prepare", "chunk_scan",
+           "recurrent_step",
            "gated_rmsnorm", "short_conv", "gated_norm_proj", "out_proj", "library_path", "load_library", "KdaError", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
+# kda_status_t (include/kda.h)
+(KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_ALIGN, KDA_ERR_CONFLICT, KDA_ERR_WORKSPACE,
+ KDA_ERR_UNSUPPORTED, KDA_ERR_HIP, KDA_ERR_TIMEOUT) = range(10)
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_ALIGN",
-           5: "KDA_ERR_CONFLICT", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_HIP", 8: "KDA_ERR_WORKSPACE"}
+           5: "KDA_ERR_CONFLICT", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_UNSUPPORTED", 8: "KDA_ERR_HIP",
+           9: "KDA_ERR_TIMEOUT"}
 
 
 class KdaError(RuntimeError):
@@ -80,6 +85,8 @@ def load_library():
     lib.kda_chunk_prefill.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 13 + [P, ctypes.c_size_t, P]
     lib.kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_prefill_workspace_size.argtypes = [ctypes.POINTER(KdaParams), i32]
+    lib.kda_chunk_prefill_status.restype = ctypes.c_int
+    lib.kda_chunk_prefill_status.argtypes = [ctypes.POINTER(KdaParams), i32, P, ctypes.c_size_t, P]
     lib.kda_chunk_prepare.restype = ctypes.c_int
     lib.kda_chunk_prepare.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 7 + [ctypes.c_size_t, P]
     lib.kda_chunk_scan.restype = ctypes.c_int
@@ -166,6 +173,51 @@ def _check_cu_seqlens(cu: torch.Tensor, T: int) -> None:
         raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at or before T")
 
 
+def _shape(t: torch.Tensor, name: str, shape, dtype) -> torch.Tensor:
+    """A caller-supplied buffer must have exactly the shape and dtype the kernel writes or
+    reads: the library sees only its address, so a smaller buffer would be overrun."""
+    shape = tuple(int(x) for x in shape)
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _on_device(device, *named) -> None:
+    """Device, placement and contiguity checks, after every shape and dtype check."""
+    for name, t in named:
+        if t is not None:
+            _dev(t, name, device)
+
+
+def _seq_count(cu_seqlens: Optional[torch.Tensor], B: int) -> int:
+    if cu_seqlens is None:
+        return B
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a 1-D tensor of N + 1 offsets")
+    if cu_seqlens.device.type != "cpu" and cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    return cu_seqlens.numel() - 1
+
+
+def _seq_device(cu_seqlens: Optional[torch.Tensor], T: int, dev) -> Optional[torch.Tensor]:
+    if cu_seqlens is None:
+        return None
+    if cu_seqlens.device.type == "cpu":
+        _check_cu_seqlens(cu_seqlens, T)
+        return cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
+    return _dev(cu_seqlens, "cu_seqlens", dev)
+
+
+def _mask_device(attention_mask: Optional[torch.Tensor], B: int, T: int, dev) -> Optional[torch.Tensor]:
+    if attention_mask is None:
+        return None
+    if tuple(attention_mask.shape) != (B, T):
+        raise ValueError("attention_mask must be [B, T]")
+    return (attention_mask != 0).to(device=dev, dtype=torch.uint8).contiguous()
+
+
 def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                   beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None, *,
                   cu_seqlens: Optional[torch.Tensor] = None,
@@ -184,67 +236,55 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
 
     cu_seqlens ([N+1] int32; a CPU tensor is validated then copied to the GPU) packs N
     sequences into B = 1; attention_mask ([B, T], nonzero = token) marks padding.
-    workspace (a device tensor) is scratch of at least the library's reported size; one
-    is allocated per call when it is not given.
+    out, final_state and y, when given, must be [B,T,H,dv], float32 [N,H,dk,dv] and
+    [B,T,H,dv]; o and y share one dtype (out's when out is given, else output_dtype or
+    q's).  workspace (a device tensor) is scratch of at least the library's reported
+    size; one is allocated per call when it is not given.
     """
     lib = load_library()
     dev = q.device
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k must be [B,T,H,dk] and v [B,T,H,dv]")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     in_dt = q.dtype
-    out_dt = output_dtype or in_dt
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _dev(t, name, dev)
+    for name, t in (("k", k), ("v", v)):
         if t.dtype != in_dt:
             raise TypeError(f"{name} dtype {t.dtype} differs from q's {in_dt}")
     if k.shape != q.shape or v.shape[:3] != (B, T, H):
         raise ValueError("q, k must be [B,T,H,dk] and v [B,T,H,dv]")
-    _dev(g, "g", dev)
-    _dev(beta, "beta", dev)
     per_head = _decay_layout(g, B, T, H, dk)
-    if beta.dtype != torch.float32 or beta.shape != (B, T, H):
-        raise ValueError("beta must be float32 [B,T,H]")
-    cu_dev = None
-    if cu_seqlens is not None:
-        if cu_seqlens.device.type == "cpu":
-            _check_cu_seqlens(cu_seqlens, T)
-            cu_dev = cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
-        else:
-            cu_dev = _dev(cu_seqlens, "cu_seqlens", dev)
-            if cu_dev.dtype != torch.int32:
-                raise TypeError("cu_seqlens must be int32")
-        N = cu_dev.numel() - 1
-    else:
-        N = B
-    mask_dev = None
-    if attention_mask is not None:
-        if attention_mask.shape != (B, T):
-            raise ValueError("attention_mask must be [B, T]")
-        mask_dev = (attention_mask != 0).to(device=dev, dtype=torch.uint8).contiguous()
+    _shape(beta, "beta", (B, T, H), torch.float32)
+    N = _seq_count(cu_seqlens, B)
     if initial_state is not None:
-        _dev(initial_state, "initial_state", dev)
-        if initial_state.dtype != torch.float32 or initial_state.shape != (N, H, dk, dv):
-            raise ValueError(f"initial_state must be float32 [{N},{H},{dk},{dv}]")
+        _shape(initial_state, "initial_state", (N, H, dk, dv), torch.float32)
     norm = gate is not None or norm_weight is not None
     if not head_outputs and not norm:
         raise ValueError("head_outputs=False needs the gated norm (gate and norm_weight)")
+    if norm and (gate is None or norm_weight is None):
+        raise ValueError("the gated norm needs both gate and norm_weight")
+    out_dt = out.dtype if (out is not None and head_outputs) else (output_dtype or in_dt)
+    _dtype_code(out_dt)
+    if out is not None and head_outputs:
+        _shape(out, "out", (B, T, H, dv), out_dt)
+    if final_state is not None:
+        _shape(final_state, "final_state", (N, H, dk, dv), torch.float32)
+    if norm:
+        _shape(gate, "gate", (B, T, H, dv), in_dt)
+        _shape(norm_weight, "norm_weight", (dv,), torch.float32)
+        if y is not None:
+            _shape(y, "y", (B, T, H, dv), out_dt)
+    _on_device(dev, ("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("initial_state", initial_state),
+               ("out", out if head_outputs else None), ("final_state", final_state), ("gate", gate),
+               ("norm_weight", norm_weight), ("y", y if norm else None))
+    cu_dev = _seq_device(cu_seqlens, T, dev)
+    mask_dev = _mask_device(attention_mask, B, T, dev)
     o = None
     if head_outputs:
         o = out if out is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
-        _dev(o, "out", dev)
     fs = final_state if final_state is not None else torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    _dev(fs, "final_state", dev)
     if norm:
-        if gate is None or norm_weight is None:
-            raise ValueError("the gated norm needs both gate and norm_weight")
-        _dev(gate, "gate", dev)
-        _dev(norm_weight, "norm_weight", dev)
-        if gate.dtype != in_dt or gate.shape != (B, T, H, dv):
-            raise ValueError("gate must match v's shape and q's dtype")
-        if norm_weight.dtype != torch.float32 or norm_weight.shape != (dv,):
-            raise ValueError("norm_weight must be float32 [dv]")
         y = y if y is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
-        _dev(y, "y", dev)
     else:
         y = None
     p = _params(B, T, H, dk, dv, num_seqs=N if cu_dev is not None else 0, chunk=chunk, scale=scale,
@@ -272,6 +312,20 @@ def chunk_prefill_workspace_size(B: int, T: int, H: int, dk: int, dv: int, *,
     p = _params(B, T, H, dk, dv, num_seqs=num_seqs or 0, chunk=chunk, in_dtype=_dtype_code(dtype),
                 out_dtype=_dtype_code(dtype))
     return int(lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), 1 if num_seqs is not None else 0))
+
+
+def chunk_prefill_status(workspace: torch.Tensor, B: int, T: int, H: int, dk: int = 128, dv: int = 128, *,
+                         num_seqs: Optional[int] = None, dtype: torch.dtype = torch.bfloat16, chunk: int = 0) -> None:
+    """Waits for the current stream and raises KdaError (KDA_ERR_TIMEOUT) if a bounded wait
+    between the two column tiles of a head ran out in a scan that applied the gated norm
+    on this workspace (y then holds NaN after that token).  num_seqs as for
+    chunk_prefill_workspace_size."""
+    lib = load_library()
+    _dev(workspace, "workspace", workspace.device)
+    p = _params(B, T, H, dk, dv, num_seqs=num_seqs or 0, chunk=chunk, in_dtype=_dtype_code(dtype),
+                out_dtype=_dtype_code(dtype))
+    _check(lib.kda_chunk_prefill_status(ctypes.byref(p), 1 if num_seqs is not None else 0, _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(workspace.device)))
 
 
 def _packing(cu_seqlens, attention_mask, B, T, dev):
@@ -334,43 +388,44 @@ def chunk_scan(v: torch.Tensor, workspace: torch.Tensor, initial_state: Optional
     """Second launch of the bf16, d = 128 chunked prefill: the state scan over the records
     chunk_prepare wrote (same shapes and cu_seqlens).  Returns (o, final_state), or
     (o, final_state, y) with the gated norm (gate and norm_weight given); with the norm
-    and head_outputs=False, o is not written (None)."""
+    and head_outputs=False, o is not written (None).  Caller-supplied out, final_state and
+    y are checked as in chunk_prefill."""
     lib = load_library()
     dev = v.device
+    if v.dim() != 4:
+        raise ValueError("v must be [B,T,H,dv]")
     B, T, H, dv = v.shape
     dk = dv if dk is None else dk
-    _dev(v, "v", dev)
-    _dev(workspace, "workspace", dev)
-    cu_dev, _, N = _packing(cu_seqlens, None, B, T, dev)
+    N = _seq_count(cu_seqlens, B)
     if initial_state is not None:
-        _dev(initial_state, "initial_state", dev)
-        if initial_state.dtype != torch.float32 or initial_state.shape != (N, H, dk, dv):
-            raise ValueError(f"initial_state must be float32 [{N},{H},{dk},{dv}]")
-    out_dt = output_dtype or v.dtype
+        _shape(initial_state, "initial_state", (N, H, dk, dv), torch.float32)
     norm = gate is not None or norm_weight is not None
     if not head_outputs and not norm:
         raise ValueError("head_outputs=False needs the gated norm (gate and norm_weight)")
+    if norm and (gate is None or norm_weight is None):
+        raise ValueError("gate and norm_weight go together")
+    out_dt = out.dtype if (out is not None and head_outputs) else (output_dtype or v.dtype)
+    _dtype_code(out_dt)
+    if out is not None and head_outputs:
+        _shape(out, "out", (B, T, H, dv), out_dt)
+    if final_state is not None:
+        _shape(final_state, "final_state", (N, H, dk, dv), torch.float32)
+    if norm:
+        _shape(gate, "gate", (B, T, H, dv), v.dtype)
+        _shape(norm_weight, "norm_weight", (dv,), torch.float32)
+        if y is not None:
+            _shape(y, "y", (B, T, H, dv), out_dt)
+    _on_device(dev, ("v", v), ("workspace", workspace), ("initial_state", initial_state),
+               ("out", out if head_outputs else None), ("final_state", final_state), ("gate", gate),
+               ("norm_weight", norm_weight), ("y", y if norm else None))
+    cu_dev = _seq_device(cu_seqlens, T, dev)
     o = None
     if head_outputs:
         o = out if out is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
-        _dev(o, "out", dev)
-        out_dt = o.dtype
     fs = final_state if final_state is not None else torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    _dev(fs, "final_state", dev)
     yy = None
     if norm:
-        if gate is None or norm_weight is None:
-            raise ValueError("gate and norm_weight go together")
-        _dev(gate, "gate", dev)
-        _dev(norm_weight, "norm_weight", dev)
-        if gate.shape != v.shape or gate.dtype != v.dtype:
-            raise ValueError("gate must have v's shape and dtype")
-        if norm_weight.dtype != torch.float32 or norm_weight.shape != (dv,):
-            raise ValueError(f"norm_weight must be float32 [{dv}]")
         yy = y if y is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
-        _dev(yy, "y", dev)
-        if yy.dtype != out_dt:
-            raise TypeError(f"y dtype {yy.dtype} differs from the output dtype {out_dt}")
     p = _params(B, T, H, dk, dv, num_seqs=N if cu_dev is not None else 0, in_dtype=_dtype_code(v.dtype),
                 out_dtype=_dtype_code(out_dt), norm_eps=norm_eps)
     _check(lib.kda_chunk_scan(ctypes.byref(p), _ptr(v), _ptr(initial_state), _ptr(cu_dev), _ptr(workspace),
@@ -389,44 +444,43 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
                    states: Optional[torch.Tensor] = None):
     """Token-by-token step(s): advances `state` ([B,H,dk,dv] fp32) in place over the T
     tokens of q/k/v and returns o (and y with the gated norm).  With `states` (a float32
-    [B,T,H,dk,dv] tensor) the state after every token is stored there as well."""
+    [B,T,H,dk,dv] tensor) the state after every token is stored there as well.  Caller-
+    supplied out and y must be [B,T,H,dv] of one dtype (out's when out is given)."""
     lib = load_library()
     dev = q.device
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k must be [B,T,H,dk] and v [B,T,H,dv]")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     in_dt = q.dtype
-    out_dt = output_dtype or in_dt
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _dev(t, name, dev)
+    for name, t in (("k", k), ("v", v)):
         if t.dtype != in_dt:
             raise TypeError(f"{name} dtype {t.dtype} differs from q's {in_dt}")
     if k.shape != q.shape or v.shape[:3] != (B, T, H):
         raise ValueError("q, k must be [B,T,H,dk] and v [B,T,H,dv]")
-    _dev(g, "g", dev)
-    _dev(beta, "beta", dev)
     per_head = _decay_layout(g, B, T, H, dk)
-    if beta.dtype != torch.float32 or beta.shape != (B, T, H):
-        raise ValueError("beta must be float32 [B,T,H]")
-    _dev(state, "state", dev)
-    if state.dtype != torch.float32 or state.shape != (B, H, dk, dv):
-        raise ValueError("state must be float32 [B,H,dk,dv]")
-    mask_dev = None
-    if attention_mask is not None:
-        if attention_mask.shape != (B, T):
-            raise ValueError("attention_mask must be [B, T]")
-        mask_dev = (attention_mask != 0).to(device=dev, dtype=torch.uint8).contiguous()
-    o = out if out is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
-    _dev(o, "out", dev)
+    _shape(beta, "beta", (B, T, H), torch.float32)
+    _shape(state, "state", (B, H, dk, dv), torch.float32)
+    out_dt = out.dtype if out is not None else (output_dtype or in_dt)
+    _dtype_code(out_dt)
+    if out is not None:
+        _shape(out, "out", (B, T, H, dv), out_dt)
     norm = gate is not None or norm_weight is not None
     if norm:
         if gate is None or norm_weight is None:
             raise ValueError("the gated norm needs both gate and norm_weight")
-        _dev(gate, "gate", dev)
-        _dev(norm_weight, "norm_weight", dev)
-        if gate.dtype != in_dt or gate.shape != (B, T, H, dv) or norm_weight.dtype != torch.float32:
-            raise ValueError("gate must match v (q's dtype); norm_weight float32 [dv]")
+        _shape(gate, "gate", (B, T, H, dv), in_dt)
+        _shape(norm_weight, "norm_weight", (dv,), torch.float32)
+        if y is not None:
+            _shape(y, "y", (B, T, H, dv), out_dt)
+    if states is not None:
+        _shape(states, "states", (B, T, H, dk, dv), torch.float32)
+    _on_device(dev, ("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state), ("out", out),
+               ("gate", gate), ("norm_weight", norm_weight), ("y", y if norm else None), ("states", states))
+    mask_dev = _mask_device(attention_mask, B, T, dev)
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
+    if norm:
         y = y if y is not None else torch.empty((B, T, H, dv), dtype=out_dt, device=dev)
-        _dev(y, "y", dev)
     else:
         y = None
     p = _params(B, T, H, dk, dv, scale=scale, use_qk_l2norm=use_qk_l2norm_in_kernel,
@@ -437,9 +491,6 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
                                       _ptr(state), _ptr(mask_dev), _ptr(o), _ptr(gate), _ptr(norm_weight),
                                       _ptr(y), _stream(dev)))
     else:
-        _dev(states, "states", dev)
-        if states.dtype != torch.float32 or states.shape != (B, T, H, dk, dv):
-            raise ValueError(f"states must be float32 [{B},{T},{H},{dk},{dv}]")
         _check(lib.kda_recurrent_states(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                         _ptr(state), _ptr(mask_dev), _ptr(o), _ptr(gate), _ptr(norm_weight),
                                         _ptr(y), _ptr(states), _stream(dev)))
@@ -451,6 +502,8 @@ def gated_rmsnorm(x: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor, eps
     """y = weight * x / sqrt(mean(x^2) + eps) * sigmoid(gate) over the last axis."""
     lib = load_library()
     dev = x.device
+    if out is not None:
+        _shape(out, "out", x.shape, out.dtype)
     _dev(x, "x", dev)
     _dev(gate, "gate", dev)
     _dev(weight, "weight", dev)
@@ -492,6 +545,8 @@ def short_conv(x: torch.Tensor, weight: torch.Tensor, initial_state: Optional[to
         _dev(initial_state, "initial_state", dev)
         if initial_state.dtype != x.dtype or initial_state.shape != (N, W - 1, D):
             raise ValueError(f"initial_state must be {x.dtype} [{N},{W - 1},{D}]")
+    if out is not None:
+        _shape(out, "out", (B, T, D), out.dtype)
     y = out if out is not None else torch.empty((B, T, D), dtype=output_dtype or x.dtype, device=dev)
     _dev(y, "out", dev)
     fs = final_state
@@ -532,6 +587,8 @@ def out_proj(x: torch.Tensor, weight: torch.Tensor, *, output_dtype: Optional[to
     if weight.shape != (N, K):
         raise ValueError("weight must be [out_features, in_features]")
     rows = x.numel() // K if K else 0
+    if out is not None:
+        _shape(out, "out", x.shape[:-1] + (N,), out.dtype)
     res = out if out is not None else torch.empty(x.shape[:-1] + (N,), dtype=output_dtype or x.dtype, device=dev)
     _dev(res, "out", dev)
     ws, nbytes = _proj_workspace(lib, rows, K, N, dev, workspace)
@@ -563,6 +620,10 @@ def gated_norm_proj(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tens
         raise ValueError("proj_weight must be [out_features, heads * head_dim]")
     rows = o.numel() // (heads * hd)
     lead = o.shape[:-2]
+    if y is not None:
+        _shape(y, "y", lead + (heads * hd,), torch.bfloat16)
+    if out is not None:
+        _shape(out, "out", lead + (N,), out.dtype)
     yy = y if y is not None else torch.empty(lead + (heads * hd,), dtype=torch.bfloat16, device=dev)
     _dev(yy, "y", dev)
     res = out if out is not None else torch.empty(lead + (N,), dtype=output_dtype or torch.bfloat16, device=dev)

@@ -54,8 +54,8 @@ kda_status_t check_params(const kda_params_t *p, bool prefill) {
   if (!(p->norm_eps >= 0.f) || !std::isfinite(p->norm_eps)) return fail(KDA_ERR_SHAPE, "norm_eps must be finite and >= 0");
   if (p->use_qk_l2norm != 0 && p->use_qk_l2norm != 1) return fail(KDA_ERR_SHAPE, "use_qk_l2norm must be 0 or 1");
   if (p->decay_per_head != 0 && p->decay_per_head != 1) return fail(KDA_ERR_SHAPE, "decay_per_head must be 0 or 1");
-  if (prefill && p->chunk != 0 && p->chunk != 16 && p->chunk != 32)
-    return fail(KDA_ERR_UNSUPPORTED, "chunk %d not supported (0, 16 or 32)", p->chunk);
+  if (prefill && p->chunk != 0 && p->chunk != 16 && p->chunk != 32 && p->chunk != 64)
+    return fail(KDA_ERR_UNSUPPORTED, "chunk %d not supported (0, 16, 32 or 64)", p->chunk);
   // Element counts must stay addressable with 32-bit token indices times heads.
   const double toks = static_cast<double>(p->B) * p->T * p->H;
   if (toks * p->dk > 9.0e18 || static_cast<double>(p->B) * p->T > 2147483647.0)
@@ -64,10 +64,12 @@ kda_status_t check_params(const kda_params_t *p, bool prefill) {
 }
 
 // The bf16 matrix-core prefill runs when the shape and dtype allow it and the caller did
-// not ask for the 16-token vector-ALU chunks.
+// not ask for the 16-token vector-ALU chunks.  Its blocks are 32 tokens; a 64-token chunk
+// (the length the pages name) is carried as its two 32-token halves, the same chunked
+// form regrouped, so chunk 64 selects it as well.
 bool use_mfma_prefill(const kda_params_t *p) {
   return kda::prefill_mfma_supports(p->dk, p->dv, p->in_dtype == KDA_BF16) &&
-         (p->chunk == 0 || p->chunk == 32) && kda::prefill_mfma_fits(p->T, p->H);
+         (p->chunk == 0 || p->chunk == 32 || p->chunk == 64) && kda::prefill_mfma_fits(p->T, p->H);
 }
 
 size_t prefill_workspace(const kda_params_t *p, bool packed) {
@@ -123,7 +125,7 @@ kda_status_t check_layout(const kda_params_t *p, const int32_t *cu, const uint8_
 // The two stages exist only for the bf16, d = 128 matrix-core kernel.
 kda_status_t check_stage_kernel(const kda_params_t *p) {
   if (!use_mfma_prefill(p))
-    return fail(KDA_ERR_UNSUPPORTED, "the two-stage prefill needs bf16 inputs, dk = dv = 128, chunk 0 or 32 "
+    return fail(KDA_ERR_UNSUPPORTED, "the two-stage prefill needs bf16 inputs, dk = dv = 128, chunk 0, 32 or 64 "
                                      "and T * H * 128 < 2^31");
   return KDA_OK;
 }
@@ -167,8 +169,9 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
   if (!mfma) {
     if (!kda::prefill_valu_supports(p->dk, p->dv))
       return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dk=%d dv=%d", p->dk, p->dv);
-    if (chunk == 32)
-      return fail(KDA_ERR_UNSUPPORTED, "chunk 32 needs bf16 inputs with dk = dv = 128 and T * H * 128 < 2^31");
+    if (chunk == 32 || chunk == 64)
+      return fail(KDA_ERR_UNSUPPORTED, "chunk %d needs bf16 inputs with dk = dv = 128 and T * H * 128 < 2^31",
+                  chunk);
   }
   if (mfma) {
     // With o wanted, the gated norm runs as its own launch over o: the scan can apply it
@@ -198,6 +201,27 @@ size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed) {
   if (p == nullptr || check_params(p, true) != KDA_OK) return 0;
   if (packed && p->num_seqs <= 0) return 0;
   return prefill_workspace(p, packed != 0);
+}
+
+kda_status_t kda_chunk_prefill_status(const kda_params_t *p, int32_t packed, const void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  KDA_TRY(check_params(p, true));
+  if (packed && p->num_seqs <= 0) return fail(KDA_ERR_SHAPE, "num_seqs must be > 0 with packing");
+  KDA_TRY(check_stage_kernel(p));
+  const size_t need = prefill_workspace(p, packed != 0);
+  if (workspace == nullptr) return fail(KDA_ERR_NULL, "workspace is NULL");
+  if (workspace_bytes < need) return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                                          workspace_bytes);
+  KDA_TRY(check_ptr(workspace, "workspace", true));
+  const uint32_t *word = kda::chunk_status_word(workspace, p->B, p->T, p->H, packed ? p->num_seqs : p->B, packed != 0);
+  uint32_t flag = 0;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  KDA_TRY(hip_status(hipMemcpyAsync(&flag, word, sizeof flag, hipMemcpyDeviceToHost, st), "status read"));
+  KDA_TRY(hip_status(hipStreamSynchronize(st), "status read"));
+  if (flag != 0)
+    return fail(KDA_ERR_TIMEOUT, "a wait between the two column tiles of a head ran out: y holds NaN for the "
+                                 "tokens after it");
+  return KDA_OK;
 }
 
 kda_status_t kda_chunk_prepare(const kda_params_t *p, const void *q, const void *k, const float *g,
@@ -420,6 +444,7 @@ const char *kda_status_string(kda_status_t s) {
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
     case KDA_ERR_HIP: return "KDA_ERR_HIP";
     case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_TIMEOUT: return "KDA_ERR_TIMEOUT";
   }
   return "KDA_ERR_UNKNOWN";
 }

@@ -105,10 +105,11 @@ __global__ void __launch_bounds__(NT)
 chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const float *__restrict__ g, const float *__restrict__ beta,
                   const int32_t *__restrict__ cu, const uint8_t *__restrict__ mask,
-                  Rec *__restrict__ ws, uint64_t *__restrict__ xs, int T, int H, int N, float scale,
-                  int use_l2) {
+                  Rec *__restrict__ ws, uint64_t *__restrict__ xs, uint32_t *__restrict__ status, int T, int H,
+                  int N, float scale, int use_l2) {
   __shared__ Shared sh;
   const int tid = threadIdx.x, lane = tid & 63;
+  if (blockIdx.x == 0 && tid == 0) *status = 0u;   // no wait of the coming scan has run out yet
   const int m = __builtin_amdgcn_readfirstlane(tid >> 6);   // sub-block of this wave
   const int r = lane & 15, lg = lane >> 4;
 
@@ -423,12 +424,17 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
 // Workspace of the bf16 chunked prefill: one record per (slot, head), then the scan's
 // norm-exchange words, 64 per (slot, head).
 size_t chunk_prep_workspace_bytes(long long B, long long T, long long H, long long N, bool packed) {
-  return static_cast<size_t>(num_slots(B, T, N, packed) * H) * (kRecBytes + kExchangeBytes);
+  return static_cast<size_t>(num_slots(B, T, N, packed) * H) * (kRecBytes + kExchangeBytes) + kStatusBytes;
 }
 
 uint64_t *chunk_exchange_words(const void *ws, long long B, long long T, long long H, long long N, bool packed) {
   const size_t rec_bytes = static_cast<size_t>(num_slots(B, T, N, packed) * H) * kRecBytes;
   return reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(const_cast<void *>(ws)) + rec_bytes);
+}
+
+uint32_t *chunk_status_word(const void *ws, long long B, long long T, long long H, long long N, bool packed) {
+  const size_t bytes = static_cast<size_t>(num_slots(B, T, N, packed) * H) * (kRecBytes + kExchangeBytes);
+  return reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(const_cast<void *>(ws)) + bytes);
 }
 
 hipError_t launch_chunk_prep(const Args &a, void *ws, hipStream_t st) {
@@ -439,21 +445,22 @@ hipError_t launch_chunk_prep(const Args &a, void *ws, hipStream_t st) {
   const uint16_t *q = static_cast<const uint16_t *>(a.q), *k = static_cast<const uint16_t *>(a.k);
   Rec *rec = static_cast<Rec *>(ws);
   uint64_t *xs = chunk_exchange_words(ws, a.B, a.T, a.H, a.N, a.cu != nullptr);
+  uint32_t *status = chunk_status_word(ws, a.B, a.T, a.H, a.N, a.cu != nullptr);
   const dim3 grid(static_cast<unsigned>(blocks));
   if (a.g_head) {
     if (a.mask)
       hipLaunchKernelGGL((chunk_prep_kernel<true, true>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                         rec, xs, a.T, a.H, a.N, a.scale, a.use_l2);
+                         rec, xs, status, a.T, a.H, a.N, a.scale, a.use_l2);
     else
       hipLaunchKernelGGL((chunk_prep_kernel<false, true>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                         rec, xs, a.T, a.H, a.N, a.scale, a.use_l2);
+                         rec, xs, status, a.T, a.H, a.N, a.scale, a.use_l2);
   } else {
     if (a.mask)
       hipLaunchKernelGGL((chunk_prep_kernel<true, false>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                         rec, xs, a.T, a.H, a.N, a.scale, a.use_l2);
+                         rec, xs, status, a.T, a.H, a.N, a.scale, a.use_l2);
     else
       hipLaunchKernelGGL((chunk_prep_kernel<false, false>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                         rec, xs, a.T, a.H, a.N, a.scale, a.use_l2);
+                         rec, xs, status, a.T, a.H, a.N, a.scale, a.use_l2);
   }
   return hipGetLastError();
 }

@@ -36,11 +36,16 @@
 // c+4 passes the sums to the helpers through LDS; the helpers write y of chunk c at step
 // c+5.  The compute waves issue no other global loads, so waiting for that read never
 // waits for the helpers' prefetches.  The tiles therefore do not wait on each other in
-// lockstep; the output tiles of the last six chunks stay in LDS.  A wait is bounded, and
-// a word that never arrives gives a NaN output instead of a hang.  The reader clears each
+// lockstep; the output tiles of the last six chunks stay in LDS.  The reader clears each
 // word after use, and the preparation kernel clears them all, so no call sees another
-// call's words.  The two tiles of a head are consecutive work-groups of one XCD's
-// dispatch order, so a tile never waits for a partner that cannot start.
+// call's words.
+// Forward progress: the two tiles of a head are consecutive work-groups of one XCD's
+// dispatch order (work-groups are dealt to the XCDs round-robin and each XCD starts its
+// own in id order), and a tile waits only for its partner.  So at most one work-group
+// per XCD can wait for a partner that has not started, and the others finish and free
+// their CUs; a wait can last long only while other work holds the CUs.  A wait is still
+// bounded (about 2^22 polls, seconds): one that runs out gives NaN in y instead of a
+// hang and sets the workspace's status word, which kda_chunk_prefill_status reports.
 //
 // Precision: fp16 operands for the state, the decayed keys/queries and V - K S0; W and U
 // as fp16 hi + lo parts; fp32 accumulation.  The fp16 state operand limits |S| to well
@@ -61,7 +66,7 @@ constexpr int NHT = NT - NCW * 64;  // helper threads (256)
 constexpr int LDV = DVT + 8;      // value tile row stride (bf16)
 constexpr int LDO = DVT + 4;      // fp32 output tile row stride
 constexpr int REC_PIECES = static_cast<int>(sizeof(Rec) / 16);
-constexpr int kSpinLimit = 1 << 18;   // polls of a partner's word before giving up (~0.3 s)
+constexpr int kSpinLimit = 1 << 22;   // polls of a partner's word before giving up (several seconds)
 
 constexpr int PPT = (REC_PIECES + NHT - 1) / NHT;   // record pieces per helper thread (8)
 static_assert(NCW == 4 && NHT == 256, "thread mappings");
@@ -88,7 +93,7 @@ __global__ void __launch_bounds__(NT, 1)
 chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, const float *init,
                   float *fin, const int32_t *__restrict__ cu, TOut *__restrict__ o,
                   const uint16_t *__restrict__ gate, const float *__restrict__ norm_w, TOut *__restrict__ y,
-                  uint64_t *xs, float eps, int T, int H, int units) {
+                  uint64_t *xs, uint32_t *status, float eps, int T, int H, int units) {
   constexpr int NOST = NORM ? kNormLag + 1 : 2;
   __shared__ Smem<NOST> sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -211,6 +216,7 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
   auto partner = [&](int cidx, int tok, uint64_t w) -> float {
     for (int n = 0; (w >> 32) != 1u; ++n) {
       if (lost || n == kSpinLimit) {
+        if (!lost) __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         lost = true;
         return __builtin_nanf("");
       }
@@ -462,26 +468,27 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
 }
 
 template <typename TOut, bool HAS_INIT, bool NORM, bool WRITE_O>
-hipError_t launch3(const Args &a, const void *ws, uint64_t *xs, hipStream_t st) {
+hipError_t launch3(const Args &a, const void *ws, uint64_t *xs, uint32_t *status, hipStream_t st) {
   static_assert(WRITE_O || NORM, "without the norm the head outputs are the only output");
   const int units = a.N * a.H;
   const unsigned grid = static_cast<unsigned>((units + 7) / 8) * 8 * NTILE;
   hipLaunchKernelGGL((chunk_scan_kernel<TOut, HAS_INIT, NORM, WRITE_O>), dim3(grid), dim3(NT), 0, st,
                      static_cast<const uint16_t *>(a.v), static_cast<const Rec *>(ws), a.init, a.state, a.cu,
                      static_cast<TOut *>(a.o), static_cast<const uint16_t *>(a.gate), a.norm_w,
-                     static_cast<TOut *>(a.y), xs, a.eps, a.T, a.H, units);
+                     static_cast<TOut *>(a.y), xs, status, a.eps, a.T, a.H, units);
   return hipGetLastError();
 }
 
 template <typename TOut, bool HAS_INIT>
-hipError_t launch2(const Args &a, const void *ws, uint64_t *xs, hipStream_t st) {
-  if (!a.y) return launch3<TOut, HAS_INIT, false, true>(a, ws, xs, st);
-  return a.o ? launch3<TOut, HAS_INIT, true, true>(a, ws, xs, st) : launch3<TOut, HAS_INIT, true, false>(a, ws, xs, st);
+hipError_t launch2(const Args &a, const void *ws, uint64_t *xs, uint32_t *status, hipStream_t st) {
+  if (!a.y) return launch3<TOut, HAS_INIT, false, true>(a, ws, xs, status, st);
+  return a.o ? launch3<TOut, HAS_INIT, true, true>(a, ws, xs, status, st)
+             : launch3<TOut, HAS_INIT, true, false>(a, ws, xs, status, st);
 }
 
 template <typename TOut>
-hipError_t launch1(const Args &a, const void *ws, uint64_t *xs, hipStream_t st) {
-  return a.init ? launch2<TOut, true>(a, ws, xs, st) : launch2<TOut, false>(a, ws, xs, st);
+hipError_t launch1(const Args &a, const void *ws, uint64_t *xs, uint32_t *status, hipStream_t st) {
+  return a.init ? launch2<TOut, true>(a, ws, xs, status, st) : launch2<TOut, false>(a, ws, xs, status, st);
 }
 
 }  // namespace
@@ -494,7 +501,8 @@ bool prefill_mfma_fits(long long T, long long H) { return T * H * DK < (1LL << 3
 hipError_t launch_chunk_scan(const Args &a, const void *ws, hipStream_t st) {
   if (a.N * static_cast<long long>(a.H) <= 0) return hipSuccess;
   uint64_t *xs = chunk_exchange_words(ws, a.B, a.T, a.H, a.N, a.cu != nullptr);
-  return a.out_bf16 ? launch1<uint16_t>(a, ws, xs, st) : launch1<float>(a, ws, xs, st);
+  uint32_t *status = chunk_status_word(ws, a.B, a.T, a.H, a.N, a.cu != nullptr);
+  return a.out_bf16 ? launch1<uint16_t>(a, ws, xs, status, st) : launch1<float>(a, ws, xs, status, st);
 }
 
 }  // namespace kda

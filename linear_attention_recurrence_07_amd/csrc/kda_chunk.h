@@ -54,6 +54,9 @@ constexpr size_t kRecBytes = sizeof(Rec);
 // Per (slot, head): the scan's gated-norm exchange, 2 tiles x 32 tokens of 64-bit words,
 // stored after all records.
 constexpr size_t kExchangeBytes = 2 * 32 * 8;
+// After the exchange words: one 32-bit status word (in a 256-byte tail), set when a
+// bounded wait between the two tiles of a head ran out; cleared by the preparation.
+constexpr size_t kStatusBytes = 256;
 // K index (0..31) of slot e (0..7) of lane group lg, and the inverse.
 __host__ __device__ constexpr int kidx(int lg, int e) { return (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4); }
 __host__ __device__ constexpr int kidx_lg(int x) { return (x & 15) >> 2; }

@@ -53,6 +53,7 @@ hipError_t launch_prefill_valu(const Args &a, hipStream_t s);
 // (slot, head) into ws), then the state scan that reads them.
 size_t chunk_prep_workspace_bytes(long long B, long long T, long long H, long long N, bool packed);
 uint64_t *chunk_exchange_words(const void *ws, long long B, long long T, long long H, long long N, bool packed);
+uint32_t *chunk_status_word(const void *ws, long long B, long long T, long long H, long long N, bool packed);
 hipError_t launch_chunk_prep(const Args &a, void *ws, hipStream_t s);
 // With a.y set the scan also applies the gated norm (a.gate, a.norm_w, a.eps).
 hipError_t launch_chunk_scan(const Args &a, const void *ws, hipStream_t s);

@@ -6,9 +6,9 @@ What is computed, and where the pages fix it
   family-module docstring (section 04): KDA is a gated DeltaNet whose log decay g is
   per key channel, [batch, seq, heads, key_dim], float32 and non-positive; the state is
   [batch, heads, key_dim, value_dim]; the state decays channel by channel before each
-  delta-rule update; betas [batch, seq, heads] are already sigmoids; queries and keys
-  reach the kernel before their L2 norm, which the kernel applies, and the queries
-  before the 1/sqrt(key_dim) scale.
+  delta-rule update; betas [batch, seq, heads] arrive already squashed into (0, 1); the
+  kernel itself L2-normalises queries and keys (the values the page tabulates are
+  un-normalised), and it also applies the 1/sqrt(key_dim) query scale.
 * Same page, section 02 (support() table): state_input is None at the start of a
   prompt; state_output is the state leaving the layer; head outputs are taken before
   the gated norm.
@@ -139,8 +139,8 @@ def kda_chunked(q, k, v, g, beta, initial_state=None, *, chunk: int = 64,
                 scale: Optional[float] = None, use_qk_l2norm: bool = True,
                 l2_eps: float = L2_EPS, mask=None, cu_seqlens=None):
     """The same recurrence evaluated chunk by chunk (fp64), used only to check the chunked
-    algebra that a blocked kernel relies on.  The pages say the prompt kernel carries the
-    state from one 64-token chunk to the next without holding it per token (nnterp
+    algebra that a blocked kernel relies on.  The prompt kernel works in 64-token blocks
+    and passes only the state between them, never a per-token state (nnterp
     Kimi-Linear page, Notes, "Loading").  Within one chunk, with S0 the incoming state,
     G_r the running sum of g over the chunk up to token r (inclusive), and the
     normalised k_s, q_r:

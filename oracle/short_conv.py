@@ -8,9 +8,9 @@ What is computed, and where the pages fix it
   (4 in config.json, linear_attn_config) with activation 'silu'.
 * nnterp Kimi-Linear page, the printed module tree: the convolution is a Conv1d with
   groups equal to the channel count (one filter per channel), kernel_size 4, padding 3,
-  no bias; and the Notes on KDA: a width-4 convolution runs over the projected queries,
-  keys and values before the delta rule, so the mixer also carries its last input
-  tokens outside the recurrent state.
+  no bias; and the Notes on KDA: the convolution sits between the projections and the
+  delta rule, so besides the recurrent state the layer has to keep a few of its most
+  recent input tokens between calls.
 
 Per channel c, with W the width and w[c, 0..W-1] its taps, a token t of a sequence gives
     z_t[c] = sum_{j=0}^{W-1} w[c, j] * x_{t-(W-1)+j}[c]          (Conv1d correlation order,

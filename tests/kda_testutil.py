@@ -50,7 +50,8 @@ def device_inputs(x: gi.KdaInputs, device="cuda:0") -> dict:
 
 
 def run_prefill(x: gi.KdaInputs, device="cuda:0", *, norm: Optional[bool] = None, chunk: int = 0,
-                initial_state=None, output_dtype=torch.float32, heads: Optional[Sequence[int]] = None):
+                initial_state=None, output_dtype=torch.float32, heads: Optional[Sequence[int]] = None,
+                scale: Optional[float] = None, use_l2: bool = True, keep_on_device: bool = False):
     """Run kda_chunk_prefill; returns numpy fp64 (o, final_state, y or None), restricted to
     `heads` (selected on the GPU before the copy) when given.
 
@@ -66,10 +67,13 @@ def run_prefill(x: gi.KdaInputs, device="cuda:0", *, norm: Optional[bool] = None
                             cu_seqlens=d["cu_seqlens"], attention_mask=d["mask"],
                             gate=d["gate"] if norm else None,
                             norm_weight=d["norm_weight"] if norm else None,
-                            norm_eps=x.norm_eps, chunk=chunk, output_dtype=output_dtype)
+                            norm_eps=x.norm_eps, chunk=chunk, output_dtype=output_dtype, scale=scale,
+                            use_qk_l2norm_in_kernel=use_l2)
     torch.cuda.synchronize(device)
     o, fs = res[0], res[1]
     y = res[2] if norm else None
+    if keep_on_device:
+        return o, fs, y
     if heads is not None:
         idx = torch.tensor(list(heads), device=device)
         o, fs = o.index_select(2, idx), fs.index_select(1, idx)
@@ -78,12 +82,13 @@ def run_prefill(x: gi.KdaInputs, device="cuda:0", *, norm: Optional[bool] = None
 
 
 def oracle(x: gi.KdaInputs, heads: Optional[Sequence[int]] = None, *, norm: Optional[bool] = None,
-           initial_state=None):
+           initial_state=None, scale: Optional[float] = None, use_l2: bool = True):
     """C fp64 oracle on the same inputs (optionally a subset of heads); returns
     (o [B,T,nh,dv], final [N,nh,dk,dv], y or None)."""
     init = x.initial_state if initial_state is None else initial_state
     o, fs = cref.recurrence(x.q, x.k, x.v, x.g, x.beta, init, in_dtype=x.in_dtype,
-                            mask=x.mask, cu_seqlens=x.cu_seqlens, heads=heads)
+                            mask=x.mask, cu_seqlens=x.cu_seqlens, heads=heads, scale=scale,
+                            use_qk_l2norm=use_l2)
     norm = (x.gate is not None) if norm is None else norm
     y = None
     if norm:

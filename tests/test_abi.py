@@ -66,6 +66,7 @@ def _p(**kw):
 
 A = ctypes.c_void_p(1 << 20)          # a 16-byte-aligned stand-in address; never dereferenced
 MIS = ctypes.c_void_p((1 << 20) + 4)  # misaligned
+WS, UNSUP = K.KDA_ERR_WORKSPACE, K.KDA_ERR_UNSUPPORTED
 
 
 def _prefill(p, ws=None, ws_bytes=0, **ptrs):
@@ -85,7 +86,7 @@ def test_prefill_validation_codes():
     assert _prefill(_p(), q=None) == 1
     assert _prefill(_p(), o=None) == 1
     # o may be NULL when y is wanted: these get past the o check and stop at a later one
-    assert _prefill(_p(), o=None, gate=A, w=A, y=A) == 8                   # the workspace check
+    assert _prefill(_p(), o=None, gate=A, w=A, y=A) == WS                   # the workspace check
     assert _prefill(_p(chunk=16), o=None, gate=A, w=A, y=MIS) == 4         # y's alignment
     assert _prefill(_p(B=0)) == 2
     assert _prefill(_p(T=-1)) == 2
@@ -94,10 +95,12 @@ def test_prefill_validation_codes():
     assert _prefill(_p(B=1, num_seqs=1), cu=A, mask=A) == 5
     assert _prefill(_p(B=2, num_seqs=2), cu=A) == 5
     assert _prefill(_p(), gate=A) == 5                       # gate without weight and y
-    assert _prefill(_p(chunk=64)) == 6
-    assert _prefill(_p(dk=96, dv=96)) == 6
-    assert _prefill(_p(dk=16, dv=16, chunk=32)) == 6         # 32-token chunks only on the MFMA path
-    assert _prefill(_p(in_dtype=0, chunk=32)) == 6
+    assert _prefill(_p(chunk=64)) == WS                      # 64-token chunks: the matrix-core kernel (needs the workspace)
+    assert _prefill(_p(chunk=48)) == UNSUP
+    assert _prefill(_p(dk=16, dv=16, chunk=64)) == UNSUP     # 32/64-token chunks only on the MFMA path
+    assert _prefill(_p(dk=96, dv=96)) == UNSUP
+    assert _prefill(_p(dk=16, dv=16, chunk=32)) == UNSUP         # 32-token chunks only on the MFMA path
+    assert _prefill(_p(in_dtype=0, chunk=32)) == UNSUP
     assert _prefill(_p(scale=float("nan"))) == 2
     bad = _p()
     bad.decay_per_head = 2
@@ -110,19 +113,21 @@ def test_prefill_workspace_size_and_checks():
     lib = K.load_library()
     size = lambda p, packed=0: lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), packed)
     rec = 30224 + 512                                      # bytes per (chunk, head): record + norm exchange
-    assert size(_p(B=1, T=64, H=2)) == 1 * 2 * 2 * rec      # B * ceil(T/32) * H records
-    assert size(_p(B=3, T=65, H=2)) == 3 * 3 * 2 * rec
-    assert size(_p(B=1, T=64, H=2, num_seqs=3), 1) == (3 + 2) * 2 * rec   # (N + ceil(T/32)) * H
+    tail = 256                                             # the status word of the partner waits
+    assert size(_p(B=1, T=64, H=2)) == 1 * 2 * 2 * rec + tail   # B * ceil(T/32) * H records
+    assert size(_p(B=3, T=65, H=2)) == 3 * 3 * 2 * rec + tail
+    assert size(_p(B=1, T=64, H=2, num_seqs=3), 1) == (3 + 2) * 2 * rec + tail   # (N + ceil(T/32)) * H
     assert size(_p(B=1, T=64, H=2), 1) == 0                 # packed without num_seqs: invalid
     assert size(_p(chunk=16)) == 0                          # vector-ALU kernel: no workspace
+    assert size(_p(chunk=64)) == size(_p(chunk=32)) == size(_p())   # 64-token chunks run as two 32-token halves
     assert size(_p(dk=64, dv=64)) == 0
     assert size(_p(in_dtype=0)) == 0
     assert lib.kda_chunk_prefill_workspace_size(None, 0) == 0
     need = size(_p())
-    assert _prefill(_p()) == 8                              # missing workspace
-    assert _prefill(_p(), ws=A, ws_bytes=need - 1) == 8     # too small
+    assert _prefill(_p()) == WS                              # missing workspace
+    assert _prefill(_p(), ws=A, ws_bytes=need - 1) == WS     # too small
     assert _prefill(_p(), ws=MIS, ws_bytes=need) == 4       # misaligned
-    assert lib.kda_status_string(8) == b"KDA_ERR_WORKSPACE"
+    assert lib.kda_status_string(WS) == b"KDA_ERR_WORKSPACE"
 
 
 def test_stage_validation_codes():
@@ -144,11 +149,11 @@ def test_stage_validation_codes():
     for f in (prep, scan):
         assert f(None) == 1
         assert f(_p(B=0)) == 2
-        assert f(_p(in_dtype=0)) == 6                       # fp32: no two-stage kernel
-        assert f(_p(chunk=16)) == 6
-        assert f(_p(dk=64, dv=64)) == 6
-        assert f(_p(), ws=None, nbytes=0) == 8
-        assert f(_p(), nbytes=need - 1) == 8
+        assert f(_p(in_dtype=0)) == UNSUP                       # fp32: no two-stage kernel
+        assert f(_p(chunk=16)) == UNSUP
+        assert f(_p(dk=64, dv=64)) == UNSUP
+        assert f(_p(), ws=None, nbytes=0) == WS
+        assert f(_p(), nbytes=need - 1) == WS
         assert f(_p(), ws=MIS) == 4
         assert f(_p(B=2, num_seqs=2), cu=A) == 5
     assert prep(_p(), q=None) == 1
@@ -157,7 +162,7 @@ def test_stage_validation_codes():
     assert scan(_p(), v=None) == 1
     assert scan(_p(), fs=None) == 1
     assert scan(_p(), o=None) == 1                          # o is required without y
-    assert scan(_p(), o=None, gate=A, w=A, y=A, nbytes=need - 1) == 8   # ... and optional with it
+    assert scan(_p(), o=None, gate=A, w=A, y=A, nbytes=need - 1) == WS   # ... and optional with it
     assert scan(_p(), init=MIS) == 4
     assert scan(_p(), y=A) == 5                             # gate, norm_weight, y: all or none
     assert scan(_p(), gate=A, w=A) == 5
@@ -175,7 +180,7 @@ def test_recurrent_and_norm_validation_codes():
 
     assert rec(_p(), state=None) == 1
     assert rec(_p(), o=None, gate=A, w=A, y=A) == 1           # o is required here, even with y
-    assert rec(_p(dk=128, dv=64)) == 6
+    assert rec(_p(dk=128, dv=64)) == UNSUP
     assert rec(_p(), y=A) == 5
     assert rec(_p(), g=MIS) == 4
     assert rec(_p(T=0)) == 0                                  # nothing to do, nothing launched
@@ -189,9 +194,9 @@ def test_recurrent_and_norm_validation_codes():
     assert rec_states(_p(), states=None) == 1
     assert rec_states(_p(), states=MIS) == 4
     assert rec_states(_p(), state=None) == 1
-    assert rec_states(_p(dk=128, dv=64)) == 6
+    assert rec_states(_p(dk=128, dv=64)) == UNSUP
     norm = lib.kda_gated_rmsnorm
-    assert norm(A, A, A, A, 10, 100, 1e-6, 1, 1, None) == 6
+    assert norm(A, A, A, A, 10, 100, 1e-6, 1, 1, None) == UNSUP
     assert norm(A, A, A, A, -1, 128, 1e-6, 1, 1, None) == 2
     assert norm(None, A, A, A, 10, 128, 1e-6, 1, 1, None) == 1
     assert norm(A, A, A, A, 10, 128, 1e-6, 5, 1, None) == 3
@@ -239,10 +244,10 @@ def test_conv_validation_codes():
     assert conv(cu=A, mask=A, N=1) == 5
     assert conv(B=2, cu=A, N=2) == 5
     assert conv(y=A) == 5                                    # y overlapping x
-    assert conv(D=60) == 6
-    assert conv(W=5) == 6
-    assert conv(W=1) == 6
-    assert conv(B=70000) == 6
+    assert conv(D=60) == UNSUP
+    assert conv(W=5) == UNSUP
+    assert conv(W=1) == UNSUP
+    assert conv(B=70000) == UNSUP
     assert conv(cu=A, N=0) == 2
 
 
@@ -264,9 +269,9 @@ def test_out_proj_validation_codes():
     assert op(K=0) == 2
     assert op(dt=9) == 3
     assert op(x=MIS) == 4
-    assert op(K=300) == 6                                    # in_features % 256
-    assert op(N=96) == 6                                     # out_features % 64
-    assert op(K=1024) == 8                                   # split K needs the workspace
+    assert op(K=300) == UNSUP                                    # in_features % 256
+    assert op(N=96) == UNSUP                                     # out_features % 64
+    assert op(K=1024) == WS                                   # split K needs the workspace
     assert op(K=1024, wsp=MIS, nb=ws(64, 1024, 64)) == 4
     assert op(rows=0) == 0                                   # no rows: nothing launched
 
@@ -277,11 +282,22 @@ def test_out_proj_validation_codes():
     assert gp(y=None) == 1
     assert gp(heads=0) == 2
     assert gp(eps=-1.0) == 2
-    assert gp(hd=100) == 6                                   # head_dim not a power of two
-    assert gp(heads=3, hd=64) == 6                           # heads * head_dim % 256
-    assert gp(N=7000) == 6                                   # out_features % 64
+    assert gp(hd=100) == UNSUP                                   # head_dim not a power of two
+    assert gp(heads=3, hd=64) == UNSUP                           # heads * head_dim % 256
+    assert gp(N=7000) == UNSUP                                   # out_features % 64
     assert gp(gate=MIS) == 4
-    assert gp() == 8                                         # the decode shape needs the workspace
+    assert gp() == WS                                         # the decode shape needs the workspace
+
+
+def test_status_codes_match_the_boundary_table():
+    """kda_status_t keeps the numbering of the boundary's status table (NULL 1 .. HIP 8);
+    the timeout of a bounded wait comes after it."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    got = {n: int(v) for n, v in re.findall(r"\b(KDA_(?:OK|ERR_[A-Z]+))\s*=\s*(\d+)", text)}
+    assert got == {"KDA_OK": 0, "KDA_ERR_NULL": 1, "KDA_ERR_SHAPE": 2, "KDA_ERR_DTYPE": 3, "KDA_ERR_ALIGN": 4,
+                   "KDA_ERR_CONFLICT": 5, "KDA_ERR_WORKSPACE": 6, "KDA_ERR_UNSUPPORTED": 7, "KDA_ERR_HIP": 8,
+                   "KDA_ERR_TIMEOUT": 9}
+    assert {K._STATUS[v]: v for v in K._STATUS} == got
 
 
 def test_status_strings_and_version():
@@ -296,3 +312,61 @@ def test_binding_rejects_cpu_tensors():
     t = torch.zeros((1, 4, 2, 16), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         K.chunk_prefill(t, t, t, t.float(), torch.zeros((1, 4, 2)))
+
+
+def test_binding_checks_caller_buffers_before_any_launch():
+    """Caller-supplied outputs are checked for shape and dtype on the host: the library
+    only sees addresses, so a short or narrower buffer would be written past its end.
+    With CPU tensors every call stops either at such a check or at the device check."""
+    import torch
+    B, T, H, d = 1, 4, 2, 16
+    bf, f32 = torch.bfloat16, torch.float32
+    q = torch.zeros((B, T, H, d), dtype=bf)
+    g = torch.zeros((B, T, H, d))
+    beta = torch.zeros((B, T, H))
+    gate, w = torch.zeros((B, T, H, d), dtype=bf), torch.ones(d)
+    with pytest.raises(ValueError, match="out must have shape"):
+        K.chunk_prefill(q, q, q, g, beta, out=torch.zeros((B, T, H, d // 2), dtype=bf))
+    with pytest.raises(TypeError, match="y must be"):          # o and y share out's dtype
+        K.chunk_prefill(q, q, q, g, beta, gate=gate, norm_weight=w, out=torch.zeros((B, T, H, d), dtype=bf),
+                        y=torch.zeros((B, T, H, d), dtype=f32), output_dtype=f32)
+    with pytest.raises(ValueError, match="final_state must have shape"):   # one slab per packed sequence
+        K.chunk_prefill(q, q, q, g, beta, cu_seqlens=torch.tensor([0, 2, 4], dtype=torch.int32),
+                        final_state=torch.zeros((1, H, d, d)))
+    with pytest.raises(TypeError, match="final_state must be"):
+        K.chunk_prefill(q, q, q, g, beta, final_state=torch.zeros((B, H, d, d), dtype=bf))
+    with pytest.raises(ValueError, match="initial_state must have shape"):
+        K.chunk_prefill(q, q, q, g, beta, torch.zeros((2, H, d, d)))
+    with pytest.raises(ValueError, match="must be a GPU tensor"):          # all shapes right: device check
+        K.chunk_prefill(q, q, q, g, beta, out=torch.zeros((B, T, H, d), dtype=f32),
+                        final_state=torch.zeros((B, H, d, d)))
+    with pytest.raises(ValueError, match="out must have shape"):
+        K.chunk_scan(q, torch.zeros(16, dtype=torch.uint8), out=torch.zeros((B, T, H + 1, d), dtype=bf))
+    with pytest.raises(TypeError, match="y must be"):
+        K.chunk_scan(q, torch.zeros(16, dtype=torch.uint8), gate=gate, norm_weight=w, output_dtype=f32,
+                     y=torch.zeros((B, T, H, d), dtype=bf))
+    st = torch.zeros((B, H, d, d))
+    with pytest.raises(ValueError, match="out must have shape"):
+        K.recurrent_step(q, q, q, g, beta, st, out=torch.zeros((B, T - 1, H, d), dtype=bf))
+    with pytest.raises(ValueError, match="states must have shape"):
+        K.recurrent_step(q, q, q, g, beta, st, states=torch.zeros((B, T, H, d, d // 2)))
+    with pytest.raises(TypeError, match="state must be"):
+        K.recurrent_step(q, q, q, g, beta, st.to(bf))
+    with pytest.raises(ValueError, match="out must have shape"):
+        K.gated_rmsnorm(q, gate, w, out=torch.zeros((B, T, H, d + 8), dtype=bf))
+
+
+def test_prefill_status_validation():
+    """kda_chunk_prefill_status fails host validation before it touches the stream or the
+    workspace (stand-in pointers are never read here)."""
+    lib = K.load_library()
+    st = lambda p, packed=0, ws=A, nbytes=1 << 30: lib.kda_chunk_prefill_status(
+        None if p is None else ctypes.byref(p), packed, ws, nbytes, None)
+    need = lib.kda_chunk_prefill_workspace_size(ctypes.byref(_p()), 0)
+    assert st(None) == 1
+    assert st(_p(), ws=None) == 1
+    assert st(_p(), nbytes=need - 1) == WS
+    assert st(_p(), ws=MIS) == 4
+    assert st(_p(in_dtype=0)) == UNSUP
+    assert st(_p(chunk=16)) == UNSUP
+    assert st(_p(), packed=1) == 2                         # packed without num_seqs

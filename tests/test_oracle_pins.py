@@ -388,3 +388,47 @@ def test_per_token_states_are_the_final_states_of_the_prefixes():
     np.testing.assert_array_equal(states[1, 3], states[1, 2])
     np.testing.assert_array_equal(states[:, -1], fin)
 
+
+
+# ----------------------------------------------------------------- the parity measure
+def test_rel_err_hand_values():
+    """rel_err is max|got - ref| / rms(ref): hand-computed cases that tell apart the
+    plausible slips (rms of got instead of ref, a mean instead of the max, a signed
+    difference)."""
+    # max|diff| = 2, rms(ref) = sqrt((1 + 16) / 2) = sqrt(8.5)
+    assert R.rel_err([1.0, 2.0], [1.0, 4.0]) == pytest.approx(2.0 / np.sqrt(8.5), rel=1e-15)
+    # the arguments are not symmetric: rms of the second one, sqrt((1 + 4) / 2)
+    assert R.rel_err([1.0, 4.0], [1.0, 2.0]) == pytest.approx(2.0 / np.sqrt(2.5), rel=1e-15)
+    # one error of 3 among 100 entries of a unit reference: the max (3), not the mean (0.03)
+    got = np.ones(100)
+    got[7] = 4.0
+    assert R.rel_err(got, np.ones(100)) == pytest.approx(3.0, rel=1e-15)
+    # absolute difference: a sign flip of a unit entry is an error of 2
+    assert R.rel_err([-1.0], [1.0]) == pytest.approx(2.0, rel=1e-15)
+    # an all-zero reference falls back to the absolute max error
+    assert R.rel_err([0.5, -0.25], [0.0, 0.0]) == 0.5
+    # shapes are flattened alike: a [2, 2] pair gives the same value as its flattening
+    a, b = np.array([[1.0, 2.0], [3.0, 4.0]]), np.array([[1.0, 2.5], [3.0, 3.0]])
+    assert R.rel_err(a, b) == pytest.approx(1.0 / np.sqrt((1 + 6.25 + 9 + 9) / 4), rel=1e-15)
+
+
+def test_c_oracle_norm_flag_and_scale_match_numpy():
+    """The C oracle's in-kernel L2 norm switch and query scale on raw (not unit) q and k,
+    against the numpy recurrence whose normalisation is pinned above."""
+    rng = np.random.default_rng(21)
+    B, T, H, d = 1, 24, 3, 16
+    q = (rng.standard_normal((B, T, H, d)) * np.array([0.05, 1.0, 40.0])[None, None, :, None]).astype(np.float32)
+    k = (rng.standard_normal((B, T, H, d)) * np.array([40.0, 0.05, 1.0])[None, None, :, None]).astype(np.float32)
+    v = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    g = rng.uniform(-5.0, 0.0, (B, T, H, d)).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
+    for use_l2, scale in ((True, None), (True, 0.3), (False, 0.3)):
+        qq, kk = (q, k) if use_l2 else (R.l2_normalize(q), R.l2_normalize(k))
+        o, s = R.kda_recurrence(qq, kk, v, g, beta, scale=scale, use_qk_l2norm=use_l2)
+        oc, sc = cref.recurrence(np.asarray(qq, np.float32), np.asarray(kk, np.float32), v, g, beta,
+                                 in_dtype="f32", scale=scale, use_qk_l2norm=use_l2)
+        assert R.rel_err(oc, o) < 1e-6 and R.rel_err(sc, s) < 1e-6
+    # the norm matters on these inputs: skipping it changes the result by O(1)
+    o_norm, _ = R.kda_recurrence(q, k, v, g, beta)
+    o_raw, _ = R.kda_recurrence(q, k, v, g, beta, use_qk_l2norm=False)
+    assert not np.all(np.isfinite(o_raw)) or R.rel_err(o_raw, o_norm) > 1.0
