@@ -329,6 +329,25 @@ kda_status_t kda_gated_norm_proj(const void *o, const void *gate, const float *n
                                  void *stream);
 
 /*
+ * kda_gated_norm_proj_noalloc -- kda_gated_norm_proj without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The split-K partial sums go to a
+ * static device array of the library (16 MiB per GPU, held until the process ends), so
+ * the call allocates nothing and needs no workspace; the caller still provides every
+ * input and output.  Arguments, layout and the other errors as kda_gated_norm_proj.
+ * Limit: the partials take 4 * S * rows * out_features bytes (S = 4 K slices for
+ * rows <= 64 and heads * head_dim a multiple of 1024, S = 2 for a multiple of 512, no
+ * partials otherwise); a call that needs more than 16 MiB returns KDA_ERR_WORKSPACE
+ * (the decode exit, 64 rows x 7,168 features, needs 7.3 MB).  Every call on one GPU
+ * shares that GPU's array, which keeps the last call's partials: calls that overlap in
+ * time on one GPU (other streams, other threads) race and must not be issued.
+ */
+kda_status_t kda_gated_norm_proj_noalloc(const void *o, const void *gate, const float *norm_weight,
+                                         const void *proj_weight, void *y, void *out, int64_t rows,
+                                         int32_t heads, int32_t head_dim, int32_t out_features, float eps,
+                                         int32_t out_dtype, void *stream);
+
+/*
  * kda_out_proj -- the output projection alone: out[rows, out_features] = x W^T with
  * x [rows, in_features] bf16 and W [out_features, in_features] bf16 (Linear layout, no
  * bias), fp32 accumulation, out in out_dtype.  in_features a multiple of 256,

@@ -27,7 +27,7 @@ import torch
 
 __all__ = ["chunk_prefill", "chunk_prefill_workspace_size", "chunk_prefill_status", "chunk_prepare", "chunk_scan",
            "recurrent_step",
-           "gated_rmsnorm", "short_conv", "gated_norm_proj", "out_proj", "library_path", "load_library", "KdaError", "version"]
+           "gated_rmsnorm", "short_conv", "gated_norm_proj", "gated_norm_proj_noalloc", "out_proj", "library_path", "load_library", "KdaError", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
@@ -93,6 +93,8 @@ def load_library():
     lib.kda_chunk_scan.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 4 + [ctypes.c_size_t] + [P] * 6
     lib.kda_gated_norm_proj.restype = ctypes.c_int
     lib.kda_gated_norm_proj.argtypes = [P] * 6 + [i64, i32, i32, i32, f32, i32, P, ctypes.c_size_t, P]
+    lib.kda_gated_norm_proj_noalloc.restype = ctypes.c_int
+    lib.kda_gated_norm_proj_noalloc.argtypes = [P] * 6 + [i64, i32, i32, i32, f32, i32, P]
     lib.kda_out_proj.restype = ctypes.c_int
     lib.kda_out_proj.argtypes = [P, P, P, i64, i32, i32, i32, P, ctypes.c_size_t, P]
     lib.kda_out_proj_workspace_size.restype = ctypes.c_size_t
@@ -634,3 +636,32 @@ def gated_norm_proj(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tens
                                    _stream(dev)))
     return yy, res
 
+
+
+def gated_norm_proj_noalloc(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tensor,
+                            proj_weight: torch.Tensor, eps: float = 1e-6, *, y: torch.Tensor, out: torch.Tensor):
+    """gated_norm_proj through the library's allocation-free entry point: the caller
+    supplies y [..., heads * head_dim] (bf16) and out [..., out_features]; the split-K
+    partial sums use the library's static per-GPU scratch (16 MiB), so neither this call
+    nor the library allocates.  Calls that overlap in time on one GPU must not be issued.
+    Returns (y, out)."""
+    lib = load_library()
+    dev = o.device
+    if o.dim() < 2 or gate.shape != o.shape:
+        raise ValueError("o and gate must be [..., heads, head_dim]")
+    heads, hd = o.shape[-2], o.shape[-1]
+    N = proj_weight.shape[0]
+    lead = o.shape[:-2]
+    _shape(y, "y", lead + (heads * hd,), torch.bfloat16)
+    _shape(out, "out", lead + (N,), out.dtype)
+    if o.dtype != torch.bfloat16 or gate.dtype != torch.bfloat16 or proj_weight.dtype != torch.bfloat16:
+        raise TypeError("o, gate and proj_weight must be bfloat16")
+    _shape(norm_weight, "norm_weight", (hd,), torch.float32)
+    _shape(proj_weight, "proj_weight", (N, heads * hd), torch.bfloat16)
+    _on_device(dev, ("o", o), ("gate", gate), ("norm_weight", norm_weight), ("proj_weight", proj_weight),
+               ("y", y), ("out", out))
+    rows = o.numel() // (heads * hd)
+    _check(lib.kda_gated_norm_proj_noalloc(_ptr(o), _ptr(gate), _ptr(norm_weight), _ptr(proj_weight), _ptr(y),
+                                           _ptr(out), rows, heads, hd, N, float(eps), _dtype_code(out.dtype),
+                                           _stream(dev)))
+    return y, out

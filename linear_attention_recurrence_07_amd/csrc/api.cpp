@@ -402,10 +402,10 @@ kda_status_t kda_out_proj(const void *x, const void *weight, void *out, int64_t 
   return KDA_OK;
 }
 
-kda_status_t kda_gated_norm_proj(const void *o, const void *gate, const float *norm_weight,
-                                 const void *proj_weight, void *y, void *out, int64_t rows, int32_t heads,
-                                 int32_t head_dim, int32_t out_features, float eps, int32_t out_dtype,
-                                 void *workspace, size_t workspace_bytes, void *stream) {
+// Shared validation of the layer-exit entry points (everything but the workspace).
+static kda_status_t check_norm_proj(const void *o, const void *gate, const float *norm_weight,
+                                    const void *proj_weight, void *y, void *out, int64_t rows, int32_t heads,
+                                    int32_t head_dim, int32_t out_features, float eps, int32_t out_dtype) {
   KDA_TRY(check_ptr(o, "o", true));
   KDA_TRY(check_ptr(gate, "gate", true));
   KDA_TRY(check_ptr(norm_weight, "norm_weight", true));
@@ -423,6 +423,39 @@ kda_status_t kda_gated_norm_proj(const void *o, const void *gate, const float *n
   if (K > 0x7fffffff || !kda::out_proj_supports(rows, static_cast<int>(K), out_features))
     return fail(KDA_ERR_UNSUPPORTED, "heads * head_dim %% 256, out_features %% 64 must be 0 and rows <= 65535 * 64");
   if (rows * heads / 256 > 2147483647LL) return fail(KDA_ERR_SHAPE, "too many rows");
+  return KDA_OK;
+}
+
+kda_status_t kda_gated_norm_proj_noalloc(const void *o, const void *gate, const float *norm_weight,
+                                         const void *proj_weight, void *y, void *out, int64_t rows, int32_t heads,
+                                         int32_t head_dim, int32_t out_features, float eps, int32_t out_dtype,
+                                         void *stream) {
+  KDA_TRY(check_norm_proj(o, gate, norm_weight, proj_weight, y, out, rows, heads, head_dim, out_features, eps,
+                          out_dtype));
+  const int K = heads * head_dim;
+  const size_t need = kda::out_proj_workspace_bytes(rows, K, out_features);
+  if (need > kda::kOutProjStaticScratchBytes)
+    return fail(KDA_ERR_WORKSPACE, "the split-K partial sums need %zu bytes; the static scratch holds %zu "
+                                   "(use kda_gated_norm_proj with a workspace)",
+                need, kda::kOutProjStaticScratchBytes);
+  void *scratch = nullptr;
+  if (need > 0) KDA_TRY(hip_status(kda::out_proj_static_scratch(&scratch), "static scratch address"));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  KDA_TRY(hip_status(kda::launch_gated_rmsnorm(o, gate, norm_weight, y, rows * heads, head_dim, eps, 1, 1, 1, st),
+                     "gated norm"));
+  KDA_TRY(hip_status(kda::launch_out_proj(y, proj_weight, out, rows, K, out_features, out_dtype == KDA_BF16,
+                                          scratch, st),
+                     "output projection"));
+  return KDA_OK;
+}
+
+kda_status_t kda_gated_norm_proj(const void *o, const void *gate, const float *norm_weight,
+                                 const void *proj_weight, void *y, void *out, int64_t rows, int32_t heads,
+                                 int32_t head_dim, int32_t out_features, float eps, int32_t out_dtype,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+  KDA_TRY(check_norm_proj(o, gate, norm_weight, proj_weight, y, out, rows, heads, head_dim, out_features, eps,
+                          out_dtype));
+  const int64_t K = static_cast<int64_t>(heads) * head_dim;
   KDA_TRY(check_proj_workspace(rows, static_cast<int>(K), out_features, workspace, workspace_bytes));
   const hipStream_t st = static_cast<hipStream_t>(stream);
   KDA_TRY(hip_status(kda::launch_gated_rmsnorm(o, gate, norm_weight, y, rows * heads, head_dim, eps, 1, 1, 1, st),

@@ -48,6 +48,11 @@ bool out_proj_supports(int64_t M, int K, int N);
 size_t out_proj_workspace_bytes(int64_t M, int K, int N);
 hipError_t launch_out_proj(const void *x, const void *w, void *out, int64_t M, int K, int N, int out_bf16,
                            void *ws, hipStream_t s);
+// The allocation-free projection's static scratch: 16 MiB per device, enough for the fp32
+// partials of up to 64 rows x 16,384 features with K split 4 ways.  *ptr is this
+// device's address of it (taken once per device, with that device current).
+constexpr size_t kOutProjStaticScratchBytes = size_t(16) << 20;
+hipError_t out_proj_static_scratch(void **ptr);
 hipError_t launch_prefill_valu(const Args &a, hipStream_t s);
 // bf16 chunked prefill, d = 128: the per-chunk preparation (writes one record per
 // (slot, head) into ws), then the state scan that reads them.

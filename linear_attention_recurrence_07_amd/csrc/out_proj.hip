@@ -11,8 +11,17 @@
 // accumulation).  With S > 1 each slice writes fp32 partial sums to a workspace and a
 // second launch adds the S partials in a fixed order (deterministic results); S = 4 at
 // the decode shape gives 448 work-groups, enough loads in flight for the weight stream.
+#include <mutex>
+
 #include "kda_chunk.h"
 #include "kda_launch.h"
+
+// Scratch of the allocation-free entry point (kda_gated_norm_proj_noalloc): the fp32
+// partial sums of the split-K projection live in this file-scope device array instead of
+// a caller workspace.  Every GPU the library runs on holds its own copy until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device address: the
+// address is taken once per device with hipGetSymbolAddress (out_proj_static_scratch).
+static __device__ __align__(256) uint8_t scratch[kda::kOutProjStaticScratchBytes];
 
 namespace kda {
 namespace {
@@ -140,6 +149,29 @@ int out_proj_slices(int64_t M, int K) {
 size_t out_proj_workspace_bytes(int64_t M, int K, int N) {
   const int S = out_proj_slices(M, K);
   return S > 1 ? static_cast<size_t>(S) * static_cast<size_t>(M) * N * sizeof(float) : 0;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+}  // namespace
+
+hipError_t out_proj_static_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with this device current
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_out_proj(const void *x, const void *w, void *out, int64_t M, int K, int N, int out_bf16,

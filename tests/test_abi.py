@@ -370,3 +370,17 @@ def test_prefill_status_validation():
     assert st(_p(in_dtype=0)) == UNSUP
     assert st(_p(chunk=16)) == UNSUP
     assert st(_p(), packed=1) == 2                         # packed without num_seqs
+
+
+def test_noalloc_exit_rejects_sizes_beyond_its_static_scratch():
+    """kda_gated_norm_proj_noalloc: the split-K partials of 64 rows x 16,448 features
+    (4 x 64 x 16,448 x 4 bytes) exceed the 16 MiB static scratch -> KDA_ERR_WORKSPACE,
+    decided on the host before anything touches the GPU; the usual validation first."""
+    lib = K.load_library()
+    f = lambda rows=64, heads=96, hd=128, N=7168, o=A: lib.kda_gated_norm_proj_noalloc(
+        o, A, A, A, A, A, rows, heads, hd, N, ctypes.c_float(1e-6), 1, None)
+    assert f(N=16448) == WS
+    assert f(o=None) == 1
+    assert f(hd=100) == UNSUP
+    assert f(rows=-1) == 2
+    assert f(o=MIS) == 4
