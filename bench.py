@@ -227,8 +227,8 @@ def time_fused_norm_scan(kda, P, ws, o, fs, y, reps: int = 10) -> float:
 
 def time_prefill_y_only(kda, P, ws, fs, y, reps: int = 10) -> dict:
     """The T=8192 prefill with the gated norm when the caller wants y alone (no head
-    outputs): the preparation, then the scan applying the norm itself and writing no o.
-    Timed on its own with HIP events; not part of the step."""
+    outputs): the preparation, the scan writing its head outputs into y, and the norm in
+    place.  Timed on its own with HIP events; not part of the step."""
     def call():
         kda.chunk_prefill(P["q"], P["k"], P["v"], P["g"], P["beta"], gate=P["gate"], norm_weight=P["w"],
                           norm_eps=P["eps"], head_outputs=False, final_state=fs, y=y, workspace=ws)
@@ -615,8 +615,8 @@ def main():
         "scan_with_fused_norm": {"avg_call_us": t_fused * 1e6, "scan_plus_norm_us": (t_scan + t_nrm) * 1e6,
                                  "algorithmic_bytes": _bytes_scan(T_PREFILL, H, D, False, norm=True),
                                  "achieved_GBps": _bytes_scan(T_PREFILL, H, D, False, norm=True) / t_fused / 1e9},
-        # the prefill + norm when only y is wanted (the scan applies the norm, no o is
-        # written), timed on its own against the step's preparation + scan + norm
+        # the prefill + norm when only y is wanted (head outputs written into y, then the
+        # norm in place), timed on its own against the step's preparation + scan + norm
         "prefill_y_only": y_only,
         "ceilings": ceil,
         # the causal short convolution in front of the kernel, timed on its own (two

@@ -128,9 +128,9 @@ typedef struct {
  * (sequence, head, chunk) at once, which stores each chunk's intra-chunk products in the
  * workspace (30,224 bytes per chunk and head, plus 512 bytes that kda_chunk_scan's own
  * norm uses), then the sequential state scan; with y and o given, a third launch applies
- * the gated norm to o.  With y given and o NULL the scan applies the norm itself and
- * writes no o (as kda_chunk_scan with gate, norm_weight and y), which saves writing o
- * and reading it back.  The other kernels apply the norm in the same launch either way.
+ * the gated norm to o.  With y given and o NULL the scan writes the head outputs into y
+ * and the norm runs on them in place (no work-group of this call waits for another).
+ * The vector-ALU kernel applies the norm in its own launch either way.
  */
 kda_status_t kda_chunk_prefill(const kda_params_t *p,
                                const void *q, const void *k, const void *v,
@@ -153,8 +153,8 @@ size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed);
 /*
  * kda_chunk_prefill_status -- whether every wait between the two column tiles of a head
  * in the scans run on this workspace since its last preparation completed normally.
- * Only the scan that applies the gated norm itself (kda_chunk_scan with y, and
- * kda_chunk_prefill with y and o == NULL) has such waits: the two work-groups of a head
+ * Only the scan that applies the gated norm itself (kda_chunk_scan with y) has such
+ * waits: the two work-groups of a head
  * exchange per-token sums of squares.  A wait always ends, since partner work-groups
  * are consecutive in one XCD's dispatch order, but it is bounded (seconds); if other work
  * held the GPU's CUs longer than that, the wait gives up, the tokens after it get NaN in
@@ -187,8 +187,8 @@ kda_status_t kda_chunk_prefill_status(const kda_params_t *p, int32_t packed, con
  * which exchange per-token sums of squares through the workspace (device-coherent
  * 64-bit words; a wait for the other work-group is bounded and, if it ever ran out,
  * would give NaN in y rather than hang).  That saves the second read of o but loads the
- * scan, so at large T it is slower than writing o and running the separate norm;
- * kda_chunk_prefill uses the separate one when o is wanted.  p and cu_seqlens must be those the workspace was prepared with, and the
+ * scan, so at large T it is slower than writing o and running the separate norm, which
+ * kda_chunk_prefill uses.  p and cu_seqlens must be those the workspace was prepared with, and the
  * preparation must have completed or be ordered before the scan on the stream; the
  * workspace must not be modified in between.  The records already hold the effect of a
  * mask, so the scan takes none.

@@ -233,8 +233,8 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   head_outputs: bool = True):
     """Chunked prefill.  Returns (o, final_state), or (o, final_state, y) with the fused
     sigmoid-gated RMSNorm when gate and norm_weight are given.  With the norm and
-    head_outputs=False the head outputs are not written (o is None): the bf16 d = 128
-    kernel then applies the norm inside its state scan.
+    head_outputs=False no o is returned (None): the head outputs pass through y, which is
+    then normalised in place.
 
     cu_seqlens ([N+1] int32; a CPU tensor is validated then copied to the GPU) packs N
     sequences into B = 1; attention_mask ([B, T], nonzero = token) marks padding.

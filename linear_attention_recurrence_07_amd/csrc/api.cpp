@@ -174,20 +174,21 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
                   chunk);
   }
   if (mfma) {
-    // With o wanted, the gated norm runs as its own launch over o: the scan can apply it
-    // itself, but on the scan's 2 work-groups per head that costs more than a separate
-    // pass at full HBM bandwidth on every CU.  With y alone, the scan applies it and
-    // writes no o.
+    // The gated norm runs as its own launch over the head outputs: the scan can apply it
+    // itself (kda_chunk_scan with y), but on the scan's 2 work-groups per head that costs
+    // more than a separate pass at full HBM bandwidth on every CU, and it needs waits
+    // between work-groups.  With y alone, the head outputs are written into y and
+    // normalised there, in place.
     KDA_TRY(check_workspace(p, cu_seqlens, workspace, workspace_bytes));
     KDA_TRY(hip_status(kda::launch_chunk_prep(a, workspace, st), "prefill (chunk preparation)"));
-    if (o == nullptr) {
-      a.gate = gate; a.norm_w = norm_weight; a.y = y;
-    }
+    void *out = o != nullptr ? o : y;
+    a.o = out;
     KDA_TRY(hip_status(kda::launch_chunk_scan(a, workspace, st), "prefill (state scan)"));
-    if (y != nullptr && o != nullptr) {
+    if (y != nullptr) {
       const int64_t rows = static_cast<int64_t>(p->B) * p->T * p->H;
-      KDA_TRY(hip_status(kda::launch_gated_rmsnorm(o, gate, norm_weight, y, rows, p->dv, p->norm_eps,
-                                                   a.out_bf16, a.in_bf16, a.out_bf16, st),
+      const int32_t *tok_end = cu_seqlens ? cu_seqlens + a.N : nullptr;   // tokens past it are not written
+      KDA_TRY(hip_status(kda::launch_gated_rmsnorm(out, gate, norm_weight, y, rows, p->dv, p->norm_eps,
+                                                   a.out_bf16, a.in_bf16, a.out_bf16, st, tok_end, p->H),
                          "gated norm"));
     }
   } else {

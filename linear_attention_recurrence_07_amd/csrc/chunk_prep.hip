@@ -52,53 +52,6 @@ struct Shared {
 };
 static_assert(sizeof(Shared) <= 20 * 1024, "LDS per work-group");
 
-// Value of lane r - N of the same 16-lane row (0 for r < N).
-template <int N>
-__device__ __forceinline__ float row_shr(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, true));
-}
-// Inclusive prefix sum over the 16 lanes of each row.
-__device__ __forceinline__ float row_prefix(float x) {
-  x += row_shr<1>(x);
-  x += row_shr<2>(x);
-  x += row_shr<4>(x);
-  x += row_shr<8>(x);
-  return x;
-}
-// Sum over the four lanes r, r + 16, r + 32, r + 48.
-__device__ __forceinline__ float col_sum4(float x) {
-  x += __shfl_xor(x, 16, 64);
-  return x + __shfl_xor(x, 32, 64);
-}
-__device__ __forceinline__ f32x4 mfma_f32k4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-// x = hi + lo with both parts fp16, four values -> two fp16 pairs each.
-__device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
-  uint2 h, l;
-  split_f16x4(x, h, l);
-  hi = u32x2{h.x, h.y};
-  lo = u32x2{l.x, l.y};
-}
-__device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
-// w holds 8 channels 8L .. 8L+7 of a K block (L = (0, 2, 1, 3)[lg]); one row swap of its
-// halves (odd rows of the first with even rows of the second) leaves channels 4lg .. 4lg+3
-// in lo and 16 + 4lg .. 16 + 4lg + 3 in hi, the MFMA operand order.
-__device__ __forceinline__ void operand_halves(u32x4 w, u32x2 &lo, u32x2 &hi) {
-  const auto a = __builtin_amdgcn_permlane16_swap(w[0], w[2], false, false);
-  const auto b = __builtin_amdgcn_permlane16_swap(w[1], w[3], false, false);
-  uint32_t a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
-  __asm__("" : "+v"(a1), "+v"(b1));   // keep the optimiser from merging the swap's two outputs
-  lo = u32x2{a0, b0};
-  hi = u32x2{a1, b1};
-}
-__device__ __forceinline__ f32x4 mma_bf16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma_f16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
 // G_HEAD: g holds one decay per (token, head), shared by every key channel.
 template <bool HAS_MASK, bool G_HEAD>
 __global__ void __launch_bounds__(NT)

@@ -42,13 +42,16 @@ constexpr int kThreads = 256;
 template <int W, typename TX, typename TG, typename TOut>
 __global__ void __launch_bounds__(kThreads)
 gated_rmsnorm_kernel(const TX *x, const TG *__restrict__ gate,
-                     const float *__restrict__ w, TOut *y, int64_t rows, float eps) {
+                     const float *__restrict__ w, TOut *y, int64_t rows, float eps,
+                     const int32_t *__restrict__ tok_end, int heads) {
   constexpr int LPR = W / 8;                 // lanes per row
   constexpr int RPB = kThreads / LPR;        // rows per block
   static_assert(LPR >= 1 && LPR <= 64, "width");
   const int tid = threadIdx.x;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + tid / LPR;
   if (row >= rows) return;                   // whole rows drop out together
+  // packed sequences: rows of tokens at or past the end of the last sequence are not touched
+  if (tok_end != nullptr && row / heads >= static_cast<int64_t>(*tok_end)) return;
   const int c0 = (tid % LPR) * 8;
   const size_t base = static_cast<size_t>(row) * W + c0;
   float xv[8], gv[8];
@@ -70,27 +73,27 @@ gated_rmsnorm_kernel(const TX *x, const TG *__restrict__ gate,
 
 template <int W, typename TX, typename TG, typename TOut>
 hipError_t launch_w(const void *x, const void *gate, const float *w, void *y, int64_t rows,
-                    float eps, hipStream_t st) {
+                    float eps, const int32_t *tok_end, int heads, hipStream_t st) {
   constexpr int RPB = kThreads / (W / 8);
   const int64_t blocks = (rows + RPB - 1) / RPB;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((gated_rmsnorm_kernel<W, TX, TG, TOut>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kThreads), 0, st, static_cast<const TX *>(x),
-                     static_cast<const TG *>(gate), w, static_cast<TOut *>(y), rows, eps);
+                     static_cast<const TG *>(gate), w, static_cast<TOut *>(y), rows, eps, tok_end, heads);
   return hipGetLastError();
 }
 
 template <typename TX, typename TG, typename TOut>
 hipError_t launch_t(const void *x, const void *gate, const float *w, void *y, int64_t rows,
-                    int width, float eps, hipStream_t st) {
+                    int width, float eps, const int32_t *tok_end, int heads, hipStream_t st) {
   switch (width) {
-    case 8: return launch_w<8, TX, TG, TOut>(x, gate, w, y, rows, eps, st);
-    case 16: return launch_w<16, TX, TG, TOut>(x, gate, w, y, rows, eps, st);
-    case 32: return launch_w<32, TX, TG, TOut>(x, gate, w, y, rows, eps, st);
-    case 64: return launch_w<64, TX, TG, TOut>(x, gate, w, y, rows, eps, st);
-    case 128: return launch_w<128, TX, TG, TOut>(x, gate, w, y, rows, eps, st);
-    case 256: return launch_w<256, TX, TG, TOut>(x, gate, w, y, rows, eps, st);
-    case 512: return launch_w<512, TX, TG, TOut>(x, gate, w, y, rows, eps, st);
+    case 8: return launch_w<8, TX, TG, TOut>(x, gate, w, y, rows, eps, tok_end, heads, st);
+    case 16: return launch_w<16, TX, TG, TOut>(x, gate, w, y, rows, eps, tok_end, heads, st);
+    case 32: return launch_w<32, TX, TG, TOut>(x, gate, w, y, rows, eps, tok_end, heads, st);
+    case 64: return launch_w<64, TX, TG, TOut>(x, gate, w, y, rows, eps, tok_end, heads, st);
+    case 128: return launch_w<128, TX, TG, TOut>(x, gate, w, y, rows, eps, tok_end, heads, st);
+    case 256: return launch_w<256, TX, TG, TOut>(x, gate, w, y, rows, eps, tok_end, heads, st);
+    case 512: return launch_w<512, TX, TG, TOut>(x, gate, w, y, rows, eps, tok_end, heads, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -99,19 +102,19 @@ hipError_t launch_t(const void *x, const void *gate, const float *w, void *y, in
 
 hipError_t launch_gated_rmsnorm(const void *x, const void *gate, const float *w, void *y,
                                 int64_t rows, int width, float eps, int x_bf16, int gate_bf16,
-                                int out_bf16, hipStream_t st) {
+                                int out_bf16, hipStream_t st, const int32_t *tok_end, int heads) {
   using B = uint16_t;
   using F = float;
   const int code = (x_bf16 ? 4 : 0) | (gate_bf16 ? 2 : 0) | (out_bf16 ? 1 : 0);
   switch (code) {
-    case 7: return launch_t<B, B, B>(x, gate, w, y, rows, width, eps, st);
-    case 6: return launch_t<B, B, F>(x, gate, w, y, rows, width, eps, st);
-    case 5: return launch_t<B, F, B>(x, gate, w, y, rows, width, eps, st);
-    case 4: return launch_t<B, F, F>(x, gate, w, y, rows, width, eps, st);
-    case 3: return launch_t<F, B, B>(x, gate, w, y, rows, width, eps, st);
-    case 2: return launch_t<F, B, F>(x, gate, w, y, rows, width, eps, st);
-    case 1: return launch_t<F, F, B>(x, gate, w, y, rows, width, eps, st);
-    default: return launch_t<F, F, F>(x, gate, w, y, rows, width, eps, st);
+    case 7: return launch_t<B, B, B>(x, gate, w, y, rows, width, eps, tok_end, heads, st);
+    case 6: return launch_t<B, B, F>(x, gate, w, y, rows, width, eps, tok_end, heads, st);
+    case 5: return launch_t<B, F, B>(x, gate, w, y, rows, width, eps, tok_end, heads, st);
+    case 4: return launch_t<B, F, F>(x, gate, w, y, rows, width, eps, tok_end, heads, st);
+    case 3: return launch_t<F, B, B>(x, gate, w, y, rows, width, eps, tok_end, heads, st);
+    case 2: return launch_t<F, B, F>(x, gate, w, y, rows, width, eps, tok_end, heads, st);
+    case 1: return launch_t<F, F, B>(x, gate, w, y, rows, width, eps, tok_end, heads, st);
+    default: return launch_t<F, F, F>(x, gate, w, y, rows, width, eps, tok_end, heads, st);
   }
 }
 

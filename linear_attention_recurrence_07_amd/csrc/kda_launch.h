@@ -62,9 +62,11 @@ uint32_t *chunk_status_word(const void *ws, long long B, long long T, long long 
 hipError_t launch_chunk_prep(const Args &a, void *ws, hipStream_t s);
 // With a.y set the scan also applies the gated norm (a.gate, a.norm_w, a.eps).
 hipError_t launch_chunk_scan(const Args &a, const void *ws, hipStream_t s);
+// With tok_end (a device pointer to the end of the last packed sequence), rows of tokens
+// at or past it (row / heads >= *tok_end) are left untouched.
 hipError_t launch_gated_rmsnorm(const void *x, const void *gate, const float *w, void *y,
                                 int64_t rows, int width, float eps, int x_bf16, int gate_bf16,
-                                int out_bf16, hipStream_t s);
+                                int out_bf16, hipStream_t s, const int32_t *tok_end = nullptr, int heads = 1);
 
 // Shape support of each kernel family.
 bool recurrent_supports(int dk, int dv);
