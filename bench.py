@@ -51,7 +51,7 @@ def _bytes_prefill(T: int, H: int, d: int, with_init: bool, norm: bool = False) 
     return T * H * per_tok_head + state * (2 if with_init else 1)
 
 
-REC_BYTES = 30224      # one chunk record (per 32-token chunk and head) in the workspace
+REC_BYTES = 32272      # one chunk record (per 32-token chunk and head) in the workspace
 XCHG_BYTES = 512       # the scan's norm-exchange words per chunk and head, cleared by the preparation
 CHUNK = 32
 
@@ -137,6 +137,52 @@ def time_per_head_decay(kda, P, ws, o, fs, reps: int = 10) -> dict:
     b_prep = (T_PREFILL // CHUNK) * H * (CHUNK * (2 * D * 2 + 4 + 4) + REC_BYTES)
     return {"prepare_us": tp * 1e6, "scan_us": ts * 1e6, "tokens_per_s": T_PREFILL / (tp + ts),
             "prepare_algorithmic_bytes": b_prep, "prepare_GBps": b_prep / tp / 1e9}
+
+
+def time_prefill_conv(kda, P, ws, o, fs, y, reps: int = 10) -> dict:
+    """The T=8192 prefill with the short convolution in front (raw q, k, v projections,
+    width-4 taps, carried inputs written), with gated norm, two ways: fused into the
+    preparation and the scan (kda_chunk_prefill_conv), and as three kda_short_conv passes
+    followed by kda_chunk_prefill.  Not part of the step."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    C = H * D
+    ws3 = tuple((torch.rand((C, 4), generator=gen, device="cuda") - 0.5) for _ in range(3))
+    fin = tuple(torch.empty((1, 3, C), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    filt = tuple(torch.empty((1, T_PREFILL, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    raw = (P["q"], P["k"], P["v"])
+
+    def fused():
+        kda.chunk_prefill_conv(P["q"], P["k"], P["v"], P["g"], P["beta"], conv_weights=ws3, conv_final_state=fin,
+                               gate=P["gate"], norm_weight=P["w"], norm_eps=P["eps"], out=o, final_state=fs, y=y,
+                               workspace=ws)
+
+    def separate():
+        for x, w, f, yv in zip(raw, ws3, fin, filt):
+            kda.short_conv(x.view(1, T_PREFILL, C), w, final_state=f, out=yv.view(1, T_PREFILL, C))
+        kda.chunk_prefill(filt[0], filt[1], filt[2], P["g"], P["beta"], gate=P["gate"], norm_weight=P["w"],
+                          norm_eps=P["eps"], out=o, final_state=fs, y=y, workspace=ws)
+
+    res = {}
+    for name, fn in (("fused", fused), ("separate", separate)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        res[f"{name}_us"] = t * 1e6
+        res[f"{name}_tokens_per_s"] = T_PREFILL / t
+    nb = _bytes_prefill(T_PREFILL, H, D, False, norm=True) + 3 * (3 * C * 2 + C * 4 * 4)
+    res["fused_algorithmic_bytes"] = nb
+    res["fused_GBps"] = nb / (res["fused_us"] * 1e-6) / 1e9
+    res["saved_bytes_vs_separate"] = 3 * 2 * T_PREFILL * C * 2      # filtered q, k, v written and read back
+    del filt, fin
+    return res
 
 
 def time_recurrent_states(kda, T: int = 256, reps: int = 5) -> dict:
@@ -531,6 +577,8 @@ def main():
     ceil = ceilings()
     print("[bench] short convolution", file=sys.stderr, flush=True)
     conv = time_short_conv(kda)
+    print("[bench] prefill with the short convolution fused", file=sys.stderr, flush=True)
+    pconv = time_prefill_conv(kda, P, ws, o, fs, y)
     print("[bench] prefill with one decay per head", file=sys.stderr, flush=True)
     per_head = time_per_head_decay(kda, P, ws, o, fs)
     print("[bench] per-token states", file=sys.stderr, flush=True)
@@ -622,6 +670,7 @@ def main():
         # the causal short convolution in front of the kernel, timed on its own (two
         # launches per call: the filter over all tokens, then the carried-input update)
         "short_conv": conv,
+        "prefill_conv": pconv,
         # the same prefill with g [1, T, H] (one decay per head), timed on its own
         "prefill_per_head_decay": per_head,
         # the token-by-token kernel storing the state after every token, timed on its own

@@ -62,6 +62,12 @@ def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
     return f32_to_bf16_bits(x) if dtype == BF16 else np.ascontiguousarray(x, dtype=np.float32)
 
 
+def store_as(x: np.ndarray, dtype: str) -> np.ndarray:
+    """x as a tensor of `dtype` would hold it: fp32 values, or raw bf16 bits rounded to
+    nearest even from the fp32 values."""
+    return _cast(np.asarray(x, dtype=np.float32), dtype)
+
+
 # --------------------------------------------------------------------------- container
 @dataclasses.dataclass
 class KdaInputs:
@@ -327,6 +333,31 @@ def conv_inputs(name: str, *, B: int, T: int, D: int, width: int = 4, in_dtype: 
                       weight=w, initial_state=None if init is None else _cast(init, in_dtype),
                       cu_seqlens=cu, mask=None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8),
                       seed=seed)
+
+
+@dataclasses.dataclass
+class LayerConv:
+    """The three short convolutions in front of a KdaInputs problem whose q, k and v are
+    the raw projections: taps (wq, wk, wv) fp32 [H*d, W] and, optionally, the carried
+    inputs (q, k, v) [N, W-1, H*d] in the problem's input dtype."""
+
+    width: int
+    weights: tuple
+    initial: Optional[tuple] = None
+
+
+def layer_conv(x: KdaInputs, *, width: int = 4, seed: int = 0, with_state: bool = False) -> LayerConv:
+    """Draw (from a generator of its own, so x's draws stay as they are) wq, wk, wv, then the
+    carried inputs of q, k, v.  Taps ~ U(-1/sqrt(W), 1/sqrt(W)) as in conv_inputs; carried
+    inputs ~ N(0, 1), like the raw projections."""
+    rng = np.random.default_rng((seed, 3))
+    bound = 1.0 / np.sqrt(width)
+    ws = tuple(_draw(rng, (x.H * d, width), "uniform", low=-bound, high=bound) for d in (x.dk, x.dk, x.dv))
+    init = None
+    if with_state:
+        n = x.num_seqs
+        init = tuple(_cast(_draw(rng, (n, width - 1, x.H * d), "normal"), x.in_dtype) for d in (x.dk, x.dk, x.dv))
+    return LayerConv(width=width, weights=ws, initial=init)
 
 
 def conv_padded_from_packed(x: ConvInputs, *, left: bool = False) -> ConvInputs:

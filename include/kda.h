@@ -126,7 +126,7 @@ typedef struct {
  *
  * The bf16 kernel for dk = dv = 128 runs in two launches: a preparation pass over every
  * (sequence, head, chunk) at once, which stores each chunk's intra-chunk products in the
- * workspace (30,224 bytes per chunk and head, plus 512 bytes that kda_chunk_scan's own
+ * workspace (32,272 bytes per chunk and head, plus 512 bytes that kda_chunk_scan's own
  * norm uses), then the sequential state scan; with y and o given, a third launch applies
  * the gated norm to o.  With y given and o NULL the scan writes the head outputs into y
  * and the norm runs on them in place (no work-group of this call waits for another).
@@ -145,7 +145,7 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p,
  * kda_chunk_prefill_workspace_size -- bytes of workspace kda_chunk_prefill needs for
  * these params; `packed` is nonzero when cu_seqlens will be given (p->num_seqs set).
  * 0 for invalid params or when the chosen kernel needs none.  With packing it is
- * (N + ceil(T / 32)) * H * 30736 + 256 bytes, otherwise B * ceil(T / 32) * H * 30736 + 256
+ * (N + ceil(T / 32)) * H * 32784 + 256 bytes, otherwise B * ceil(T / 32) * H * 32784 + 256
  * (a record and the norm-exchange words per chunk and head, then a status word).
  */
 size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed);
@@ -299,6 +299,76 @@ typedef struct {
 kda_status_t kda_short_conv(const kda_conv_params_t *p, const void *x, const float *weight,
                             const void *initial_state, const int32_t *cu_seqlens,
                             const uint8_t *mask, void *y, void *final_state, void *stream);
+
+/*
+ * The short convolution fused into the KDA kernels' prologue: the layer's q, k and v
+ * projections each pass a causal width-W filter (then SiLU) right before the recurrence,
+ * and the layer carries the last W-1 inputs of every sequence between calls, besides the
+ * state (Kimi-K3 atlas, KDA layer page, kda-init code: ShortConvolution with activation
+ * 'silu' on q, k and v; nnterp Kimi-Linear page, Notes on KDA: the convolution runs over
+ * the projected queries, keys and values, so the mixer keeps its last tokens outside the
+ * state).  The filter, the window rule (padding skipped, a sequence starting from its
+ * carried inputs) and the carried inputs after the call are those of kda_short_conv, with
+ * x = the raw q, k or v and D = H * d channels each (head h owns channels h*d .. h*d+d-1).
+ * The filtered values stay in fp32 inside the kernels (a separate kda_short_conv pass would
+ * store them in its out_dtype first): the fused call equals kda_short_conv with fp32 outputs
+ * followed by the recurrence on those values, up to the recurrence kernels' own rounding.
+ */
+typedef struct {
+  int32_t width;            /* W, 2..4 (4 in the pages' configuration)                        */
+  int32_t activation;       /* 1: SiLU after the filter (the pages' setting), 0: none          */
+  const float *weight_q;    /* [H * dk, W] fp32 taps per channel; weight[c][W-1] meets the     */
+  const float *weight_k;    /*   newest input (as kda_short_conv's weight)                     */
+  const float *weight_v;    /* [H * dv, W]                                                     */
+  const void *initial_q;    /* [N, W-1, H * dk] in_dtype: the W-1 inputs before each sequence  */
+  const void *initial_k;    /*   (oldest first), or NULL for zeros (start of a prompt)         */
+  const void *initial_v;    /* [N, W-1, H * dv]                                                */
+  void *final_q;            /* [N, W-1, H * d] in_dtype: the last W-1 inputs of each sequence  */
+  void *final_k;            /*   after the call (padding skipped), or NULL to skip; each may   */
+  void *final_v;            /*   be the same buffer as its initial_* (updated in place)        */
+} kda_conv_t;
+
+/*
+ * kda_chunk_prefill_conv -- kda_chunk_prefill on the raw projections: q, k and v are the
+ * inputs of the short convolution `conv`, which the kernels apply themselves (the
+ * preparation filters q and k of each chunk, the scan filters v; the filtered values never
+ * go to memory).  Every other argument, layout and rule as kda_chunk_prefill (same
+ * workspace size); N = num_seqs with cu_seqlens, else B.  After the recurrence, one more
+ * launch writes the carried inputs of every sequence whose final_* is set.
+ * Kernel: the bf16 matrix-core prefill only (in_dtype bf16, dk = dv = 128, chunk 0, 32 or
+ * 64, T * H * 128 < 2^31); other shapes return KDA_ERR_UNSUPPORTED (run kda_short_conv,
+ * then kda_chunk_prefill).  All conv pointers are 16-byte aligned device memory owned by
+ * the caller; nothing is allocated.  Errors: those of kda_chunk_prefill, KDA_ERR_NULL
+ * (conv or a weight NULL), KDA_ERR_SHAPE (activation), KDA_ERR_UNSUPPORTED (width outside
+ * 2..4, more than 65535 sequences, other kernels), KDA_ERR_ALIGN.
+ */
+kda_status_t kda_chunk_prefill_conv(const kda_params_t *p, const kda_conv_t *conv,
+                                    const void *q, const void *k, const void *v,
+                                    const float *g, const float *beta,
+                                    const float *initial_state,
+                                    const int32_t *cu_seqlens, const uint8_t *mask,
+                                    void *o, float *final_state,
+                                    const void *gate, const float *norm_weight, void *y,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_recurrent_step_conv -- kda_recurrent_step on the raw projections of the new tokens:
+ * each token's q, k and v are filtered with the row's carried inputs (conv->initial_*,
+ * [B, W-1, H * d]) in the kernel, and the carried inputs after the call go to
+ * conv->final_* (decode: pass the same buffer as initial_* and final_*; the kernel that
+ * owns a head updates its channels in place, or, when a head is split over several
+ * work-groups, a second launch does).  A padding token (mask 0) leaves the window as it
+ * is.  T = 0 only copies the carried inputs.  Other arguments, layout and errors as
+ * kda_recurrent_step, plus those of kda_chunk_prefill_conv's conv checks.  Any dk = dv
+ * that kda_recurrent_step takes.
+ */
+kda_status_t kda_recurrent_step_conv(const kda_params_t *p, const kda_conv_t *conv,
+                                     const void *q, const void *k, const void *v,
+                                     const float *g, const float *beta,
+                                     float *state, const uint8_t *mask,
+                                     void *o,
+                                     const void *gate, const float *norm_weight, void *y,
+                                     void *stream);
 
 /*
  * kda_gated_norm_proj -- the layer's exit at decode: the sigmoid-gated RMSNorm of each

@@ -55,6 +55,13 @@ class KdaConvParams(ctypes.Structure):
                 ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
 
 
+class KdaConv(ctypes.Structure):
+    _fields_ = [("width", ctypes.c_int32), ("activation", ctypes.c_int32),
+                ("weight_q", ctypes.c_void_p), ("weight_k", ctypes.c_void_p), ("weight_v", ctypes.c_void_p),
+                ("initial_q", ctypes.c_void_p), ("initial_k", ctypes.c_void_p), ("initial_v", ctypes.c_void_p),
+                ("final_q", ctypes.c_void_p), ("final_k", ctypes.c_void_p), ("final_v", ctypes.c_void_p)]
+
+
 class KdaParams(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
@@ -83,6 +90,11 @@ def load_library():
     P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     lib.kda_chunk_prefill.restype = ctypes.c_int
     lib.kda_chunk_prefill.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 13 + [P, ctypes.c_size_t, P]
+    lib.kda_chunk_prefill_conv.restype = ctypes.c_int
+    lib.kda_chunk_prefill_conv.argtypes = [ctypes.POINTER(KdaParams), ctypes.POINTER(KdaConv)] + [P] * 13 + \
+        [P, ctypes.c_size_t, P]
+    lib.kda_recurrent_step_conv.restype = ctypes.c_int
+    lib.kda_recurrent_step_conv.argtypes = [ctypes.POINTER(KdaParams), ctypes.POINTER(KdaConv)] + [P] * 12
     lib.kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_prefill_workspace_size.argtypes = [ctypes.POINTER(KdaParams), i32]
     lib.kda_chunk_prefill_status.restype = ctypes.c_int
@@ -230,7 +242,7 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   output_dtype: Optional[torch.dtype] = None,
                   out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
                   y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  head_outputs: bool = True):
+                  head_outputs: bool = True, _conv=None):
     """Chunked prefill.  Returns (o, final_state), or (o, final_state, y) with the fused
     sigmoid-gated RMSNorm when gate and norm_weight are given.  With the norm and
     head_outputs=False no o is returned (None): the head outputs pass through y, which is
@@ -298,11 +310,73 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     else:
         _dev(workspace, "workspace", dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.kda_chunk_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                 _ptr(initial_state), _ptr(cu_dev), _ptr(mask_dev), _ptr(o), _ptr(fs),
-                                 _ptr(gate), _ptr(norm_weight), _ptr(y), _ptr(workspace), ws_bytes,
-                                 _stream(dev)))
+    if _conv is None:
+        _check(lib.kda_chunk_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(initial_state), _ptr(cu_dev), _ptr(mask_dev), _ptr(o), _ptr(fs),
+                                     _ptr(gate), _ptr(norm_weight), _ptr(y), _ptr(workspace), ws_bytes,
+                                     _stream(dev)))
+    else:
+        cv = _conv(N, H, dk, in_dt, dev)
+        _check(lib.kda_chunk_prefill_conv(ctypes.byref(p), ctypes.byref(cv), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                          _ptr(beta), _ptr(initial_state), _ptr(cu_dev), _ptr(mask_dev), _ptr(o),
+                                          _ptr(fs), _ptr(gate), _ptr(norm_weight), _ptr(y), _ptr(workspace),
+                                          ws_bytes, _stream(dev)))
     return (o, fs) if y is None else (o, fs, y)
+
+
+class _ConvSpec:
+    """Marshals the fused short convolution's tensors into a KdaConv once the problem's
+    sizes are known; keeps the final carried inputs it allocates in `final`."""
+
+    def __init__(self, weights, initial, final, with_final, activation):
+        if activation not in ("silu", None):
+            raise ValueError("activation must be 'silu' or None")
+        if len(weights) != 3:
+            raise ValueError("conv_weights must be (weight_q, weight_k, weight_v)")
+        self.weights, self.initial, self.final = tuple(weights), initial, final
+        self.with_final, self.silu = with_final, activation == "silu"
+
+    def __call__(self, N, H, d, in_dt, dev):
+        W = self.weights[0].shape[-1] if self.weights[0].dim() == 2 else 0
+        for name, w in zip("qkv", self.weights):
+            _shape(w, f"conv weight_{name}", (H * d, W), torch.float32)
+        st_shape = (N, W - 1, H * d)
+        init = self.initial if self.initial is not None else (None, None, None)
+        if len(init) != 3:
+            raise ValueError("conv_state must be (q, k, v) carried inputs")
+        for name, t in zip("qkv", init):
+            if t is not None:
+                _shape(t, f"conv_state[{name}]", st_shape, in_dt)
+        fin = self.final
+        if fin is None and self.with_final:
+            fin = tuple(torch.empty(st_shape, dtype=in_dt, device=dev) for _ in range(3))
+        fin = fin if fin is not None else (None, None, None)
+        if len(fin) != 3:
+            raise ValueError("conv_final_state must be (q, k, v) tensors")
+        for name, t in zip("qkv", fin):
+            if t is not None:
+                _shape(t, f"conv_final_state[{name}]", st_shape, in_dt)
+        _on_device(dev, *[(f"conv weight_{n}", w) for n, w in zip("qkv", self.weights)],
+                   *[(f"conv_state[{n}]", t) for n, t in zip("qkv", init)],
+                   *[(f"conv_final_state[{n}]", t) for n, t in zip("qkv", fin)])
+        self.final = fin if self.with_final or self.final is not None else None
+        return KdaConv(W, 1 if self.silu else 0, *[_ptr(w) for w in self.weights], *[_ptr(t) for t in init],
+                       *[_ptr(t) for t in fin])
+
+
+def chunk_prefill_conv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                       beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None, *,
+                       conv_weights, conv_state=None, conv_final_state=None, with_conv_state: bool = True,
+                       activation: Optional[str] = "silu", **kw):
+    """chunk_prefill on the raw q, k, v projections: the library runs their causal short
+    convolution (conv_weights = (wq, wk, wv), float32 [H*d, W] each, then SiLU) inside the
+    prefill.  conv_state = (q, k, v) carried inputs [N, W-1, H*d] in q's dtype (or None:
+    zeros).  Returns chunk_prefill's tuple followed by the (q, k, v) carried inputs after
+    the call (written into conv_final_state when given; the same tensors as conv_state
+    update them in place), or None with with_conv_state=False."""
+    spec = _ConvSpec(conv_weights, conv_state, conv_final_state, with_conv_state, activation)
+    res = chunk_prefill(q, k, v, g, beta, initial_state, _conv=spec, **kw)
+    return (*res, spec.final)
 
 
 def chunk_prefill_workspace_size(B: int, T: int, H: int, dk: int, dv: int, *,
@@ -443,7 +517,7 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
                    norm_eps: float = 1e-6, scale: Optional[float] = None,
                    use_qk_l2norm_in_kernel: bool = True, output_dtype: Optional[torch.dtype] = None,
                    out: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
-                   states: Optional[torch.Tensor] = None):
+                   states: Optional[torch.Tensor] = None, _conv=None):
     """Token-by-token step(s): advances `state` ([B,H,dk,dv] fp32) in place over the T
     tokens of q/k/v and returns o (and y with the gated norm).  With `states` (a float32
     [B,T,H,dk,dv] tensor) the state after every token is stored there as well.  Caller-
@@ -488,7 +562,14 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     p = _params(B, T, H, dk, dv, scale=scale, use_qk_l2norm=use_qk_l2norm_in_kernel,
                 in_dtype=_dtype_code(in_dt), out_dtype=_dtype_code(out_dt), norm_eps=norm_eps,
                 decay_per_head=per_head)
-    if states is None:
+    if _conv is not None:
+        if states is not None:
+            raise ValueError("the fused convolution stores no per-token states")
+        cv = _conv(B, H, dk, in_dt, dev)
+        _check(lib.kda_recurrent_step_conv(ctypes.byref(p), ctypes.byref(cv), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                           _ptr(beta), _ptr(state), _ptr(mask_dev), _ptr(o), _ptr(gate),
+                                           _ptr(norm_weight), _ptr(y), _stream(dev)))
+    elif states is None:
         _check(lib.kda_recurrent_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                       _ptr(state), _ptr(mask_dev), _ptr(o), _ptr(gate), _ptr(norm_weight),
                                       _ptr(y), _stream(dev)))
@@ -497,6 +578,19 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
                                         _ptr(state), _ptr(mask_dev), _ptr(o), _ptr(gate), _ptr(norm_weight),
                                         _ptr(y), _ptr(states), _stream(dev)))
     return o if y is None else (o, y)
+
+
+def recurrent_step_conv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                        beta: torch.Tensor, state: torch.Tensor, *, conv_weights, conv_state=None,
+                        conv_final_state=None, with_conv_state: bool = True, activation: Optional[str] = "silu",
+                        **kw):
+    """recurrent_step on the raw q, k, v of the new tokens: each is filtered with the row's
+    carried inputs conv_state = (q, k, v) [B, W-1, H*d] (or None: zeros) inside the kernel.
+    Returns recurrent_step's result and the (q, k, v) carried inputs after the call; pass the
+    same tensors as conv_state and conv_final_state to update them in place (decode)."""
+    spec = _ConvSpec(conv_weights, conv_state, conv_final_state, with_conv_state, activation)
+    res = recurrent_step(q, k, v, g, beta, state, _conv=spec, **kw)
+    return res, spec.final
 
 
 def gated_rmsnorm(x: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *,

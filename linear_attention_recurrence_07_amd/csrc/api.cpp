@@ -138,15 +138,40 @@ kda_status_t check_workspace(const kda_params_t *p, const int32_t *cu, const voi
   return check_ptr(ws, "workspace", false);
 }
 
-}  // namespace
+// The fused short convolution: filter width and activation, taps of q, k and v, and the
+// optional carried inputs before and after the call.
+kda_status_t check_conv(const kda_conv_t *c, const kda_params_t *p, int N) {
+  if (c == nullptr) return fail(KDA_ERR_NULL, "conv is NULL");
+  if (c->activation != 0 && c->activation != 1) return fail(KDA_ERR_SHAPE, "conv activation must be 0 or 1");
+  if (c->width < 2 || c->width > 4) return fail(KDA_ERR_UNSUPPORTED, "conv width %d not in 2..4", c->width);
+  KDA_TRY(check_ptr(c->weight_q, "conv weight_q", true));
+  KDA_TRY(check_ptr(c->weight_k, "conv weight_k", true));
+  KDA_TRY(check_ptr(c->weight_v, "conv weight_v", true));
+  KDA_TRY(check_ptr(c->initial_q, "conv initial_q", false));
+  KDA_TRY(check_ptr(c->initial_k, "conv initial_k", false));
+  KDA_TRY(check_ptr(c->initial_v, "conv initial_v", false));
+  KDA_TRY(check_ptr(c->final_q, "conv final_q", false));
+  KDA_TRY(check_ptr(c->final_k, "conv final_k", false));
+  KDA_TRY(check_ptr(c->final_v, "conv final_v", false));
+  if (p->dk != p->dv) return fail(KDA_ERR_UNSUPPORTED, "the fused convolution needs dk == dv");
+  if (N > 65535) return fail(KDA_ERR_UNSUPPORTED, "the fused convolution takes at most 65535 sequences");
+  return KDA_OK;
+}
 
-extern "C" {
+void set_conv(kda::Args &a, const kda_conv_t *c) {
+  a.conv.W = c->width;
+  a.conv.silu = c->activation;
+  a.conv.w[0] = c->weight_q; a.conv.w[1] = c->weight_k; a.conv.w[2] = c->weight_v;
+  a.conv.init[0] = c->initial_q; a.conv.init[1] = c->initial_k; a.conv.init[2] = c->initial_v;
+  a.conv.fin[0] = c->final_q; a.conv.fin[1] = c->final_k; a.conv.fin[2] = c->final_v;
+}
 
-kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void *k, const void *v,
-                               const float *g, const float *beta, const float *initial_state,
-                               const int32_t *cu_seqlens, const uint8_t *mask, void *o,
-                               float *final_state, const void *gate, const float *norm_weight,
-                               void *y, void *workspace, size_t workspace_bytes, void *stream) {
+// Shared body of kda_chunk_prefill (conv NULL) and kda_chunk_prefill_conv.
+kda_status_t prefill_impl(const kda_params_t *p, const kda_conv_t *conv, bool with_conv, const void *q,
+                          const void *k, const void *v, const float *g, const float *beta,
+                          const float *initial_state, const int32_t *cu_seqlens, const uint8_t *mask, void *o,
+                          float *final_state, const void *gate, const float *norm_weight, void *y,
+                          void *workspace, size_t workspace_bytes, void *stream) {
   KDA_TRY(check_params(p, true));
   KDA_TRY(check_ptr(q, "q", true));
   KDA_TRY(check_ptr(k, "k", true));
@@ -166,6 +191,13 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int chunk = p->chunk;
   const bool mfma = use_mfma_prefill(p);
+  if (with_conv) {
+    KDA_TRY(check_conv(conv, p, a.N));
+    if (!mfma)
+      return fail(KDA_ERR_UNSUPPORTED, "the fused convolution runs in the bf16, dk = dv = 128 matrix-core prefill "
+                                       "(chunk 0, 32 or 64); for other shapes run kda_short_conv first");
+    set_conv(a, conv);
+  }
   if (!mfma) {
     if (!kda::prefill_valu_supports(p->dk, p->dv))
       return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dk=%d dv=%d", p->dk, p->dv);
@@ -191,11 +223,35 @@ kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void 
                                                    a.out_bf16, a.in_bf16, a.out_bf16, st, tok_end, p->H),
                          "gated norm"));
     }
+    // the carried inputs after the call, once every kernel that reads the old ones is done
+    if (with_conv) KDA_TRY(hip_status(kda::launch_conv_carry(a, st), "carried convolution inputs"));
   } else {
     a.gate = gate; a.norm_w = norm_weight; a.y = y;
     KDA_TRY(hip_status(kda::launch_prefill_valu(a, st), "prefill (VALU)"));
   }
   return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_prefill(const kda_params_t *p, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *initial_state,
+                               const int32_t *cu_seqlens, const uint8_t *mask, void *o,
+                               float *final_state, const void *gate, const float *norm_weight,
+                               void *y, void *workspace, size_t workspace_bytes, void *stream) {
+  return prefill_impl(p, nullptr, false, q, k, v, g, beta, initial_state, cu_seqlens, mask, o, final_state, gate,
+                      norm_weight, y, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_prefill_conv(const kda_params_t *p, const kda_conv_t *conv, const void *q, const void *k,
+                                    const void *v, const float *g, const float *beta, const float *initial_state,
+                                    const int32_t *cu_seqlens, const uint8_t *mask, void *o, float *final_state,
+                                    const void *gate, const float *norm_weight, void *y, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  return prefill_impl(p, conv, true, q, k, v, g, beta, initial_state, cu_seqlens, mask, o, final_state, gate,
+                      norm_weight, y, workspace, workspace_bytes, stream);
 }
 
 size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed) {
@@ -267,11 +323,11 @@ kda_status_t kda_chunk_scan(const kda_params_t *p, const void *v, const float *i
   return KDA_OK;
 }
 
-// Shared body of the two token-by-token entry points.
-static kda_status_t recurrent_impl(const kda_params_t *p, const void *q, const void *k, const void *v,
-                            const float *g, const float *beta, float *state, const uint8_t *mask,
-                            void *o, const void *gate, const float *norm_weight, void *y,
-                            float *states, void *stream) {
+// Shared body of the token-by-token entry points (conv: the fused convolution, or NULL).
+static kda_status_t recurrent_impl(const kda_params_t *p, const kda_conv_t *conv, bool with_conv, const void *q,
+                                   const void *k, const void *v, const float *g, const float *beta, float *state,
+                                   const uint8_t *mask, void *o, const void *gate, const float *norm_weight,
+                                   void *y, float *states, void *stream) {
   KDA_TRY(check_params(p, false));
   KDA_TRY(check_ptr(q, "q", true));
   KDA_TRY(check_ptr(k, "k", true));
@@ -284,13 +340,20 @@ static kda_status_t recurrent_impl(const kda_params_t *p, const void *q, const v
   KDA_TRY(check_norm(gate, norm_weight, y, p->dv));
   if (!kda::recurrent_supports(p->dk, p->dv))
     return fail(KDA_ERR_UNSUPPORTED, "no recurrent kernel for dk=%d dv=%d", p->dk, p->dv);
-  if (p->T == 0) return KDA_OK;
+  if (with_conv) KDA_TRY(check_conv(conv, p, p->B));
   kda::Args a = make_args(p);
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.state = state; a.mask = mask; a.o = o;
   a.gate = gate; a.norm_w = norm_weight; a.y = y;
   a.states_out = states;
-  KDA_TRY(hip_status(kda::launch_recurrent(a, static_cast<hipStream_t>(stream)), "recurrent step"));
+  if (with_conv) set_conv(a, conv);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p->T == 0) {
+    // no token: the carried inputs stay as they were (copied when the buffers differ)
+    if (with_conv) KDA_TRY(hip_status(kda::launch_conv_carry(a, st), "carried convolution inputs"));
+    return KDA_OK;
+  }
+  KDA_TRY(hip_status(kda::launch_recurrent(a, st), "recurrent step"));
   return KDA_OK;
 }
 
@@ -298,7 +361,14 @@ kda_status_t kda_recurrent_step(const kda_params_t *p, const void *q, const void
                                 const float *g, const float *beta, float *state,
                                 const uint8_t *mask, void *o, const void *gate,
                                 const float *norm_weight, void *y, void *stream) {
-  return recurrent_impl(p, q, k, v, g, beta, state, mask, o, gate, norm_weight, y, nullptr, stream);
+  return recurrent_impl(p, nullptr, false, q, k, v, g, beta, state, mask, o, gate, norm_weight, y, nullptr, stream);
+}
+
+kda_status_t kda_recurrent_step_conv(const kda_params_t *p, const kda_conv_t *conv, const void *q, const void *k,
+                                     const void *v, const float *g, const float *beta, float *state,
+                                     const uint8_t *mask, void *o, const void *gate, const float *norm_weight,
+                                     void *y, void *stream) {
+  return recurrent_impl(p, conv, true, q, k, v, g, beta, state, mask, o, gate, norm_weight, y, nullptr, stream);
 }
 
 kda_status_t kda_recurrent_states(const kda_params_t *p, const void *q, const void *k, const void *v,
@@ -306,7 +376,7 @@ kda_status_t kda_recurrent_states(const kda_params_t *p, const void *q, const vo
                                   const uint8_t *mask, void *o, const void *gate,
                                   const float *norm_weight, void *y, float *states, void *stream) {
   KDA_TRY(check_ptr(states, "states", true));
-  return recurrent_impl(p, q, k, v, g, beta, state, mask, o, gate, norm_weight, y, states, stream);
+  return recurrent_impl(p, nullptr, false, q, k, v, g, beta, state, mask, o, gate, norm_weight, y, states, stream);
 }
 
 kda_status_t kda_gated_rmsnorm(const void *x, const void *gate, const float *weight, void *y,

@@ -31,6 +31,8 @@
 // bf16 hi + lo parts, three products), the sub-block boundary for the off-diagonal block
 // (both factors <= 1, fp16).  The diagonal blocks of I + A are inverted by forward
 // substitution; the off-diagonal block of W comes from two fp32 matrix-core products.
+#include <type_traits>
+
 #include "kda_chunk.h"
 #include "kda_launch.h"
 
@@ -52,15 +54,26 @@ struct Shared {
 };
 static_assert(sizeof(Shared) <= 20 * 1024, "LDS per work-group");
 
+constexpr int kNoInput = -0x40000000;   // a window entry that reads zeros
+
 // G_HEAD: g holds one decay per (token, head), shared by every key channel.
-template <bool HAS_MASK, bool G_HEAD>
+// CONV: q and k are the raw projections; the kernel runs their short convolution (cv).
+template <bool HAS_MASK, bool G_HEAD, bool CONV>
 __global__ void __launch_bounds__(NT)
 chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                   const float *__restrict__ g, const float *__restrict__ beta,
                   const int32_t *__restrict__ cu, const uint8_t *__restrict__ mask,
                   Rec *__restrict__ ws, uint64_t *__restrict__ xs, uint32_t *__restrict__ status, int T, int H,
-                  int N, float scale, int use_l2) {
-  __shared__ Shared sh;
+                  int N, float scale, int use_l2, ConvIn cv) {
+  // CONV: the filtered q (0) and k (1) of the chunk, fp32 [token][channel], in the space of
+  // the shared arrays below (they are first written after the last read of these)
+  union SmemU {
+    Shared s;
+    float cst[CONV ? 2 : 1][CONV ? C : 1][DK + 4];
+  };
+  __shared__ SmemU smu;
+  Shared &sh = smu.s;
+  auto &cst = smu.cst;
   const int tid = threadIdx.x, lane = tid & 63;
   if (blockIdx.x == 0 && tid == 0) *status = 0u;   // no wait of the coming scan has run out yet
   const int m = __builtin_amdgcn_readfirstlane(tid >> 6);   // sub-block of this wave
@@ -69,7 +82,7 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
   // ---------------------------------------------------------------- locate the chunk
   const int h = static_cast<int>(blockIdx.x) % H;
   const int slot = static_cast<int>(blockIdx.x) / H;
-  int b, t_begin, t_end, c;
+  int b, t_begin, t_end, c, nseq;
   if (cu) {
     // largest n whose first slot is <= slot (first slots increase with n)
     int lo = 0, hi = N - 1;
@@ -82,12 +95,14 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     t_end = min(cu[lo + 1], T);
     t_begin = max(0, min(cu[lo], t_end));
     c = slot - (lo + min(max(cu[lo], 0), T) / C);
+    nseq = lo;
   } else {
     const int nch = (T + C - 1) / C;
     b = slot / nch;
     c = slot - b * nch;
     t_begin = 0;
     t_end = T;
+    nseq = b;
   }
   if (c < 0 || c * C >= t_end - t_begin) return;   // no chunk in this slot (whole work-group)
   const int c0 = t_begin + c * C;
@@ -95,6 +110,129 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
   // clear the chunk's words of the scan's norm exchange (2 tiles x 32 tokens)
   if (tid < 32) reinterpret_cast<u32x4 *>(xs + (static_cast<size_t>(slot) * H + h) * 64)[tid] = u32x4{0u, 0u, 0u, 0u};
   const size_t row0 = static_cast<size_t>(b) * T;
+
+  // ---------------------------------------------------------------- fused short convolution
+  // CONV (Kimi-K3 atlas, KDA layer page, kda-init code: a causal ShortConvolution with SiLU
+  // on each projection; nnterp Kimi-Linear page, Notes: the layer carries its last inputs
+  // outside the state).  Wave 0 filters q and wave 1 k over the chunk; lane (tg, cg) takes
+  // channels 8 cg .. 8 cg + 7 of tokens 8 tg .. 8 tg + 7.  Its window starts with the three
+  // newest real tokens before its first one (padding never enters it), reaching back
+  // before the chunk and then into the carried inputs of the sequence, and slides over its
+  // real tokens.  The outputs go to LDS in fp32, where the loads below take them in
+  // operand order instead of the inputs (no bf16 rounding: a filtered value lying at a
+  // bf16 rounding midpoint would otherwise round either way depending on the last bits of
+  // its fp32 computation, and the recurrence can be sensitive to one unit of a key).
+  if constexpr (CONV) {
+    const int cg = lane & 15, tg = lane >> 4;
+    const int W = cv.W;
+    const uint16_t *xin = m == 0 ? q : k;
+    const uint16_t *xinit = static_cast<const uint16_t *>(m == 0 ? cv.init[0] : cv.init[1]);
+    const size_t dstride = static_cast<size_t>(H) * DK;             // elements between tokens
+    const size_t chan = static_cast<size_t>(h) * DK + 8 * cg;
+    // the chunk's real tokens (bit i: token c0 + i)
+    uint32_t vbits;
+    {
+      const int tt = c0 + (lane & 31);
+      bool ok = tt < t_end;
+      if constexpr (HAS_MASK) ok = ok && mask[row0 + min(tt, t_end - 1)] != 0;
+      vbits = static_cast<uint32_t>(__ballot(ok));
+    }
+    // Sources of the three newest inputs before the chunk, newest first: a token of the
+    // row (>= 0), carried input j (-1 - j), or zeros (kNoInput).
+    int p0 = kNoInput, p1 = kNoInput, p2 = kNoInput, cnt = 0;
+    auto push = [&](int src) {   // selects, not branches: kept in registers
+      p0 = cnt == 0 ? src : p0;
+      p1 = cnt == 1 ? src : p1;
+      p2 = cnt == 2 ? src : p2;
+      ++cnt;
+    };
+    if constexpr (HAS_MASK) {
+      // 64 tokens at a time, back from the chunk start, until three real ones are found
+      for (int base = c0 - 1; base >= t_begin && cnt < 3; base -= 64) {
+        const int t = base - lane;
+        const bool ok = t >= t_begin && mask[row0 + max(t, 0)] != 0;
+        uint64_t bal = __ballot(ok);
+        while (bal != 0 && cnt < 3) {
+          push(base - __builtin_ctzll(bal));
+          bal &= bal - 1;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 1; j <= 3; ++j)
+        if (c0 - j >= t_begin) push(c0 - j);
+    }
+    // the j-th newest carried input is entry W-1-j of the sequence's carried inputs
+    for (int j = 1; cnt < 3; ++j) push(xinit != nullptr && j <= W - 1 ? -1 - (W - 1 - j) : kNoInput);
+    // this lane's window before token c0 + 8 tg: real tokens of the chunk before it, then p
+    uint32_t below = vbits & ((1u << (8 * tg)) - 1u);
+    auto pop_top = [&]() -> int {
+      if (below == 0u) return -1;
+      const int i = 31 - __builtin_clz(below);
+      below &= ~(1u << i);
+      return i;
+    };
+    const int i0 = pop_top(), i1 = pop_top(), i2 = pop_top();
+    const int nin = (i0 >= 0) + (i1 >= 0) + (i2 >= 0);
+    const int s0 = nin >= 1 ? c0 + i0 : p0;
+    const int s1 = nin >= 2 ? c0 + i1 : (nin == 1 ? p0 : p1);
+    const int s2 = nin >= 3 ? c0 + i2 : (nin == 2 ? p0 : (nin == 1 ? p1 : p2));
+    auto load_src = [&](int src) -> u32x4 {
+      if (src >= 0) return *reinterpret_cast<const u32x4 *>(xin + (row0 + src) * dstride + chan);
+      if (src == kNoInput) return u32x4{0u, 0u, 0u, 0u};
+      return *reinterpret_cast<const u32x4 *>(xinit + (static_cast<size_t>(nseq) * (W - 1) + (-1 - src)) * dstride + chan);
+    };
+    u32x4 rows[8];
+    const int tt0 = c0 + 8 * tg;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rows[i] = load_src(min(tt0 + i, t_end - 1));
+    const u32x4 w2 = load_src(s0), w1 = load_src(s1), w0 = load_src(s2);
+    float tap[8][4];
+    const float *wp = (m == 0 ? cv.w[0] : cv.w[1]) + chan * W;
+    if (W == 4) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const f32x4 t4 = *reinterpret_cast<const f32x4 *>(wp + 4 * i);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) tap[i][jj] = t4[jj];
+      }
+    } else {
+      // right-aligned: slot jj holds weight jj - (4 - W)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) tap[i][jj] = jj >= 4 - W ? wp[i * W + jj - (4 - W)] : 0.f;
+    }
+    auto unpack = [](u32x4 w, float (&x)[8]) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = lo_bf16(w[e]);
+        x[2 * e + 1] = hi_bf16(w[e]);
+      }
+    };
+    float h0[8], h1[8], h2[8];   // the window, oldest first
+    unpack(w0, h0);
+    unpack(w1, h1);
+    unpack(w2, h2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool ok = (vbits >> (8 * tg + i)) & 1u;
+      float x[8], z[8];
+      unpack(rows[i], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        z[e] = conv_z(tap[e], h0[e], h1[e], h2[e], x[e], W);
+        if (cv.silu) z[e] = silu_act(z[e]);
+        z[e] = ok ? z[e] : 0.f;
+        h0[e] = ok ? h1[e] : h0[e];
+        h1[e] = ok ? h2[e] : h1[e];
+        h2[e] = ok ? x[e] : h2[e];
+      }
+      *reinterpret_cast<f32x4 *>(&cst[m][8 * tg + i][8 * cg]) = f32x4{z[0], z[1], z[2], z[3]};
+      *reinterpret_cast<f32x4 *>(&cst[m][8 * tg + i][8 * cg + 4]) = f32x4{z[4], z[5], z[6], z[7]};
+    }
+    sync_lds();
+  }
 
   // ---------------------------------------------------------------- load (operand order)
   const int tok = c0 + SB * m + r;
@@ -110,11 +248,25 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
   const float *gp = G_HEAD ? g + (row0 + tcl) * H + h : g + row0 * H * DK + off;
   u32x2 kr[4][2], qr[4][2];
   u32x4 kw[4], qw[4];
+  // CONV: the filtered k and q in operand order, fp32: slot e of K block s is channel
+  // 32 s + kidx(lg, e) (read straight from LDS in that order)
+  f32x4 kf[CONV ? 4 : 1][2], qf[CONV ? 4 : 1][2];
   f32x4 G[4][2];
+  if constexpr (CONV) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    kw[s] = *reinterpret_cast<const u32x4 *>(kp + 32 * s);
-    qw[s] = *reinterpret_cast<const u32x4 *>(qp + 32 * s);
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        kf[s][hh] = *reinterpret_cast<const f32x4 *>(&cst[1][SB * m + r][32 * s + 16 * hh + 4 * lg]);
+        qf[s][hh] = *reinterpret_cast<const f32x4 *>(&cst[0][SB * m + r][32 * s + 16 * hh + 4 * lg]);
+      }
+    sync_lds();   // every read of the filtered values is done before the shared arrays are written
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kw[s] = *reinterpret_cast<const u32x4 *>(kp + 32 * s);
+      qw[s] = *reinterpret_cast<const u32x4 *>(qp + 32 * s);
+    }
   }
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -128,10 +280,12 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
       }
     }
   const float bt = beta[(row0 + tcl) * H + h];
+  if constexpr (!CONV) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    operand_halves(kw[s], kr[s][0], kr[s][1]);
-    operand_halves(qw[s], qr[s][0], qr[s][1]);
+    for (int s = 0; s < 4; ++s) {
+      operand_halves(kw[s], kr[s][0], kr[s][1]);
+      operand_halves(qw[s], qr[s][0], qr[s][1]);
+    }
   }
 
   // ---------------------------------------------------------------- norms, running sums
@@ -145,8 +299,14 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
-          const float k0 = lo_bf16(kr[s][hh][w]), k1 = hi_bf16(kr[s][hh][w]);
-          const float q0 = lo_bf16(qr[s][hh][w]), q1 = hi_bf16(qr[s][hh][w]);
+          float k0, k1, q0, q1;
+          if constexpr (CONV) {
+            k0 = kf[s][hh][2 * w]; k1 = kf[s][hh][2 * w + 1];
+            q0 = qf[s][hh][2 * w]; q1 = qf[s][hh][2 * w + 1];
+          } else {
+            k0 = lo_bf16(kr[s][hh][w]); k1 = hi_bf16(kr[s][hh][w]);
+            q0 = lo_bf16(qr[s][hh][w]); q1 = hi_bf16(qr[s][hh][w]);
+          }
           ssk += k0 * k0 + k1 * k1;
           ssq += q0 * q0 + q1 * q1;
         }
@@ -171,12 +331,20 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
   }
   if (lg == 0) sh.sb[SB * m + r] = valid ? bt : 0.f;
   auto kval = [&](int s, int e) {
-    const uint32_t w = kr[s][e >> 2][(e >> 1) & 1];
-    return (e & 1 ? hi_bf16(w) : lo_bf16(w)) * nk;
+    if constexpr (CONV) {
+      return kf[s][e >> 2][e & 3] * nk;
+    } else {
+      const uint32_t w = kr[s][e >> 2][(e >> 1) & 1];
+      return (e & 1 ? hi_bf16(w) : lo_bf16(w)) * nk;
+    }
   };
   auto qval = [&](int s, int e) {
-    const uint32_t w = qr[s][e >> 2][(e >> 1) & 1];
-    return (e & 1 ? hi_bf16(w) : lo_bf16(w)) * nq;
+    if constexpr (CONV) {
+      return qf[s][e >> 2][e & 3] * nq;
+    } else {
+      const uint32_t w = qr[s][e >> 2][(e >> 1) & 1];
+      return (e & 1 ? hi_bf16(w) : lo_bf16(w)) * nq;
+    }
   };
   if (m == 0) {
     // sub-block 0's off-diagonal operand k^ exp(G_15 - G), needed by the other wave
@@ -287,14 +455,17 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     for (int i = 0; i < 4; ++i) w[i] = (r < 4 * lg + i) ? bm[i] * accA[i] : 0.f;
     *reinterpret_cast<f32x4 *>(&sh.at[m][r][4 * lg]) = w;
     // accB[i] = Bqk[r][4 lg + i] of this sub-block (query row r, key column 4 lg + i)
-    float bd[4];
+    f32x4 bd;
 #pragma unroll
     for (int i = 0; i < 4; ++i) bd[i] = (4 * lg + i <= r) ? accB[i] : 0.f;
-    const u32x2 diag = {pack_f16x2(bd[0], bd[1]), pack_f16x2(bd[2], bd[3])};
-    const u32x2 left = m ? u32x2{pack_f16x2(accB10[0], accB10[1]), pack_f16x2(accB10[2], accB10[3])}
-                         : u32x2{0u, 0u};
+    // hi + lo parts: the outputs are often much smaller than the two terms they are the
+    // sum of (q^ exp(G) S0 and Bqk U), so Bqk's own rounding must stay far below fp16's
+    u32x2 diag, diagl, left = {0u, 0u}, leftl = {0u, 0u};
+    split4(bd, diag, diagl);
+    if (m) split4(accB10, left, leftl);
     // row r of bq[m]: slots 0-3 = key tokens 4 lg + i, slots 4-7 = key tokens 16 + 4 lg + i
     reinterpret_cast<u32x4 *>(rec->bq[m])[lane] = m ? cat(left, diag) : cat(diag, u32x2{0u, 0u});
+    reinterpret_cast<u32x4 *>(rec->bqlo[m])[lane] = m ? cat(leftl, diagl) : cat(diagl, u32x2{0u, 0u});
     if (m) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) sh.a10[4 * lg + i][r] = bm[i] * accA10[i];
@@ -400,20 +571,23 @@ hipError_t launch_chunk_prep(const Args &a, void *ws, hipStream_t st) {
   uint64_t *xs = chunk_exchange_words(ws, a.B, a.T, a.H, a.N, a.cu != nullptr);
   uint32_t *status = chunk_status_word(ws, a.B, a.T, a.H, a.N, a.cu != nullptr);
   const dim3 grid(static_cast<unsigned>(blocks));
+  auto go = [&](auto mask_t, auto ghead_t, auto conv_t) {
+    hipLaunchKernelGGL((chunk_prep_kernel<decltype(mask_t)::value, decltype(ghead_t)::value, decltype(conv_t)::value>),
+                       grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask, rec, xs, status, a.T, a.H, a.N,
+                       a.scale, a.use_l2, a.conv);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  auto go2 = [&](auto mask_t, auto ghead_t) {
+    if (a.conv.W > 0) go(mask_t, ghead_t, T_{});
+    else go(mask_t, ghead_t, F_{});
+  };
   if (a.g_head) {
-    if (a.mask)
-      hipLaunchKernelGGL((chunk_prep_kernel<true, true>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                         rec, xs, status, a.T, a.H, a.N, a.scale, a.use_l2);
-    else
-      hipLaunchKernelGGL((chunk_prep_kernel<false, true>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                         rec, xs, status, a.T, a.H, a.N, a.scale, a.use_l2);
+    if (a.mask) go2(T_{}, T_{});
+    else go2(F_{}, T_{});
   } else {
-    if (a.mask)
-      hipLaunchKernelGGL((chunk_prep_kernel<true, false>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                         rec, xs, status, a.T, a.H, a.N, a.scale, a.use_l2);
-    else
-      hipLaunchKernelGGL((chunk_prep_kernel<false, false>), grid, dim3(NT), 0, st, q, k, a.g, a.beta, a.cu, a.mask,
-                         rec, xs, status, a.T, a.H, a.N, a.scale, a.use_l2);
+    if (a.mask) go2(T_{}, F_{});
+    else go2(F_{}, F_{});
   }
   return hipGetLastError();
 }

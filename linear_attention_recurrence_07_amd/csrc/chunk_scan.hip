@@ -47,9 +47,13 @@
 // bounded (about 2^22 polls, seconds): one that runs out gives NaN in y instead of a
 // hang and sets the workspace's status word, which kda_chunk_prefill_status reports.
 //
-// Precision: fp16 operands for the state, the decayed keys/queries and V - K S0; W and U
-// as fp16 hi + lo parts; fp32 accumulation.  The fp16 state operand limits |S| to well
-// inside fp16 range.
+// Precision: fp16 operands for the state and the decayed keys/queries; W, U, Bqk and
+// V - K S0 as fp16 hi + lo parts; fp32 accumulation.  The outputs can be far smaller than
+// the terms they are the sum of (when the state already predicts the values well, as with
+// filtered inputs that share a common direction), so the parts of those terms carry more
+// than fp16's precision.  The fp16 state operand limits |S| to well inside fp16 range.
+#include <type_traits>
+
 #include "kda_chunk.h"
 #include "kda_launch.h"
 
@@ -71,31 +75,39 @@ constexpr int kSpinLimit = 1 << 22;   // polls of a partner's word before giving
 constexpr int PPT = (REC_PIECES + NHT - 1) / NHT;   // record pieces per helper thread (8)
 static_assert(NCW == 4 && NHT == 256, "thread mappings");
 
+constexpr int LDVF = DVT + 4;     // fp32 value tile row stride
+// F32V: the value tile holds fp32 values (the filtered values of the fused convolution)
+template <bool F32V>
 struct alignas(16) Hand {
   Rec rec;
-  uint16_t vt[C * LDV];        // bf16 value tile [token][column]
+  typename std::conditional<F32V, float, uint16_t>::type vt[C * (F32V ? LDVF : LDV)];   // [token][column]
 };
-template <int NOST>
+template <int NOST, bool CONV>
 struct alignas(16) Smem {
-  Hand hand[2];
+  Hand<CONV> hand[2];
   float ost[NOST][C * LDO];    // fp32 output tiles: chunk c in ost[c % NOST]
   float pss[2][C];             // NORM: the partner tile's sums of squares, chunk c in pss[c & 1]
+  // CONV: raw value rows of chunk c in raw[c & 1][3 ..], after the three newest real
+  // inputs before the chunk (rows 0..2, oldest first)
+  uint16_t raw[CONV ? 2 : 1][CONV ? 3 + C : 1][LDV];
 };
 constexpr int kNormLag = 5;          // y of chunk c is written at step c + kNormLag
-static_assert(sizeof(Smem<kNormLag + 1>) <= 160 * 1024, "LDS budget");
-static_assert(sizeof(Hand) % 16 == 0 && (LDV * 2) % 16 == 0 && (LDO * 4) % 16 == 0, "16-byte LDS access");
+static_assert(sizeof(Smem<kNormLag + 1, true>) <= 160 * 1024, "LDS budget");
+static_assert(sizeof(Hand<false>) % 16 == 0 && sizeof(Hand<true>) % 16 == 0 && (LDV * 2) % 16 == 0 &&
+                  (LDVF * 4) % 16 == 0 && (LDO * 4) % 16 == 0, "16-byte LDS access");
 
 // NORM: also write y (gated norm over the head's 128 channels); xs holds the exchanged
 // partial sums of squares, 2 tiles x 32 tokens per (slot, head).  WRITE_O: store the head
-// outputs o (only NORM may leave them out: the caller then wants y alone).
-template <typename TOut, bool HAS_INIT, bool NORM, bool WRITE_O>
+// outputs o (only NORM may leave them out: the caller then wants y alone).  CONV: v is
+// the raw projection; the helpers run its short convolution (cv).
+template <typename TOut, bool HAS_INIT, bool NORM, bool WRITE_O, bool CONV>
 __global__ void __launch_bounds__(NT, 1)
 chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, const float *init,
                   float *fin, const int32_t *__restrict__ cu, TOut *__restrict__ o,
                   const uint16_t *__restrict__ gate, const float *__restrict__ norm_w, TOut *__restrict__ y,
-                  uint64_t *xs, uint32_t *status, float eps, int T, int H, int units) {
+                  uint64_t *xs, uint32_t *status, float eps, int T, int H, int units, ConvIn cv) {
   constexpr int NOST = NORM ? kNormLag + 1 : 2;
-  __shared__ Smem<NOST> sm;
+  __shared__ Smem<NOST, CONV> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: branches stay scalar
   const int l16 = lane & 15, lg = lane >> 4;
@@ -135,11 +147,12 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
   const uint32_t tok_bytes = static_cast<uint32_t>(H * DV) * 2u;
   const uint8_t *vrow = reinterpret_cast<const uint8_t *>(v + row0 * tok_stride);
   const Rec *rp0 = ws + slot0 * H + h;                         // chunk c's record: rp0 + c * H
+  const int last = nchunks - 1;
 
   // ================================================================ helper side
   struct Pre {
     u32x4 r[PPT];
-    u32x4 v;
+    u32x4 v;                   // the value piece of the chunk (CONV: of the next chunk)
     uint32_t valid;            // the chunk's token flags
   };
   const uint8_t *grow = reinterpret_cast<const uint8_t *>(gate + row0 * tok_stride);
@@ -154,18 +167,85 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
         pre.r[i] = *reinterpret_cast<const u32x4 *>(rpi + static_cast<uint32_t>(ht) * 16u);
     }
     pre.valid = *reinterpret_cast<const uint32_t *>(rp + offsetof(Rec, valid) + vzero);
-    const uint32_t tv = static_cast<uint32_t>(min(t_begin + cidx * C + hr, t_end - 1));
+    const int vidx = CONV ? min(cidx + 1, last) : cidx;
+    const uint32_t tv = static_cast<uint32_t>(min(t_begin + vidx * C + hr, t_end - 1));
     pre.v = *reinterpret_cast<const u32x4 *>(vrow + (piece + tv * tok_bytes));
     __asm__ volatile("" ::: "memory");   // keep the loads here, ahead of their use
   };
-  auto stage = [&](Hand &hd, const Pre &pre) {
+  auto stage = [&](Hand<CONV> &hd, const Pre &pre) {
     u32x4 *dst = reinterpret_cast<u32x4 *>(&hd.rec);
 #pragma unroll
     for (int i = 0; i < PPT; ++i)
       if (i < PPT - 1 || ht + NHT * i < REC_PIECES) dst[ht + NHT * i] = pre.r[i];
     // values of padding and of tokens past the end are zeroed
-    const bool keep = (pre.valid >> hr) & 1u;
-    *reinterpret_cast<u32x4 *>(hd.vt + hr * LDV + hc8) = keep ? pre.v : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (!CONV) {
+      const bool keep = (pre.valid >> hr) & 1u;
+      *reinterpret_cast<u32x4 *>(&hd.vt[hr * LDV + hc8]) = keep ? pre.v : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  // ================================================================ short convolution (helpers)
+  // CONV (Kimi-K3 atlas, KDA layer page, kda-init code: a causal ShortConvolution with
+  // SiLU on the value projection).  The value tile of a chunk is filtered from its raw rows
+  // in LDS one step after they were written there, and handed to the compute waves in fp32.  A chunk's raw area starts with the
+  // three newest real inputs before it, so a token's window is the newest real rows
+  // before it in that area (its flags: the chunk's, with the three rows in front always
+  // real); the next chunk's three rows are taken from the same area.  Padding therefore
+  // never enters a window, and the window needs no look-back past one chunk.  At the
+  // sequence start the three rows are its carried inputs (or zeros).
+  float ctap[8][4];            // right-aligned taps of this thread's 8 value channels
+  if constexpr (CONV) {
+    if (helper) {
+      const float *wp = cv.w[2] + (static_cast<size_t>(h) * DV + col0 + hc8) * cv.W;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) ctap[i][jj] = jj >= 4 - cv.W ? wp[i * cv.W + jj - (4 - cv.W)] : 0.f;
+    }
+  }
+  auto put_raw = [&](int buf, u32x4 w) { *reinterpret_cast<u32x4 *>(&sm.raw[buf][3 + hr][hc8]) = w; };
+  // Filter chunk buf's tile into hd.vt (token hr, columns hc8..hc8+7), in fp32.
+  auto conv_tile = [&](Hand<CONV> &hd, int buf, uint32_t valid) {
+    const uint64_t ext = (static_cast<uint64_t>(valid) << 3) | 7u;
+    const int e = hr + 3;
+    uint64_t below = ext & ((uint64_t{1} << e) - 1u);
+    const int p1 = 63 - __builtin_clzll(below);
+    below &= ~(uint64_t{1} << p1);
+    const int p2 = 63 - __builtin_clzll(below);
+    below &= ~(uint64_t{1} << p2);
+    const int p3 = 63 - __builtin_clzll(below);
+    const u32x4 xr = *reinterpret_cast<const u32x4 *>(&sm.raw[buf][e][hc8]);
+    const u32x4 r2 = *reinterpret_cast<const u32x4 *>(&sm.raw[buf][p1][hc8]);
+    const u32x4 r1 = *reinterpret_cast<const u32x4 *>(&sm.raw[buf][p2][hc8]);
+    const u32x4 r0 = *reinterpret_cast<const u32x4 *>(&sm.raw[buf][p3][hc8]);
+    float z[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int w = i >> 1;
+      auto el = [&](u32x4 x) { return (i & 1) ? hi_bf16(x[w]) : lo_bf16(x[w]); };
+      z[i] = conv_z(ctap[i], el(r0), el(r1), el(r2), el(xr), cv.W);
+      if (cv.silu) z[i] = silu_act(z[i]);
+    }
+    const bool keep = (valid >> hr) & 1u;
+    if constexpr (CONV) {
+      float *dst = hd.vt + hr * LDVF + hc8;
+      reinterpret_cast<float4 *>(dst)[0] = keep ? make_float4(z[0], z[1], z[2], z[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+      reinterpret_cast<float4 *>(dst)[1] = keep ? make_float4(z[4], z[5], z[6], z[7]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  // The three newest real rows of chunk area `from` (flags `valid`) become rows 0..2 of
+  // area `to` (threads 0..23: row ht/8).
+  auto carry = [&](int from, int to, uint32_t valid) {
+    if (ht < 24) {
+      uint64_t ext = (static_cast<uint64_t>(valid) << 3) | 7u;
+      const int q1 = 63 - __builtin_clzll(ext);
+      ext &= ~(uint64_t{1} << q1);
+      const int q2 = 63 - __builtin_clzll(ext);
+      ext &= ~(uint64_t{1} << q2);
+      const int q3 = 63 - __builtin_clzll(ext);
+      const int src = hr == 2 ? q1 : (hr == 1 ? q2 : q3);
+      *reinterpret_cast<u32x4 *>(&sm.raw[to][hr][hc8]) = *reinterpret_cast<const u32x4 *>(&sm.raw[from][src][hc8]);
+    }
   };
   // Token ht/8 of chunk cidx, columns (ht%8)*8..+7 of the tile.
   auto store_row = [&](TOut *dst, int t, float4 x0, float4 x1) {
@@ -291,11 +371,12 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
   // One chunk's products.  The LDS reads of each phase are issued together ahead of their
   // first use (the empty asm statements keep them there), so their latency overlaps the
   // matrix-core work of the previous phase instead of stalling each product.
-  auto products = [&](const Hand &hc, float *ost) {
+  auto products = [&](const Hand<CONV> &hc, float *ost) {
     const u32x4 *KB = reinterpret_cast<const u32x4 *>(hc.rec.kb);
     const u32x4 *QT = reinterpret_cast<const u32x4 *>(hc.rec.qt);
     const u32x4 *KE = reinterpret_cast<const u32x4 *>(hc.rec.ket);
     const u32x4 *BQ = reinterpret_cast<const u32x4 *>(hc.rec.bq);
+    const u32x4 *BQL = reinterpret_cast<const u32x4 *>(hc.rec.bqlo);
     // Every operand of the chunk is read at the start, in order of first use; each
     // phase then waits only for its own part.
     uint4 kbf[8];
@@ -309,18 +390,23 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vv[m][i] = bf16_to_f32(hc.vt[(SB * m + 4 * lg + i) * LDV + wcol]);
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (CONV) vv[m][i] = hc.vt[(SB * m + 4 * lg + i) * LDVF + wcol];
+        else vv[m][i] = bf16_to_f32(hc.vt[(SB * m + 4 * lg + i) * LDV + wcol]);
+      }
     uint4 kef[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) kef[t] = __builtin_bit_cast(uint4, KE[t * 64 + lane]);
     float4 ecv[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) ecv[t] = *reinterpret_cast<const float4 *>(hc.rec.ec + 16 * t + 4 * lg);
-    uint4 qtf[8], bqf[2];
+    uint4 qtf[8], bqf[2], bqlf[2];
 #pragma unroll
     for (int f = 0; f < 8; ++f) qtf[f] = __builtin_bit_cast(uint4, QT[f * 64 + lane]);
 #pragma unroll
     for (int m = 0; m < 2; ++m) bqf[m] = __builtin_bit_cast(uint4, BQ[m * 64 + lane]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) bqlf[m] = __builtin_bit_cast(uint4, BQL[m * 64 + lane]);
     __asm__ volatile("" ::: "memory");
     // Y = V - (k^ exp(G)) S0 in fp16 (W carries the extra precision)
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
@@ -329,15 +415,18 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
       acc0 = mfma_f16(kbf[s], Sh[s], acc0);
       acc1 = mfma_f16(kbf[4 + s], Sh[s], acc1);
     }
-    uint2 yf[2];
-    yf[0] = pack_f16x4(vv[0][0] - acc0[0], vv[0][1] - acc0[1], vv[0][2] - acc0[2], vv[0][3] - acc0[3]);
-    yf[1] = pack_f16x4(vv[1][0] - acc1[0], vv[1][1] - acc1[1], vv[1][2] - acc1[2], vv[1][3] - acc1[3]);
-    // U0 = W00 Y0, U1 = W10 Y0 + W11 Y1, with W as hi + lo parts
+    // Y as hi + lo parts too: the delta rule's residual is often much smaller than V
+    uint2 yf[2], yl[2];
+    split_f16x4(f32x4{vv[0][0] - acc0[0], vv[0][1] - acc0[1], vv[0][2] - acc0[2], vv[0][3] - acc0[3]}, yf[0], yl[0]);
+    split_f16x4(f32x4{vv[1][0] - acc1[0], vv[1][1] - acc1[1], vv[1][2] - acc1[2], vv[1][3] - acc1[3]}, yf[1], yl[1]);
+    // U0 = W00 Y0, U1 = W10 Y0 + W11 Y1, with W and Y as hi + lo parts (lo x lo dropped)
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     f32x4 U0 = mfma_f16k16(w00l, yf[0], zero);
+    U0 = mfma_f16k16(w00, yl[0], U0);
     U0 = mfma_f16k16(w00, yf[0], U0);
-    const uint4 y01 = join(yf[0], yf[1]);
+    const uint4 y01 = join(yf[0], yf[1]), yl01 = join(yl[0], yl[1]);
     f32x4 U1 = mfma_f16(w1l, y01, zero);
+    U1 = mfma_f16(w1, yl01, U1);
     U1 = mfma_f16(w1, y01, U1);
     // the decay over the chunk, applied while the products above run
 #pragma unroll
@@ -362,6 +451,7 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
 #pragma unroll
       for (int s = 0; s < DK / 32; ++s) acc = mfma_f16(qtf[4 * m + s], Sh[s], acc);
       acc = mfma_f16(bqf[m], Ul, acc);
+      acc = mfma_f16(bqlf[m], Uh, acc);
       acc = mfma_f16(bqf[m], Uh, acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) ost[(SB * m + 4 * lg + i) * LDO + wcol] = acc[i];
@@ -373,12 +463,33 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
   // register set and write chunk s-1's rows; compute waves run chunk s.  Chunks past the
   // end repeat the last.  The two sides run separate loops with one work-group barrier
   // per step each (nchunks + 1 in all), so their loop-carried registers never overlap.
+  // CONV: the value loads run one chunk ahead of the record loads; step s also filters
+  // chunk s+1's tile (raw rows written at step s-1), carries its three newest real rows
+  // to chunk s+2's area and writes chunk s+2's raw rows there.  One more barrier before
+  // the loops puts chunk 0's raw rows in place.
   if (nchunks > 0) {
-    const int last = nchunks - 1;
     if (helper) {
       Pre pre0, pre1;                            // two sets: loads run two steps ahead
       load(pre0, 0);
       load(pre1, min(1, last));
+      if constexpr (CONV) {
+        const uint32_t tv = static_cast<uint32_t>(min(t_begin + hr, t_end - 1));
+        put_raw(0, *reinterpret_cast<const u32x4 *>(vrow + (piece + tv * tok_bytes)));
+        if (ht < 24) {
+          // row hr of the window before the sequence: its carried input W-4+hr (or zeros)
+          const int e = cv.W - 4 + hr;
+          u32x4 w = {0u, 0u, 0u, 0u};
+          if (cv.init[2] != nullptr && e >= 0)
+            w = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(cv.init[2]) +
+                                                 (static_cast<size_t>(n) * (cv.W - 1) + e) * tok_stride + h * DV +
+                                                 col0 + hc8);
+          *reinterpret_cast<u32x4 *>(&sm.raw[0][hr][hc8]) = w;
+        }
+        sync_lds();
+        conv_tile(sm.hand[0], 0, pre0.valid);
+        carry(0, 1, pre0.valid);
+        put_raw(1, pre0.v);                      // chunk 1's raw rows
+      }
       stage(sm.hand[0], pre0);
       load(pre0, min(2, last));
       // NORM: the gate pieces and flags of chunk s-5 in the set of step s's parity
@@ -390,6 +501,11 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
       sync_lds();
       auto hstep = [&](int s, Pre &from, u32x4 &gs, uint32_t &fs) {
         stage(sm.hand[(s + 1) & 1], from);
+        if constexpr (CONV) {
+          conv_tile(sm.hand[(s + 1) & 1], (s + 1) & 1, from.valid);
+          carry((s + 1) & 1, s & 1, from.valid);
+          put_raw(s & 1, from.v);                // chunk s+2's raw rows
+        }
         load(from, min(s + 3, last));
         float ss = 0.f;
         if (s >= 1) {
@@ -438,6 +554,7 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
         }
       }
     } else {
+      if constexpr (CONV) sync_lds();
       sync_lds();
       int oi = 0;
       uint64_t xw = 0;                           // NORM, wave 0: the partner's word of chunk s-4
@@ -472,10 +589,14 @@ hipError_t launch3(const Args &a, const void *ws, uint64_t *xs, uint32_t *status
   static_assert(WRITE_O || NORM, "without the norm the head outputs are the only output");
   const int units = a.N * a.H;
   const unsigned grid = static_cast<unsigned>((units + 7) / 8) * 8 * NTILE;
-  hipLaunchKernelGGL((chunk_scan_kernel<TOut, HAS_INIT, NORM, WRITE_O>), dim3(grid), dim3(NT), 0, st,
-                     static_cast<const uint16_t *>(a.v), static_cast<const Rec *>(ws), a.init, a.state, a.cu,
-                     static_cast<TOut *>(a.o), static_cast<const uint16_t *>(a.gate), a.norm_w,
-                     static_cast<TOut *>(a.y), xs, status, a.eps, a.T, a.H, units);
+  auto go = [&](auto conv_t) {
+    hipLaunchKernelGGL((chunk_scan_kernel<TOut, HAS_INIT, NORM, WRITE_O, decltype(conv_t)::value>), dim3(grid),
+                       dim3(NT), 0, st, static_cast<const uint16_t *>(a.v), static_cast<const Rec *>(ws), a.init,
+                       a.state, a.cu, static_cast<TOut *>(a.o), static_cast<const uint16_t *>(a.gate), a.norm_w,
+                       static_cast<TOut *>(a.y), xs, status, a.eps, a.T, a.H, units, a.conv);
+  };
+  if (a.conv.W > 0) go(std::true_type{});
+  else go(std::false_type{});
   return hipGetLastError();
 }
 

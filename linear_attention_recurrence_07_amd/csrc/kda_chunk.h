@@ -29,7 +29,8 @@ constexpr int SB = 16;    // tokens per sub-block
 //   kb[m*4+s]  fp16  k^ exp(G)      rows = tokens 16m.., K = channels 32s..
 //   qt[m*4+s]  fp16  q^ exp(G)      same tiling (q^ includes the query scale)
 //   ket[t]     fp16  k^ exp(G_last - G), transposed: rows = channels 16t.., K = tokens
-//   bq[m]      fp16  Bqk[r][s] = sum_c q^_rc k^_sc exp(G_rc - G_sc) (s <= r), rows 16m..
+//   bq[m], bqlo[m]  fp16  Bqk[r][s] = sum_c q^_rc k^_sc exp(G_rc - G_sc) (s <= r) as hi + lo
+//              parts, rows 16m..
 //   w1, w1lo   fp16  W = (I + A)^-1 diag(beta) as hi + lo parts, rows 16..31, K = 32 tokens
 //   w00, w00lo fp16  W rows 0..15, K = tokens 0..15 (16x16x16 operand: e < 4 only)
 //   ec[c]      fp32  exp(G_last) per key channel
@@ -41,6 +42,7 @@ struct alignas(16) Rec {
   uint16_t qt[8][64][8];
   uint16_t ket[8][64][8];
   uint16_t bq[2][64][8];
+  uint16_t bqlo[2][64][8];
   uint16_t w1[64][8];
   uint16_t w00[64][4];
   uint16_t w1lo[64][8];
@@ -49,7 +51,7 @@ struct alignas(16) Rec {
   uint32_t valid;
   uint32_t pad[3];
 };
-static_assert(sizeof(Rec) == 30224, "record layout");
+static_assert(sizeof(Rec) == 32272, "record layout");
 constexpr size_t kRecBytes = sizeof(Rec);
 // Per (slot, head): the scan's gated-norm exchange, 2 tiles x 32 tokens of 64-bit words,
 // stored after all records.

@@ -130,4 +130,22 @@ __device__ __forceinline__ void store_nt(uint16_t *p, uint4 w) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// ------------------------------------------------------------------ short convolution
+// One output of the causal width-W filter (W = 2..4) of a channel, before the activation:
+//     z = tap[3] x + tap[4-W] h[4-W] + ... + tap[2] h[2]
+// with x the current input and h[0..2] the three inputs before it (h[2] the newest).  The
+// taps are right-aligned: tap[3] is the filter's last weight (the one that meets x) and
+// tap[4-W .. 2] its first W-1, oldest first; window entries older than W-1 inputs are not
+// read.  Every kernel that filters goes through these two functions in the same order of
+// operations, so the separate and the fused convolutions give the same bits.
+__device__ __forceinline__ float conv_z(const float (&tap)[4], float h0, float h1, float h2, float x, int W) {
+  float z = tap[3] * x;
+  if (W >= 4) z = __builtin_fmaf(tap[0], h0, z);
+  if (W >= 3) z = __builtin_fmaf(tap[1], h1, z);
+  return __builtin_fmaf(tap[2], h2, z);
+}
+// z * sigmoid(z) from the hardware exp and reciprocal; 1 + e^-z = inf gives -0 for very
+// negative z.
+__device__ __forceinline__ float silu_act(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
+
 }  // namespace kda

@@ -8,6 +8,16 @@
 
 namespace kda {
 
+// The short convolution fused in front of the recurrence (q, k, v in that order): taps
+// [H * d, W] fp32, carried inputs [N, W-1, H * d] in the input dtype (or null: zeros) and
+// the carried inputs after the call (or null).  W = 0: no convolution.
+struct ConvIn {
+  const float *w[3];
+  const void *init[3];
+  void *fin[3];
+  int W, silu;
+};
+
 // Arguments of one prefill or recurrent call after host validation.
 struct Args {
   const void *q, *k, *v;
@@ -26,6 +36,7 @@ struct Args {
   int in_bf16, out_bf16;
   int g_head;                 // g is [B, T, H] (one decay per head), not [B, T, H, dk]
   float *states_out;          // recurrent: the state after every token [B, T, H, dk, dv], or null
+  ConvIn conv;                // q, k, v arrive as raw projections when conv.W > 0
 };
 
 // Arguments of one short-convolution call after host validation.
@@ -43,6 +54,10 @@ struct ConvArgs {
 
 hipError_t launch_recurrent(const Args &a, hipStream_t s);
 hipError_t launch_short_conv(const ConvArgs &a, hipStream_t s);
+// The carried inputs after a call for each of q, k and v whose a.conv.fin is set: the
+// last W-1 inputs of every sequence (padding skipped), as kda_short_conv leaves them.
+// Runs after every kernel of the call that reads a.conv.init (they may be one buffer).
+hipError_t launch_conv_carry(const Args &a, hipStream_t s);
 // Output projection out[M, N] = x[M, K] W[N, K]^T, bf16 operands, fp32 accumulation.
 bool out_proj_supports(int64_t M, int K, int N);
 size_t out_proj_workspace_bytes(int64_t M, int K, int N);

@@ -33,14 +33,18 @@ namespace {
 
 // DVW: value columns per work-group (D: whole slab; the fused norm needs whole rows).
 // STATES: also store the state after every token into `states`.
-template <int D, int DVW, int RPT, typename TIn, typename TOut, bool NORM, bool STATES>
+// CONV: q, k and v are the raw projections; the kernel runs their short convolution (cv)
+// token by token from each row's carried inputs and, for whole slabs, writes the carried
+// inputs after the call.
+template <int D, int DVW, int RPT, typename TIn, typename TOut, bool NORM, bool STATES, bool CONV>
 __global__ void __launch_bounds__((D / RPT) * (DVW / 4))
 recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
                  const float *__restrict__ g, const float *__restrict__ beta,
                  float *__restrict__ state, const uint8_t *__restrict__ mask,
                  TOut *__restrict__ o, const TIn *__restrict__ gate,
                  const float *__restrict__ norm_w, TOut *__restrict__ y,
-                 int T, int H, float scale, int use_l2, float eps, int g_head, float *__restrict__ states) {
+                 int T, int H, float scale, int use_l2, float eps, int g_head, float *__restrict__ states,
+                 ConvIn cv) {
   constexpr int CG = DVW / 4;        // column groups (float4 each)
   constexpr int RG = D / RPT;        // row groups
   constexpr int NT = RG * CG;
@@ -69,6 +73,54 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
   __shared__ float s_red[NR][NW][2][DVW];
   __shared__ float s_scal[NB][4];
 
+  // CONV: the filtered v of the tile's columns per input set, and the filter windows (the
+  // three newest real inputs, oldest first) of q, k (D channels) and v (the tile's DVW),
+  // which only wave 0 reads and writes.
+  constexpr int NB_ = DVW < D ? 3 : 1;
+  __shared__ float s_v[CONV ? NB_ : 1][CONV ? DVW : 1];
+  __shared__ float s_win[CONV ? 3 : 1][CONV ? 3 : 1][CONV ? D : 1];
+  const size_t ch_stride = static_cast<size_t>(H) * D;            // channels of a projection
+  // element of window row jj (0..2, oldest first) of channel ch in a carried-input array
+  auto carried = [&](int jj, size_t ch) {
+    return (static_cast<size_t>(b) * (cv.W - 1) + (cv.W - 4 + jj)) * ch_stride + ch;
+  };
+  if constexpr (CONV) {
+    // Wave 0 puts the windows in place before it loads its state rows (the other waves
+    // load theirs meanwhile), so the two sets of loads never hold registers together.
+    if (wave == 0) {
+#pragma unroll
+      for (int x = 0; x < 3; ++x) {
+        const TIn *init = static_cast<const TIn *>(x == 0 ? cv.init[0] : (x == 1 ? cv.init[1] : cv.init[2]));
+        if (init == nullptr) continue;
+        // row b's carried inputs of the head's (or the tile's) channels; entry W-4+jj is row jj
+        const TIn *base = init + static_cast<size_t>(b) * (cv.W - 1) * ch_stride + static_cast<size_t>(h) * D +
+                          (x == 2 ? col0 : 0);
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          const int e = lane + 64 * j;
+          if (e >= (x == 2 ? DVW : D)) continue;
+#pragma unroll
+          for (int jj = 0; jj < 3; ++jj)
+            if (jj >= 4 - cv.W)
+              s_win[x][jj][e] = Elem<TIn>::load(base, static_cast<uint32_t>((cv.W - 4 + jj) * ch_stride + e));
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 3; ++x) {
+        const void *init = x == 0 ? cv.init[0] : (x == 1 ? cv.init[1] : cv.init[2]);
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          const int e = lane + 64 * j;
+          if (e >= (x == 2 ? DVW : D)) continue;
+#pragma unroll
+          for (int jj = 0; jj < 3; ++jj)
+            if (init == nullptr || jj < 4 - cv.W) s_win[x][jj][e] = 0.f;
+        }
+      }
+      __asm__ volatile("" ::: "memory");
+    }
+  }
+
   float4 s[RPT];
 #pragma unroll
   for (int m = 0; m < RPT; ++m)
@@ -86,6 +138,7 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
     float g[EPL], bt;
     uint32_t mk;
     RawV v;
+    TIn vw[EPL];               // CONV, wave 0: raw v of the tile's columns lane + 64 j
   };
   auto f32_of = [](TIn x) -> float {
     if constexpr (sizeof(TIn) == 2) return bf16_to_f32(x);
@@ -109,8 +162,43 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
       }
       in.bt = beta[tok];
       in.mk = mask == nullptr ? 1u : mask[static_cast<size_t>(b) * T + t];
+      if constexpr (CONV) {
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          if (lane + 64 * j < DVW) in.vw[j] = v[tok * D + col0 + lane + 64 * j];
+      }
     }
-    in.v = *reinterpret_cast<const RawV *>(v + tok * D + col0 + 4 * cg);
+    if constexpr (!CONV) in.v = *reinterpret_cast<const RawV *>(v + tok * D + col0 + 4 * cg);
+  };
+
+  // CONV (Kimi-K3 atlas, KDA layer page, kda-init code: a causal ShortConvolution with SiLU
+  // on each projection; nnterp Kimi-Linear page, Notes: the layer carries its last inputs
+  // outside the state).  Wave 0 filters every channel of the token (q and k: lane + 64 j;
+  // v: the tile's columns), reading the taps from memory and the windows from LDS; a
+  // padding token leaves the windows as they are.  The filtered values stay in fp32.
+  // One filter output of channel e of projection x (0 q, 1 k, 2 v) for raw input xr; the
+  // window advances when `live`.
+  auto filt = [&](int x, int e, float xr, bool live) -> float {
+    const int W = cv.W;
+    const size_t ch = static_cast<size_t>(h) * D + (x == 2 ? col0 : 0) + e;
+    const float *wp = (x == 0 ? cv.w[0] : (x == 1 ? cv.w[1] : cv.w[2])) + ch * W;
+    float tap[4];
+    if (W == 4) {
+      const float4 t4 = *reinterpret_cast<const float4 *>(wp);
+      tap[0] = t4.x; tap[1] = t4.y; tap[2] = t4.z; tap[3] = t4.w;
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) tap[jj] = jj >= 4 - W ? wp[jj - (4 - W)] : 0.f;
+    }
+    const float h0 = s_win[x][0][e], h1 = s_win[x][1][e], h2 = s_win[x][2][e];
+    float z = conv_z(tap, h0, h1, h2, xr, W);
+    if (cv.silu) z = silu_act(z);
+    if (live) {
+      s_win[x][0][e] = h1;
+      s_win[x][1][e] = h2;
+      s_win[x][2][e] = xr;
+    }
+    return z;                  // kept in fp32
   };
 
   // Wave 0: normalise token t's k and q, its decay factors, k.q, beta and the valid flag
@@ -136,6 +224,29 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
         }
         sk += kk[j] * kk[j];
         sq += qq[j] * qq[j];
+      }
+    }
+    if constexpr (CONV) {
+      // filter the raw inputs; the sums of squares are over the filtered values
+      bool live;
+      if constexpr (PF) live = in.mk != 0;
+      else live = mask == nullptr || mask[static_cast<size_t>(b) * T + t] != 0;
+      sk = sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        if (e < D) {
+          kk[j] = filt(1, e, kk[j], live);
+          qq[j] = filt(0, e, qq[j], live);
+          sk += kk[j] * kk[j];
+          sq += qq[j] * qq[j];
+        }
+        if (e < DVW) {
+          float vr;
+          if constexpr (PF) vr = f32_of(in.vw[j]);
+          else vr = Elem<TIn>::load(v, tok * D + col0 + e);
+          s_v[nb][e] = filt(2, e, vr, live);
+        }
       }
     }
     sk = wave_sum(sk);
@@ -287,9 +398,11 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
       sync_lds();
       // refill `cur` with token t+2's inputs before this token's stores, so that waiting
       // for those loads later does not wait for the stores (one in-order counter)
-      const RawV vv = cur.v;
+      float4 vv;
+      if constexpr (CONV) vv = *reinterpret_cast<const float4 *>(&s_v[nb][4 * cg]);
+      else vv = f32x4_of(cur.v);
       fetch(min(t + 2, T - 1), cur);          // (the last token again near the end)
-      finish(t, nb, nr, valid, f32x4_of(vv), RawV{});   // column tiles: no fused norm, no gate
+      finish(t, nb, nr, valid, vv, RawV{});   // column tiles: no fused norm, no gate
     };
     int t = 0;
     for (; t + 1 < T; t += 2) {
@@ -303,7 +416,8 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
       // before the prologue: their latency overlaps the prologue and the partial sums
       // instead of following them.
       const size_t tok = (static_cast<size_t>(b) * T + t) * H + h;
-      const RawV vraw = *reinterpret_cast<const RawV *>(v + tok * D + col0 + 4 * cg);
+      RawV vraw{};
+      if constexpr (!CONV) vraw = *reinterpret_cast<const RawV *>(v + tok * D + col0 + 4 * cg);
       RawV graw{};
       if constexpr (NORM) {
         if (wave == 0) graw = *reinterpret_cast<const RawV *>(gate + tok * D + 4 * cg);
@@ -313,7 +427,10 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
       const bool valid = s_scal[0][2] != 0.f;
       if (valid) partials(0, 0);
       sync_lds();
-      finish(t, 0, 0, valid, f32x4_of(vraw), graw);
+      float4 vv;
+      if constexpr (CONV) vv = *reinterpret_cast<const float4 *>(&s_v[0][4 * cg]);
+      else vv = f32x4_of(vraw);
+      finish(t, 0, 0, valid, vv, graw);
       sync_lds();   // the input and sum sets are rewritten by the next token
     }
   }
@@ -321,6 +438,28 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
 #pragma unroll
   for (int m = 0; m < RPT; ++m)
     store_nt(S + static_cast<size_t>(rg + RG * m) * D + 4 * cg, s[m]);
+
+  if constexpr (CONV && !PF) {
+    // The carried inputs after the call: window rows 4-W .. 2.  A whole slab is the only
+    // reader of its head's channels, and they were read before any was written, so the
+    // update may be in place.
+    if (wave == 0) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        if (e >= D) continue;
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+          TIn *fin = static_cast<TIn *>(x == 0 ? cv.fin[0] : (x == 1 ? cv.fin[1] : cv.fin[2]));
+          if (fin == nullptr) continue;
+          const size_t ch = static_cast<size_t>(h) * D + e;
+#pragma unroll
+          for (int jj = 0; jj < 3; ++jj)
+            if (jj >= 4 - cv.W) Elem<TIn>::store(fin, carried(jj, ch), s_win[x][jj][e]);
+        }
+      }
+    }
+  }
 }
 
 template <int D, int DVW, int RPT, typename TIn, typename TOut>
@@ -330,15 +469,25 @@ hipError_t launch_typed(const Args &a, hipStream_t st) {
   const TIn *q = static_cast<const TIn *>(a.q), *k = static_cast<const TIn *>(a.k),
             *v = static_cast<const TIn *>(a.v), *gate = static_cast<const TIn *>(a.gate);
   TOut *o = static_cast<TOut *>(a.o), *y = static_cast<TOut *>(a.y);
-  auto go = [&](auto norm, auto with_states) {
-    hipLaunchKernelGGL((recurrent_kernel<D, DVW, RPT, TIn, TOut, decltype(norm)::value, decltype(with_states)::value>),
+  auto go3 = [&](auto norm, auto with_states, auto conv) {
+    hipLaunchKernelGGL((recurrent_kernel<D, DVW, RPT, TIn, TOut, decltype(norm)::value, decltype(with_states)::value,
+                                         decltype(conv)::value>),
                        grid, block, 0, st, q, k, v, a.g, a.beta, a.state, a.mask, o, gate, a.norm_w, y, a.T, a.H,
-                       a.scale, a.use_l2, a.eps, a.g_head, a.states_out);
+                       a.scale, a.use_l2, a.eps, a.g_head, a.states_out, a.conv);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
+  auto go = [&](auto norm, auto with_states) { go3(norm, with_states, F_{}); };
   const bool norm = DVW == D && a.y != nullptr;
-  if (a.states_out) {
+  if (a.conv.W > 0) {
+    // the filtered path stores no per-token states
+    if constexpr (DVW == D) {
+      if (norm) go3(T_{}, F_{}, T_{});
+      else go3(F_{}, F_{}, T_{});
+    } else {
+      go3(F_{}, F_{}, T_{});
+    }
+  } else if (a.states_out) {
     if constexpr (DVW == D) {
       if (norm) go(T_{}, T_{});
       else go(F_{}, T_{});
@@ -354,8 +503,14 @@ hipError_t launch_typed(const Args &a, hipStream_t st) {
     }
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || DVW == D || a.y == nullptr) return e;
-  // column tiles: the gated norm over whole rows as its own pass
+  if (e != hipSuccess || DVW == D) return e;
+  // column tiles: the carried inputs after the call (every tile of a head reads its q and
+  // k windows) and the gated norm over whole rows run as passes of their own
+  if (a.conv.W > 0) {
+    e = launch_conv_carry(a, st);
+    if (e != hipSuccess) return e;
+  }
+  if (a.y == nullptr) return hipSuccess;
   return launch_gated_rmsnorm(a.o, a.gate, a.norm_w, a.y, static_cast<int64_t>(a.B) * a.T * a.H, D, a.eps,
                               a.out_bf16, a.in_bf16, a.out_bf16, st);
 }

@@ -140,11 +140,26 @@ short_conv_kernel(const TIn *__restrict__ x, const float *__restrict__ w, const 
   const TIn *xrow = x + static_cast<size_t>(row) * T * D;
   TOut *yrow = y + static_cast<size_t>(row) * T * D;
   const uint8_t *mrow = HAS_MASK ? mask + static_cast<size_t>(row) * T : nullptr;
-  f8 tap[W];
+  float tap[CPT][4];            // right-aligned taps per channel (conv_z)
 #pragma unroll
-  for (int j = 0; j < W; ++j)
+  for (int i = 0; i < CPT; ++i) {
+    tap[i][0] = tap[i][1] = tap[i][2] = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) tap[j][i] = w[(c0 + i) * W + j];
+    for (int j = 0; j < W; ++j) tap[i][4 - W + j] = w[(c0 + i) * W + j];
+  }
+  // filter output of the CPT channels for input x after the W-1 inputs hw[0..W-2] (oldest first)
+  auto filt = [&](const f8 (&hw)[W - 1], f8 x) {
+    f8 z;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      float h4[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < W - 1; ++j) h4[4 - W + j] = hw[j][c];
+      z[c] = conv_z(tap[c], h4[0], h4[1], h4[2], x[c], W);
+      if (silu) z[c] = silu_act(z[c]);
+    }
+    return z;
+  };
 
   Seq q = find_seq(cu, N, T, row, t0);
   if (t0 >= q.e) {                     // past the last packed sequence: nothing here
@@ -181,14 +196,10 @@ short_conv_kernel(const TIn *__restrict__ x, const float *__restrict__ w, const 
       for (int i = 0; i < PF; ++i) win[W - 1 + i] = xin[i];
 #pragma unroll
       for (int i = 0; i < PF; ++i) {
-        f8 z = tap[W - 1] * R::cvt(win[i + W - 1]);
+        f8 hw[W - 1];
 #pragma unroll
-        for (int j = 0; j < W - 1; ++j) z += tap[j] * R::cvt(win[i + j]);
-        if (silu) {                    // z * sigmoid(z); 1 + e^-z = inf gives -0 for very negative z
-#pragma unroll
-          for (int c = 0; c < CPT; ++c) z[c] = z[c] * __builtin_amdgcn_rcpf(1.f + __expf(-z[c]));
-        }
-        store8(yrow + static_cast<size_t>(tb + i) * D + c0, z);
+        for (int j = 0; j < W - 1; ++j) hw[j] = R::cvt(win[i + j]);
+        store8(yrow + static_cast<size_t>(tb + i) * D + c0, filt(hw, R::cvt(win[i + W - 1])));
       }
 #pragma unroll
       for (int j = 0; j < W - 1; ++j) h[j] = win[PF + j];
@@ -210,14 +221,10 @@ short_conv_kernel(const TIn *__restrict__ x, const float *__restrict__ w, const 
       }
       f8 out = f8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       if (!HAS_MASK || mrow[t] != 0) {
-        f8 z = tap[W - 1] * R::cvt(xin[i]);
+        f8 hw[W - 1];
 #pragma unroll
-        for (int j = 0; j < W - 1; ++j) z += tap[j] * R::cvt(h[j]);
-        if (silu) {
-#pragma unroll
-          for (int c = 0; c < CPT; ++c) z[c] = z[c] * __builtin_amdgcn_rcpf(1.f + __expf(-z[c]));
-        }
-        out = z;
+        for (int j = 0; j < W - 1; ++j) hw[j] = R::cvt(h[j]);
+        out = filt(hw, R::cvt(xin[i]));
 #pragma unroll
         for (int j = 0; j + 1 < W - 1; ++j) h[j] = h[j + 1];
         h[W - 2] = xin[i];
@@ -307,7 +314,44 @@ hipError_t launch2(const ConvArgs &a, hipStream_t st) {
   }
 }
 
+template <typename TIn, int W>
+hipError_t carry3(const Args &a, hipStream_t st) {
+  const int D = a.H * a.dk;            // channels of each projection (dk = dv)
+  const unsigned gx = static_cast<unsigned>((D / CPT + NTH - 1) / NTH);
+  const dim3 grid(gx, static_cast<unsigned>(a.N));
+  const void *xs[3] = {a.q, a.k, a.v};
+  for (int i = 0; i < 3; ++i) {
+    if (a.conv.fin[i] == nullptr) continue;
+    const TIn *x = static_cast<const TIn *>(xs[i]);
+    const TIn *init = static_cast<const TIn *>(a.conv.init[i]);
+    TIn *fin = static_cast<TIn *>(a.conv.fin[i]);
+    if (a.mask)
+      hipLaunchKernelGGL((short_conv_state_kernel<TIn, W, true>), grid, dim3(NTH), 0, st, x, init, a.cu, a.mask, fin,
+                         a.T, D, a.N);
+    else
+      hipLaunchKernelGGL((short_conv_state_kernel<TIn, W, false>), grid, dim3(NTH), 0, st, x, init, a.cu, a.mask, fin,
+                         a.T, D, a.N);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename TIn>
+hipError_t carry2(const Args &a, hipStream_t st) {
+  switch (a.conv.W) {
+    case 2: return carry3<TIn, 2>(a, st);
+    case 3: return carry3<TIn, 3>(a, st);
+    default: return carry3<TIn, 4>(a, st);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_conv_carry(const Args &a, hipStream_t st) {
+  if (a.N <= 0) return hipSuccess;
+  return a.in_bf16 ? carry2<uint16_t>(a, st) : carry2<float>(a, st);
+}
 
 hipError_t launch_short_conv(const ConvArgs &a, hipStream_t st) {
   if (a.in_bf16)

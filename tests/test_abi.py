@@ -112,7 +112,7 @@ def test_prefill_validation_codes():
 def test_prefill_workspace_size_and_checks():
     lib = K.load_library()
     size = lambda p, packed=0: lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), packed)
-    rec = 30224 + 512                                      # bytes per (chunk, head): record + norm exchange
+    rec = 32272 + 512                                      # bytes per (chunk, head): record + norm exchange
     tail = 256                                             # the status word of the partner waits
     assert size(_p(B=1, T=64, H=2)) == 1 * 2 * 2 * rec + tail   # B * ceil(T/32) * H records
     assert size(_p(B=3, T=65, H=2)) == 3 * 3 * 2 * rec + tail
@@ -249,6 +249,84 @@ def test_conv_validation_codes():
     assert conv(W=1) == UNSUP
     assert conv(B=70000) == UNSUP
     assert conv(cu=A, N=0) == 2
+
+
+def test_fused_conv_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "fused_conv_layout.c"
+    src.write_text(f'''#include <stdio.h>
+#include <stddef.h>
+#include "{HEADER}"
+int main(void) {{
+  printf("%zu", sizeof(kda_conv_t));
+#define F(x) printf(" %zu", offsetof(kda_conv_t, x));
+  F(width) F(activation) F(weight_q) F(weight_k) F(weight_v) F(initial_q) F(initial_k) F(initial_v)
+  F(final_q) F(final_k) F(final_v)
+  return 0;
+}}''')
+    exe = tmp_path / "fused_conv_layout"
+    subprocess.run(["gcc", "-o", str(exe), str(src)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(K.KdaConv)] + [getattr(K.KdaConv, f).offset for f, _ in K.KdaConv._fields_]
+    assert got == want
+
+
+def _cv(**kw):
+    f = dict(width=4, activation=1, weight_q=A, weight_k=A, weight_v=A, initial_q=None, initial_k=None,
+             initial_v=None, final_q=None, final_k=None, final_v=None)
+    f.update(kw)
+    return K.KdaConv(*[f[n] for n, _ in K.KdaConv._fields_])
+
+
+def test_fused_conv_validation_codes():
+    """Every call fails host validation (none may launch on the stand-in addresses)."""
+    lib = K.load_library()
+
+    def pre(p, cv, **ptrs):
+        names = ["q", "k", "v", "g", "beta", "init", "cu", "mask", "o", "fs", "gate", "w", "y"]
+        d = dict(q=A, k=A, v=A, g=A, beta=A, init=None, cu=None, mask=None, o=A, fs=A, gate=None, w=None, y=None)
+        d.update(ptrs)
+        return lib.kda_chunk_prefill_conv(ctypes.byref(p), None if cv is None else ctypes.byref(cv),
+                                          *[d[n] for n in names], None, 0, None)
+
+    def rec(p, cv, **ptrs):
+        names = ["q", "k", "v", "g", "beta", "state", "mask", "o", "gate", "w", "y"]
+        d = dict(q=A, k=A, v=A, g=A, beta=A, state=A, mask=None, o=A, gate=None, w=None, y=None)
+        d.update(ptrs)
+        return lib.kda_recurrent_step_conv(ctypes.byref(p), None if cv is None else ctypes.byref(cv),
+                                           *[d[n] for n in names], None)
+
+    assert pre(_p(), None) == 1
+    assert pre(_p(), _cv(weight_k=None)) == 1
+    assert pre(_p(), _cv(activation=2)) == 2
+    assert pre(_p(), _cv(width=5)) == UNSUP
+    assert pre(_p(), _cv(width=1)) == UNSUP
+    assert pre(_p(), _cv(weight_v=MIS)) == 4
+    assert pre(_p(), _cv(initial_q=MIS)) == 4
+    assert pre(_p(), _cv(final_v=MIS)) == 4
+    assert pre(_p(), _cv()) == WS                              # a valid call stops at the missing workspace
+    assert pre(_p(dk=16, dv=16), _cv()) == UNSUP               # only the matrix-core prefill filters in-kernel
+    assert pre(_p(in_dtype=0), _cv()) == UNSUP
+    assert pre(_p(chunk=16), _cv()) == UNSUP
+    assert pre(_p(), _cv(), q=None) == 1                       # the ordinary checks still run first
+    assert pre(_p(B=70000, T=1, H=1), _cv()) == UNSUP          # more sequences than the carry launch takes
+    assert rec(_p(T=1), None) == 1
+    assert rec(_p(T=1), _cv(weight_q=None)) == 1
+    assert rec(_p(T=1), _cv(activation=-1)) == 2
+    assert rec(_p(T=1), _cv(width=7)) == UNSUP
+    assert rec(_p(T=1), _cv(final_k=MIS)) == 4
+    assert rec(_p(T=1, dk=128, dv=64), _cv()) == UNSUP
+
+
+def test_fused_conv_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros((1, 4, 2, 128), dtype=torch.bfloat16)
+    g = torch.zeros((1, 4, 2, 128))
+    b = torch.zeros((1, 4, 2))
+    w = torch.zeros((256, 4))
+    with pytest.raises(ValueError):
+        K.chunk_prefill_conv(q, q, q, g, b, conv_weights=(w, w, w))
+    with pytest.raises(ValueError):
+        K.recurrent_step_conv(q, q, q, g, b, torch.zeros((1, 2, 128, 128)), conv_weights=(w, w, w))
 
 
 def test_out_proj_validation_codes():
