@@ -185,6 +185,52 @@ def time_prefill_conv(kda, P, ws, o, fs, y, reps: int = 10) -> dict:
     return res
 
 
+def time_decode_conv(kda, S, state0, reps: int = 10) -> dict:
+    """The B=64 decode step with the short convolution in front (raw q, k, v of the new
+    token, carried inputs updated in place), with gated norm: fused into the decode kernel
+    (kda_recurrent_step_conv) against three kda_short_conv passes and kda_recurrent_step.
+    Not part of the step."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12)
+    C = H * D
+    ws3 = tuple((torch.rand((C, 4), generator=gen, device="cuda") - 0.5) for _ in range(3))
+    cst = tuple(torch.randn((B_DECODE, 3, C), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(3))
+    filt = tuple(torch.empty((B_DECODE, 1, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    st = state0.clone()
+    od = torch.empty((B_DECODE, 1, H, D), dtype=torch.bfloat16, device="cuda")
+    yd = torch.empty_like(od)
+    raw = (S["q"], S["k"], S["v"])
+
+    def fused():
+        kda.recurrent_step_conv(S["q"], S["k"], S["v"], S["g"], S["beta"], st, conv_weights=ws3, conv_state=cst,
+                                conv_final_state=cst, gate=S["gate"], norm_weight=S["w"], out=od, y=yd)
+
+    def separate():
+        for x, w, c, f in zip(raw, ws3, cst, filt):
+            kda.short_conv(x.view(B_DECODE, 1, C), w, c, final_state=c, out=f.view(B_DECODE, 1, C),
+                           with_final_state=False)
+        kda.recurrent_step(filt[0], filt[1], filt[2], S["g"], S["beta"], st, gate=S["gate"], norm_weight=S["w"],
+                           out=od, y=yd)
+
+    res = {}
+    for name, fn in (("fused", fused), ("separate", separate)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"{name}_us"] = e0.elapsed_time(e1) * 1e3 / reps
+    nb = _bytes_decode_state(B_DECODE, H, D)
+    res["state_GBps_fused"] = nb / (res["fused_us"] * 1e-6) / 1e9
+    res["state_frac_fused"] = res["state_GBps_fused"] / HBM_PEAK_GBPS
+    del st, filt
+    return res
+
+
 def time_recurrent_states(kda, T: int = 256, reps: int = 5) -> dict:
     """The token-by-token kernel over a T-token prompt at the 96-head, 128-dim shape,
     storing the state after every token (64 KB per token and head); not part of the step."""
@@ -579,6 +625,8 @@ def main():
     conv = time_short_conv(kda)
     print("[bench] prefill with the short convolution fused", file=sys.stderr, flush=True)
     pconv = time_prefill_conv(kda, P, ws, o, fs, y)
+    print("[bench] decode step with the short convolution fused", file=sys.stderr, flush=True)
+    dconv = time_decode_conv(kda, S, state0)
     print("[bench] prefill with one decay per head", file=sys.stderr, flush=True)
     per_head = time_per_head_decay(kda, P, ws, o, fs)
     print("[bench] per-token states", file=sys.stderr, flush=True)
@@ -671,6 +719,7 @@ def main():
         # launches per call: the filter over all tokens, then the carried-input update)
         "short_conv": conv,
         "prefill_conv": pconv,
+        "decode_conv": dconv,
         # the same prefill with g [1, T, H] (one decay per head), timed on its own
         "prefill_per_head_decay": per_head,
         # the token-by-token kernel storing the state after every token, timed on its own

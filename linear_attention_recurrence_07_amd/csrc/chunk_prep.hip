@@ -110,6 +110,29 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
   // clear the chunk's words of the scan's norm exchange (2 tiles x 32 tokens)
   if (tid < 32) reinterpret_cast<u32x4 *>(xs + (static_cast<size_t>(slot) * H + h) * 64)[tid] = u32x4{0u, 0u, 0u, 0u};
   const size_t row0 = static_cast<size_t>(b) * T;
+  // this lane's token (operand order, see below), its decays and its write strength (CONV:
+  // loaded first, so that their latency overlaps the filter work)
+  const int tok = c0 + SB * m + r;
+  const int tcl = min(tok, t_end - 1);
+  const int off = tcl * (H * DK) + h * DK + 4 * lg;
+  const float *gp = G_HEAD ? g + (row0 + tcl) * H + h : g + row0 * H * DK + off;
+  f32x4 G[4][2];
+  float bt;
+  auto load_g = [&]() {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        if constexpr (G_HEAD) {
+          const float gs = *gp;
+          G[s][hh] = f32x4{gs, gs, gs, gs};
+        } else {
+          G[s][hh] = *reinterpret_cast<const f32x4 *>(gp + 32 * s + 16 * hh);
+        }
+      }
+    bt = beta[(row0 + tcl) * H + h];
+  };
+  if constexpr (CONV) load_g();
 
   // ---------------------------------------------------------------- fused short convolution
   // CONV (Kimi-K3 atlas, KDA layer page, kda-init code: a causal ShortConvolution with SiLU
@@ -214,44 +237,44 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
     unpack(w0, h0);
     unpack(w1, h1);
     unpack(w2, h2);
+    auto filter = [&](auto all_real) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = (vbits >> (8 * tg + i)) & 1u;
-      float x[8], z[8];
-      unpack(rows[i], x);
+      for (int i = 0; i < 8; ++i) {
+        const bool ok = decltype(all_real)::value || ((vbits >> (8 * tg + i)) & 1u);
+        float x[8], z[8];
+        unpack(rows[i], x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        z[e] = conv_z(tap[e], h0[e], h1[e], h2[e], x[e], W);
-        if (cv.silu) z[e] = silu_act(z[e]);
-        z[e] = ok ? z[e] : 0.f;
-        h0[e] = ok ? h1[e] : h0[e];
-        h1[e] = ok ? h2[e] : h1[e];
-        h2[e] = ok ? x[e] : h2[e];
+        for (int e = 0; e < 8; ++e) {
+          z[e] = conv_z(tap[e], h0[e], h1[e], h2[e], x[e], W);
+          if (cv.silu) z[e] = silu_act(z[e]);
+          z[e] = ok ? z[e] : 0.f;
+          h0[e] = ok ? h1[e] : h0[e];
+          h1[e] = ok ? h2[e] : h1[e];
+          h2[e] = ok ? x[e] : h2[e];
+        }
+        *reinterpret_cast<f32x4 *>(&cst[m][8 * tg + i][8 * cg]) = f32x4{z[0], z[1], z[2], z[3]};
+        *reinterpret_cast<f32x4 *>(&cst[m][8 * tg + i][8 * cg + 4]) = f32x4{z[4], z[5], z[6], z[7]};
       }
-      *reinterpret_cast<f32x4 *>(&cst[m][8 * tg + i][8 * cg]) = f32x4{z[0], z[1], z[2], z[3]};
-      *reinterpret_cast<f32x4 *>(&cst[m][8 * tg + i][8 * cg + 4]) = f32x4{z[4], z[5], z[6], z[7]};
-    }
+    };
+    // a wave whose lanes' tokens are all real (no padding, not past the end) skips the selects
+    if (vbits == 0xffffffffu) filter(std::true_type{});
+    else filter(std::false_type{});
     sync_lds();
   }
 
   // ---------------------------------------------------------------- load (operand order)
-  const int tok = c0 + SB * m + r;
-  const int tcl = min(tok, t_end - 1);
   bool valid = tok < t_end;
   if constexpr (HAS_MASK) valid = valid && mask[row0 + tcl] != 0;
-  const int off = tcl * (H * DK) + h * DK + 4 * lg;
   // q and k: one 16-byte load per K block, lane group lg reading channels 32 s + 8 L ..
   // 32 s + 8 L + 7 with L = (0, 2, 1, 3)[lg], then a row swap (operand_halves)
   const int off16 = tcl * (H * DK) + h * DK + 8 * (((lg & 1) << 1) | (lg >> 1));
   const uint16_t *kp = k + row0 * H * DK + off16;
   const uint16_t *qp = q + row0 * H * DK + off16;
-  const float *gp = G_HEAD ? g + (row0 + tcl) * H + h : g + row0 * H * DK + off;
   u32x2 kr[4][2], qr[4][2];
   u32x4 kw[4], qw[4];
   // CONV: the filtered k and q in operand order, fp32: slot e of K block s is channel
   // 32 s + kidx(lg, e) (read straight from LDS in that order)
   f32x4 kf[CONV ? 4 : 1][2], qf[CONV ? 4 : 1][2];
-  f32x4 G[4][2];
   if constexpr (CONV) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -267,19 +290,8 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
       kw[s] = *reinterpret_cast<const u32x4 *>(kp + 32 * s);
       qw[s] = *reinterpret_cast<const u32x4 *>(qp + 32 * s);
     }
+    load_g();
   }
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      if constexpr (G_HEAD) {
-        const float gs = *gp;
-        G[s][hh] = f32x4{gs, gs, gs, gs};
-      } else {
-        G[s][hh] = *reinterpret_cast<const f32x4 *>(gp + 32 * s + 16 * hh);
-      }
-    }
-  const float bt = beta[(row0 + tcl) * H + h];
   if constexpr (!CONV) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {

@@ -204,8 +204,15 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     }
   }
   auto put_raw = [&](int buf, u32x4 w) { *reinterpret_cast<u32x4 *>(&sm.raw[buf][3 + hr][hc8]) = w; };
-  // Filter chunk buf's tile into hd.vt (token hr, columns hc8..hc8+7), in fp32.
-  auto conv_tile = [&](Hand<CONV> &hd, int buf, uint32_t valid) {
+  // Filter chunk buf's tile into hd.vt (token hr, columns hc8..hc8+7), in fp32: the LDS
+  // reads first (conv_read), the arithmetic and the stores later (conv_write), so that
+  // other work covers the reads' latency.
+  struct ConvRows {
+    u32x4 x, r0, r1, r2;
+  };
+  auto conv_read = [&](int buf, uint32_t valid) -> ConvRows {
+    // newest three real rows before token hr: bits 0..2 of ext (the rows before the chunk)
+    // are always set, so three are always found
     const uint64_t ext = (static_cast<uint64_t>(valid) << 3) | 7u;
     const int e = hr + 3;
     uint64_t below = ext & ((uint64_t{1} << e) - 1u);
@@ -214,16 +221,20 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     const int p2 = 63 - __builtin_clzll(below);
     below &= ~(uint64_t{1} << p2);
     const int p3 = 63 - __builtin_clzll(below);
-    const u32x4 xr = *reinterpret_cast<const u32x4 *>(&sm.raw[buf][e][hc8]);
-    const u32x4 r2 = *reinterpret_cast<const u32x4 *>(&sm.raw[buf][p1][hc8]);
-    const u32x4 r1 = *reinterpret_cast<const u32x4 *>(&sm.raw[buf][p2][hc8]);
-    const u32x4 r0 = *reinterpret_cast<const u32x4 *>(&sm.raw[buf][p3][hc8]);
+    ConvRows cr;
+    cr.x = *reinterpret_cast<const u32x4 *>(&sm.raw[buf][e][hc8]);
+    cr.r2 = *reinterpret_cast<const u32x4 *>(&sm.raw[buf][p1][hc8]);
+    cr.r1 = *reinterpret_cast<const u32x4 *>(&sm.raw[buf][p2][hc8]);
+    cr.r0 = *reinterpret_cast<const u32x4 *>(&sm.raw[buf][p3][hc8]);
+    return cr;
+  };
+  auto conv_write = [&](Hand<CONV> &hd, const ConvRows &cr, uint32_t valid) {
     float z[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int w = i >> 1;
       auto el = [&](u32x4 x) { return (i & 1) ? hi_bf16(x[w]) : lo_bf16(x[w]); };
-      z[i] = conv_z(ctap[i], el(r0), el(r1), el(r2), el(xr), cv.W);
+      z[i] = conv_z(ctap[i], el(cr.r0), el(cr.r1), el(cr.r2), el(cr.x), cv.W);
       if (cv.silu) z[i] = silu_act(z[i]);
     }
     const bool keep = (valid >> hr) & 1u;
@@ -233,9 +244,11 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
       reinterpret_cast<float4 *>(dst)[1] = keep ? make_float4(z[4], z[5], z[6], z[7]) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
+  auto conv_tile = [&](Hand<CONV> &hd, int buf, uint32_t valid) { conv_write(hd, conv_read(buf, valid), valid); };
   // The three newest real rows of chunk area `from` (flags `valid`) become rows 0..2 of
-  // area `to` (threads 0..23: row ht/8).
-  auto carry = [&](int from, int to, uint32_t valid) {
+  // area `to` (threads 0..23: row ht/8); read and write apart, as for the filter.
+  auto carry_read = [&](int from, uint32_t valid) -> u32x4 {
+    u32x4 w = {0u, 0u, 0u, 0u};
     if (ht < 24) {
       uint64_t ext = (static_cast<uint64_t>(valid) << 3) | 7u;
       const int q1 = 63 - __builtin_clzll(ext);
@@ -244,9 +257,14 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
       ext &= ~(uint64_t{1} << q2);
       const int q3 = 63 - __builtin_clzll(ext);
       const int src = hr == 2 ? q1 : (hr == 1 ? q2 : q3);
-      *reinterpret_cast<u32x4 *>(&sm.raw[to][hr][hc8]) = *reinterpret_cast<const u32x4 *>(&sm.raw[from][src][hc8]);
+      w = *reinterpret_cast<const u32x4 *>(&sm.raw[from][src][hc8]);
     }
+    return w;
   };
+  auto carry_write = [&](int to, u32x4 w) {
+    if (ht < 24) *reinterpret_cast<u32x4 *>(&sm.raw[to][hr][hc8]) = w;
+  };
+  auto carry = [&](int from, int to, uint32_t valid) { carry_write(to, carry_read(from, valid)); };
   // Token ht/8 of chunk cidx, columns (ht%8)*8..+7 of the tile.
   auto store_row = [&](TOut *dst, int t, float4 x0, float4 x1) {
     const size_t off = row0 * tok_stride + (piece + static_cast<uint32_t>(t) * tok_bytes) / 2u;
@@ -500,13 +518,22 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
       float ssr[kNormLag - 1] = {};
       sync_lds();
       auto hstep = [&](int s, Pre &from, u32x4 &gs, uint32_t &fs) {
-        stage(sm.hand[(s + 1) & 1], from);
         if constexpr (CONV) {
-          conv_tile(sm.hand[(s + 1) & 1], (s + 1) & 1, from.valid);
-          carry((s + 1) & 1, s & 1, from.valid);
-          put_raw(s & 1, from.v);                // chunk s+2's raw rows
+          // the filter's LDS reads go out first, then the record staging and the next loads
+          // cover their latency; the filter arithmetic then overlaps the loads
+          const uint32_t fvalid = from.valid;
+          const ConvRows cr = conv_read((s + 1) & 1, fvalid);
+          const u32x4 cw = carry_read((s + 1) & 1, fvalid);
+          stage(sm.hand[(s + 1) & 1], from);
+          const u32x4 fv = from.v;
+          load(from, min(s + 3, last));
+          conv_write(sm.hand[(s + 1) & 1], cr, fvalid);
+          carry_write(s & 1, cw);
+          put_raw(s & 1, fv);                    // chunk s+2's raw rows
+        } else {
+          stage(sm.hand[(s + 1) & 1], from);
+          load(from, min(s + 3, last));
         }
-        load(from, min(s + 3, last));
         float ss = 0.f;
         if (s >= 1) {
           ss = emit(s - 1, sm.ost[(s - 1) % NOST]);

@@ -144,6 +144,14 @@ __device__ __forceinline__ float conv_z(const float (&tap)[4], float h0, float h
   if (W >= 3) z = __builtin_fmaf(tap[1], h1, z);
   return __builtin_fmaf(tap[2], h2, z);
 }
+// The same with all four taps applied (a narrower filter padded with zero taps on the left;
+// its window entries there must be finite).
+__device__ __forceinline__ float conv_z4(float4 tap, float h0, float h1, float h2, float x) {
+  float z = tap.w * x;
+  z = __builtin_fmaf(tap.x, h0, z);
+  z = __builtin_fmaf(tap.y, h1, z);
+  return __builtin_fmaf(tap.z, h2, z);
+}
 // z * sigmoid(z) from the hardware exp and reciprocal; 1 + e^-z = inf gives -0 for very
 // negative z.
 __device__ __forceinline__ float silu_act(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }

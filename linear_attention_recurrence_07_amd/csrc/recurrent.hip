@@ -73,58 +73,107 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
   __shared__ float s_red[NR][NW][2][DVW];
   __shared__ float s_scal[NB][4];
 
-  // CONV: the filtered v of the tile's columns per input set, and the filter windows (the
-  // three newest real inputs, oldest first) of q, k (D channels) and v (the tile's DVW),
-  // which only wave 0 reads and writes.
+  // CONV: the filtered v of the tile's columns per input set; the filter windows (the
+  // three newest real inputs, oldest first) of q, k (D channels) and v (the tile's DVW), raw
+  // in the input dtype; the taps [channel][W] of the head's q, k and of the tile's v.  Only
+  // wave 0 reads and writes the windows and taps.
   constexpr int NB_ = DVW < D ? 3 : 1;
   __shared__ float s_v[CONV ? NB_ : 1][CONV ? DVW : 1];
-  __shared__ float s_win[CONV ? 3 : 1][CONV ? 3 : 1][CONV ? D : 1];
+  __shared__ __attribute__((aligned(16))) TIn s_wq[CONV ? 3 : 1][CONV ? D : 1];
+  __shared__ __attribute__((aligned(16))) TIn s_wk[CONV ? 3 : 1][CONV ? D : 1];
+  __shared__ __attribute__((aligned(16))) TIn s_wv[CONV ? 3 : 1][CONV ? DVW : 1];
+  __shared__ __attribute__((aligned(16))) float4 s_tq[CONV ? D : 1], s_tk[CONV ? D : 1], s_tv[CONV ? DVW : 1];
   const size_t ch_stride = static_cast<size_t>(H) * D;            // channels of a projection
   // element of window row jj (0..2, oldest first) of channel ch in a carried-input array
   auto carried = [&](int jj, size_t ch) {
     return (static_cast<size_t>(b) * (cv.W - 1) + (cv.W - 4 + jj)) * ch_stride + ch;
   };
   if constexpr (CONV) {
-    // Wave 0 puts the windows in place before it loads its state rows (the other waves
-    // load theirs meanwhile), so the two sets of loads never hold registers together.
+    // Wave 0 copies the taps and the carried inputs of row b into LDS with direct
+    // global-to-LDS loads, issued just before its state loads: they hold no registers and
+    // arrive with the state.  Data loaded this way is not covered by the compiler's own
+    // waits, so wave 0 waits for all its loads (conv_ready) before it reads any of it.
+    // Taps are kept four wide: a narrower filter's are right-aligned with zeros in front,
+    // and the window rows they meet are zero, so the filter runs without width branches.
     if (wave == 0) {
+      const int W = cv.W;
+      // bytes: a multiple of 16; source and destination 16-byte aligned
+      auto copy_lds = [&](const void *src, void *dst, int bytes) {
+        // a wave-uniform base (scalar registers) plus one per-lane offset; the builtin
+        // returns a signed int, so each half is taken back as unsigned before widening
+        // (a sign-extended low half would set the address's upper bits)
+        const uint64_t a = reinterpret_cast<uint64_t>(src);
+        const uint32_t ahi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+        const uint32_t alo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu)));
+        const char *base = reinterpret_cast<const char *>((static_cast<uint64_t>(ahi) << 32) | alo);
+        for (int off = 0; off < bytes; off += 1024)
+          if (lane * 16 < bytes - off)
+            __builtin_amdgcn_global_load_lds(base + off + lane * 16,
+                                             (__attribute__((address_space(3))) void *)(static_cast<char *>(dst) + off),
+                                             16, 0, 0);
+      };
+      const float *wsrc[3] = {cv.w[0] + static_cast<size_t>(h) * D * W, cv.w[1] + static_cast<size_t>(h) * D * W,
+                              cv.w[2] + (static_cast<size_t>(h) * D + col0) * W};
+      float4 *tdst[3] = {s_tq, s_tk, s_tv};
+      // the taps as stored ([channel][W]); a narrower filter's are spread to four wide in
+      // place once they have arrived (conv_ready)
+#pragma unroll
+      for (int x = 0; x < 3; ++x) copy_lds(wsrc[x], tdst[x], (x == 2 ? DVW : D) * W * 4);
 #pragma unroll
       for (int x = 0; x < 3; ++x) {
         const TIn *init = static_cast<const TIn *>(x == 0 ? cv.init[0] : (x == 1 ? cv.init[1] : cv.init[2]));
-        if (init == nullptr) continue;
-        // row b's carried inputs of the head's (or the tile's) channels; entry W-4+jj is row jj
-        const TIn *base = init + static_cast<size_t>(b) * (cv.W - 1) * ch_stride + static_cast<size_t>(h) * D +
-                          (x == 2 ? col0 : 0);
+        const int nch = x == 2 ? DVW : D;
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-          const int e = lane + 64 * j;
-          if (e >= (x == 2 ? DVW : D)) continue;
+        for (int jj = 0; jj < 3; ++jj) {
+          TIn *row = x == 0 ? s_wq[jj] : (x == 1 ? s_wk[jj] : s_wv[jj]);
+          if (init != nullptr && jj >= 4 - W) {
+            copy_lds(init + carried(jj, static_cast<size_t>(h) * D + (x == 2 ? col0 : 0)), row,
+                     nch * static_cast<int>(sizeof(TIn)));
+          } else {
 #pragma unroll
-          for (int jj = 0; jj < 3; ++jj)
-            if (jj >= 4 - cv.W)
-              s_win[x][jj][e] = Elem<TIn>::load(base, static_cast<uint32_t>((cv.W - 4 + jj) * ch_stride + e));
+            for (int j = 0; j < EPL; ++j)
+              if (lane + 64 * j < nch) row[lane + 64 * j] = TIn{};
+          }
         }
       }
-#pragma unroll
-      for (int x = 0; x < 3; ++x) {
-        const void *init = x == 0 ? cv.init[0] : (x == 1 ? cv.init[1] : cv.init[2]);
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-          const int e = lane + 64 * j;
-          if (e >= (x == 2 ? DVW : D)) continue;
-#pragma unroll
-          for (int jj = 0; jj < 3; ++jj)
-            if (init == nullptr || jj < 4 - cv.W) s_win[x][jj][e] = 0.f;
-        }
-      }
-      __asm__ volatile("" ::: "memory");
     }
   }
-
   float4 s[RPT];
 #pragma unroll
   for (int m = 0; m < RPT; ++m)
     s[m] = *reinterpret_cast<const float4 *>(S + static_cast<size_t>(rg + RG * m) * D + 4 * cg);
+
+  auto conv_ready = [&]() {   // wave 0, before its first read of the taps or windows
+    if constexpr (CONV) {
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const int W = cv.W;
+      if (W != 4) {
+        // [channel][W] -> [channel][4] right-aligned: every lane reads its channels' taps
+        // before any lane writes (one wave, LDS operations in order)
+        float4 *tdst[3] = {s_tq, s_tk, s_tv};
+        float t[3][EPL][4];
+#pragma unroll
+        for (int x = 0; x < 3; ++x)
+#pragma unroll
+          for (int j = 0; j < EPL; ++j) {
+            const int e = lane + 64 * j;
+            const float *src = reinterpret_cast<const float *>(tdst[x]);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              t[x][j][jj] = (e < (x == 2 ? DVW : D) && jj >= 4 - W) ? src[e * W + jj - (4 - W)] : 0.f;
+          }
+        wave_sync_lds();
+#pragma unroll
+        for (int x = 0; x < 3; ++x)
+#pragma unroll
+          for (int j = 0; j < EPL; ++j) {
+            const int e = lane + 64 * j;
+            if (e < (x == 2 ? DVW : D)) tdst[x][e] = make_float4(t[x][j][0], t[x][j][1], t[x][j][2], t[x][j][3]);
+          }
+        wave_sync_lds();
+      }
+    }
+  };
 
   // Inputs of token t: wave 0 holds k, q, g, beta and the mask flag, every thread its
   // four columns of v.  Column tiles (few work-groups, each walking its tokens) load them
@@ -179,24 +228,18 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
   // One filter output of channel e of projection x (0 q, 1 k, 2 v) for raw input xr; the
   // window advances when `live`.
   auto filt = [&](int x, int e, float xr, bool live) -> float {
-    const int W = cv.W;
-    const size_t ch = static_cast<size_t>(h) * D + (x == 2 ? col0 : 0) + e;
-    const float *wp = (x == 0 ? cv.w[0] : (x == 1 ? cv.w[1] : cv.w[2])) + ch * W;
-    float tap[4];
-    if (W == 4) {
-      const float4 t4 = *reinterpret_cast<const float4 *>(wp);
-      tap[0] = t4.x; tap[1] = t4.y; tap[2] = t4.z; tap[3] = t4.w;
-    } else {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) tap[jj] = jj >= 4 - W ? wp[jj - (4 - W)] : 0.f;
-    }
-    const float h0 = s_win[x][0][e], h1 = s_win[x][1][e], h2 = s_win[x][2][e];
-    float z = conv_z(tap, h0, h1, h2, xr, W);
+    const float4 tap = (x == 0 ? s_tq : (x == 1 ? s_tk : s_tv))[e];
+    TIn *w0 = x == 0 ? s_wq[0] : (x == 1 ? s_wk[0] : s_wv[0]);
+    TIn *w1 = x == 0 ? s_wq[1] : (x == 1 ? s_wk[1] : s_wv[1]);
+    TIn *w2 = x == 0 ? s_wq[2] : (x == 1 ? s_wk[2] : s_wv[2]);
+    const TIn r0 = w0[e], r1 = w1[e], r2 = w2[e];
+    float z = conv_z4(tap, f32_of(r0), f32_of(r1), f32_of(r2), xr);
     if (cv.silu) z = silu_act(z);
-    if (live) {
-      s_win[x][0][e] = h1;
-      s_win[x][1][e] = h2;
-      s_win[x][2][e] = xr;
+    if (live) {                // raw inputs, exact in the input dtype
+      w0[e] = r1;
+      w1[e] = r2;
+      if constexpr (sizeof(TIn) == 2) w2[e] = f32_to_bf16(xr);
+      else w2[e] = xr;
     }
     return z;                  // kept in fp32
   };
@@ -232,20 +275,33 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
       if constexpr (PF) live = in.mk != 0;
       else live = mask == nullptr || mask[static_cast<size_t>(b) * T + t] != 0;
       sk = sq = 0.f;
+      float vr[EPL];
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        vr[j] = 0.f;
+        if (e < DVW) {
+          if constexpr (PF) vr[j] = f32_of(in.vw[j]);
+          else vr[j] = Elem<TIn>::load(v, tok * D + col0 + e);
+        }
+      }
+      // one filter at a time (the empty asm statements keep the compiler from hoisting the
+      // next one's LDS reads): their operands would otherwise all be live at once, next to
+      // the state, and cost occupancy
 #pragma unroll
       for (int j = 0; j < EPL; ++j) {
         const int e = lane + 64 * j;
         if (e < D) {
           kk[j] = filt(1, e, kk[j], live);
+          __asm__ volatile("" ::: "memory");
           qq[j] = filt(0, e, qq[j], live);
+          __asm__ volatile("" ::: "memory");
           sk += kk[j] * kk[j];
           sq += qq[j] * qq[j];
         }
         if (e < DVW) {
-          float vr;
-          if constexpr (PF) vr = f32_of(in.vw[j]);
-          else vr = Elem<TIn>::load(v, tok * D + col0 + e);
-          s_v[nb][e] = filt(2, e, vr, live);
+          s_v[nb][e] = filt(2, e, vr[j], live);
+          __asm__ volatile("" ::: "memory");
         }
       }
     }
@@ -385,7 +441,10 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
     if (T > 0) {
       fetch(0, inA);
       if (T > 1) fetch(1, inB);
-      if (wave == 0) prologue(0, inA, 0);
+      if (wave == 0) {
+        conv_ready();
+        prologue(0, inA, 0);
+      }
       sync_lds();
     }
     // token t: `cur` holds its inputs (v used here), `nxt` those of t+1 (prepared here);
@@ -411,6 +470,7 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
     }
     if (t < T) step(t, inA, inB);
   } else {
+    if (wave == 0) conv_ready();
     for (int t = 0; t < T; ++t) {
       // v of this thread's columns and the gate (wave 0, which writes y) are loaded
       // before the prologue: their latency overlaps the prologue and the partial sums
@@ -453,9 +513,12 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
           TIn *fin = static_cast<TIn *>(x == 0 ? cv.fin[0] : (x == 1 ? cv.fin[1] : cv.fin[2]));
           if (fin == nullptr) continue;
           const size_t ch = static_cast<size_t>(h) * D + e;
+          const TIn *const wrow[3] = {x == 0 ? s_wq[0] : (x == 1 ? s_wk[0] : s_wv[0]),
+                                      x == 0 ? s_wq[1] : (x == 1 ? s_wk[1] : s_wv[1]),
+                                      x == 0 ? s_wq[2] : (x == 1 ? s_wk[2] : s_wv[2])};
 #pragma unroll
           for (int jj = 0; jj < 3; ++jj)
-            if (jj >= 4 - cv.W) Elem<TIn>::store(fin, carried(jj, ch), s_win[x][jj][e]);
+            if (jj >= 4 - cv.W) fin[carried(jj, ch)] = wrow[jj][e];
         }
       }
     }
