@@ -139,7 +139,27 @@ def time_per_head_decay(kda, P, ws, o, fs, reps: int = 10) -> dict:
             "prepare_algorithmic_bytes": b_prep, "prepare_GBps": b_prep / tp / 1e9}
 
 
-def time_prefill_conv(kda, P, ws, o, fs, y, reps: int = 10) -> dict:
+def _median_pair_us(fns: dict, reps: int, rounds: int = 5) -> dict:
+    """Median over `rounds` of the mean time per call (us) of `reps` back-to-back calls,
+    the callables taking turns round by round so that clock drift hits each alike."""
+    for fn in fns.values():
+        for _ in range(2):
+            fn()
+    torch.cuda.synchronize()
+    times = {name: [] for name in fns}
+    for _ in range(rounds):
+        for name, fn in fns.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times[name].append(e0.elapsed_time(e1) * 1e3 / reps)
+    return {name: float(np.median(v)) for name, v in times.items()}
+
+
+def time_prefill_conv(kda, P, ws, o, fs, y, reps: int = 4) -> dict:
     """The T=8192 prefill with the short convolution in front (raw q, k, v projections,
     width-4 taps, carried inputs written), with gated norm, two ways: fused into the
     preparation and the scan (kda_chunk_prefill_conv), and as three kda_short_conv passes
@@ -164,19 +184,9 @@ def time_prefill_conv(kda, P, ws, o, fs, y, reps: int = 10) -> dict:
                           norm_eps=P["eps"], out=o, final_state=fs, y=y, workspace=ws)
 
     res = {}
-    for name, fn in (("fused", fused), ("separate", separate)):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / reps
-        res[f"{name}_us"] = t * 1e6
-        res[f"{name}_tokens_per_s"] = T_PREFILL / t
+    for name, us in _median_pair_us({"fused": fused, "separate": separate}, reps).items():
+        res[f"{name}_us"] = us
+        res[f"{name}_tokens_per_s"] = T_PREFILL / (us * 1e-6)
     nb = _bytes_prefill(T_PREFILL, H, D, False, norm=True) + 3 * (3 * C * 2 + C * 4 * 4)
     res["fused_algorithmic_bytes"] = nb
     res["fused_GBps"] = nb / (res["fused_us"] * 1e-6) / 1e9
@@ -185,7 +195,7 @@ def time_prefill_conv(kda, P, ws, o, fs, y, reps: int = 10) -> dict:
     return res
 
 
-def time_decode_conv(kda, S, state0, reps: int = 10) -> dict:
+def time_decode_conv(kda, S, state0, reps: int = 20) -> dict:
     """The B=64 decode step with the short convolution in front (raw q, k, v of the new
     token, carried inputs updated in place), with gated norm: fused into the decode kernel
     (kda_recurrent_step_conv) against three kda_short_conv passes and kda_recurrent_step.
@@ -212,18 +222,7 @@ def time_decode_conv(kda, S, state0, reps: int = 10) -> dict:
         kda.recurrent_step(filt[0], filt[1], filt[2], S["g"], S["beta"], st, gate=S["gate"], norm_weight=S["w"],
                            out=od, y=yd)
 
-    res = {}
-    for name, fn in (("fused", fused), ("separate", separate)):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        res[f"{name}_us"] = e0.elapsed_time(e1) * 1e3 / reps
+    res = {f"{name}_us": us for name, us in _median_pair_us({"fused": fused, "separate": separate}, reps).items()}
     nb = _bytes_decode_state(B_DECODE, H, D)
     res["state_GBps_fused"] = nb / (res["fused_us"] * 1e-6) / 1e9
     res["state_frac_fused"] = res["state_GBps_fused"] / HBM_PEAK_GBPS
