@@ -231,8 +231,10 @@ def time_decode_conv(kda, S, state0, reps: int = 20) -> dict:
 
 
 def time_recurrent_states(kda, T: int = 256, reps: int = 5) -> dict:
-    """The token-by-token kernel over a T-token prompt at the 96-head, 128-dim shape,
-    storing the state after every token (64 KB per token and head); not part of the step."""
+    """The state after every token of a T-token prompt at the 96-head, 128-dim shape (64 KB
+    per token and head), two ways: the token-by-token kernel (kda_recurrent_states), and
+    the chunked form (kda_chunk_prefill_states: preparation, scan, then the per-token
+    fill), under "chunked".  Not part of the step."""
     gen = torch.Generator(device="cuda")
     gen.manual_seed(11)
     shp = (1, T, H, D)
@@ -258,9 +260,17 @@ def time_recurrent_states(kda, T: int = 256, reps: int = 5) -> dict:
         ts.append(e0.elapsed_time(e1) * 1e-3)
     t = float(np.mean(ts))
     nbytes = T * H * D * D * 4 + 2 * H * D * D * 4 + T * H * (4 * D * 2 + D * 4 + 4)
+    # the chunked form on the same inputs (initial state read, final state written)
+    fs = torch.empty_like(st0)
+    ws = torch.empty((kda.chunk_prefill_workspace_size(1, T, H, D, D, states=True),), dtype=torch.uint8,
+                     device="cuda")
+    run = lambda: kda.chunk_prefill(q, k, v, g, beta, st0, out=o, final_state=fs, states=states, workspace=ws)
+    tc = _median_pair_us({"chunked": run}, reps=5)["chunked"] * 1e-6
     del states
     return {"T": T, "H": H, "avg_call_us": t * 1e6, "algorithmic_bytes": nbytes, "achieved": nbytes / t / 1e9,
-            "unit": "GB/s", "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS}
+            "unit": "GB/s", "frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
+            "chunked": {"avg_call_us": tc * 1e6, "achieved": nbytes / tc / 1e9, "unit": "GB/s",
+                        "frac": nbytes / tc / 1e9 / HBM_PEAK_GBPS}}
 
 
 def time_layer_exit(kda, rows: int = B_DECODE, N: int = 7168, reps: int = 10) -> dict:

@@ -245,6 +245,43 @@ kda_status_t kda_recurrent_states(const kda_params_t *p,
                                   float *states, void *stream);
 
 /*
+ * kda_chunk_prefill_states -- kda_chunk_prefill that also stores the state after every
+ * token (the 'states' output of the nnterp Kimi-Linear page's support() table,
+ * [batch, seq, heads, key_dim, value_dim]), computed through the chunked form rather than
+ * token by token.  Within a chunk the recurrence unrolls to
+ *     S_t = diag(exp(g_t)) S_{t-1} + k_t u_t^T
+ * with u_t the rows of the chunk's corrected values U, which the state scan forms anyway
+ * (nnterp Kimi-Linear page, Notes, "Loading": the prompt kernel carries the state from
+ * chunk to chunk).  The scan stores U of every chunk in the workspace and the state after
+ * each chunk's last position into `states`; one more launch writes every other position
+ * from the state before its chunk, 16 KB per store stream, independent across chunks.
+ *   states [B, T, H, dk, dv] fp32, 16-byte aligned: states[b, t, h] is S after token t
+ *          (a padding token repeats the carried state; tokens of a packed batch at or past
+ *          cu_seqlens[N] are not written).  64 KB per token and head.
+ *   o      required (the gated norm, when asked for, runs over it as its own launch).
+ *   workspace  at least kda_chunk_prefill_states_workspace_size(p, cu_seqlens != NULL)
+ *          bytes: the prefill's workspace plus 16,384 bytes per chunk and head.
+ * Other arguments, results and the precision are those of kda_chunk_prefill; the states
+ * agree with the token-by-token recurrence to the chunked kernel's rounding (the state
+ * after a chunk's last position is the same value final_state gets at a sequence end).
+ * Only the bf16, dk = dv = 128 matrix-core kernel has this form: other shapes return
+ * KDA_ERR_UNSUPPORTED (kda_recurrent_states covers them).  Errors as for kda_chunk_prefill,
+ * KDA_ERR_NULL also for a NULL o or states.  Nothing is allocated.
+ */
+kda_status_t kda_chunk_prefill_states(const kda_params_t *p,
+                                      const void *q, const void *k, const void *v,
+                                      const float *g, const float *beta,
+                                      const float *initial_state,
+                                      const int32_t *cu_seqlens, const uint8_t *mask,
+                                      void *o, float *final_state,
+                                      const void *gate, const float *norm_weight, void *y,
+                                      float *states, void *workspace, size_t workspace_bytes, void *stream);
+/* Bytes of workspace kda_chunk_prefill_states needs; 0 for invalid params or a shape
+ * without the chunked form.  (N + ceil(T / 32)) * H * 49168 + 256 with packing, otherwise
+ * B * ceil(T / 32) * H * 49168 + 256. */
+size_t kda_chunk_prefill_states_workspace_size(const kda_params_t *p, int32_t packed);
+
+/*
  * kda_gated_rmsnorm -- y = w * x / sqrt(mean(x^2) + eps) * sigmoid(gate) over each row
  * of `width` features (one head).  x and gate: [rows, width] in in_dtype; weight:
  * [width] fp32 shared by every row; y: [rows, width] out_dtype.  width must be a power

@@ -97,6 +97,10 @@ def load_library():
     lib.kda_recurrent_step_conv.argtypes = [ctypes.POINTER(KdaParams), ctypes.POINTER(KdaConv)] + [P] * 12
     lib.kda_chunk_prefill_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_prefill_workspace_size.argtypes = [ctypes.POINTER(KdaParams), i32]
+    lib.kda_chunk_prefill_states.restype = ctypes.c_int
+    lib.kda_chunk_prefill_states.argtypes = [ctypes.POINTER(KdaParams)] + [P] * 15 + [ctypes.c_size_t, P]
+    lib.kda_chunk_prefill_states_workspace_size.restype = ctypes.c_size_t
+    lib.kda_chunk_prefill_states_workspace_size.argtypes = [ctypes.POINTER(KdaParams), i32]
     lib.kda_chunk_prefill_status.restype = ctypes.c_int
     lib.kda_chunk_prefill_status.argtypes = [ctypes.POINTER(KdaParams), i32, P, ctypes.c_size_t, P]
     lib.kda_chunk_prepare.restype = ctypes.c_int
@@ -242,11 +246,15 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   output_dtype: Optional[torch.dtype] = None,
                   out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
                   y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  head_outputs: bool = True, _conv=None):
+                  head_outputs: bool = True, states: Optional[torch.Tensor] = None, _conv=None):
     """Chunked prefill.  Returns (o, final_state), or (o, final_state, y) with the fused
     sigmoid-gated RMSNorm when gate and norm_weight are given.  With the norm and
     head_outputs=False no o is returned (None): the head outputs pass through y, which is
     then normalised in place.
+
+    states ([B,T,H,dk,dv] float32 on the device), when given, receives the state after
+    every token, computed through the chunked form (kda_chunk_prefill_states: bf16
+    inputs, dk = dv = 128); it needs head_outputs=True.
 
     cu_seqlens ([N+1] int32; a CPU tensor is validated then copied to the GPU) packs N
     sequences into B = 1; attention_mask ([B, T], nonzero = token) marks padding.
@@ -283,6 +291,11 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         _shape(out, "out", (B, T, H, dv), out_dt)
     if final_state is not None:
         _shape(final_state, "final_state", (N, H, dk, dv), torch.float32)
+    if states is not None:
+        if not head_outputs or _conv is not None:
+            raise ValueError("per-token states need head_outputs=True and no fused convolution")
+        _shape(states, "states", (B, T, H, dk, dv), torch.float32)
+        _dev(states, "states", dev)
     if norm:
         _shape(gate, "gate", (B, T, H, dv), in_dt)
         _shape(norm_weight, "norm_weight", (dv,), torch.float32)
@@ -304,13 +317,19 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     p = _params(B, T, H, dk, dv, num_seqs=N if cu_dev is not None else 0, chunk=chunk, scale=scale,
                 use_qk_l2norm=use_qk_l2norm_in_kernel, in_dtype=_dtype_code(in_dt),
                 out_dtype=_dtype_code(out_dt), norm_eps=norm_eps, decay_per_head=per_head)
-    need = lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), 1 if cu_dev is not None else 0)
+    size_fn = lib.kda_chunk_prefill_workspace_size if states is None else lib.kda_chunk_prefill_states_workspace_size
+    need = size_fn(ctypes.byref(p), 1 if cu_dev is not None else 0)
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
     else:
         _dev(workspace, "workspace", dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if _conv is None:
+    if states is not None:
+        _check(lib.kda_chunk_prefill_states(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                            _ptr(initial_state), _ptr(cu_dev), _ptr(mask_dev), _ptr(o), _ptr(fs),
+                                            _ptr(gate), _ptr(norm_weight), _ptr(y), _ptr(states), _ptr(workspace),
+                                            ws_bytes, _stream(dev)))
+    elif _conv is None:
         _check(lib.kda_chunk_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                      _ptr(initial_state), _ptr(cu_dev), _ptr(mask_dev), _ptr(o), _ptr(fs),
                                      _ptr(gate), _ptr(norm_weight), _ptr(y), _ptr(workspace), ws_bytes,
@@ -381,13 +400,14 @@ def chunk_prefill_conv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: tor
 
 def chunk_prefill_workspace_size(B: int, T: int, H: int, dk: int, dv: int, *,
                                   num_seqs: Optional[int] = None, dtype: torch.dtype = torch.bfloat16,
-                                  chunk: int = 0) -> int:
-    """Bytes of workspace chunk_prefill needs; num_seqs is the sequence count when
-    cu_seqlens packs the batch (B = 1)."""
+                                  chunk: int = 0, states: bool = False) -> int:
+    """Bytes of workspace chunk_prefill needs (with states=True: with per-token states);
+    num_seqs is the sequence count when cu_seqlens packs the batch (B = 1)."""
     lib = load_library()
     p = _params(B, T, H, dk, dv, num_seqs=num_seqs or 0, chunk=chunk, in_dtype=_dtype_code(dtype),
                 out_dtype=_dtype_code(dtype))
-    return int(lib.kda_chunk_prefill_workspace_size(ctypes.byref(p), 1 if num_seqs is not None else 0))
+    fn = lib.kda_chunk_prefill_states_workspace_size if states else lib.kda_chunk_prefill_workspace_size
+    return int(fn(ctypes.byref(p), 1 if num_seqs is not None else 0))
 
 
 def chunk_prefill_status(workspace: torch.Tensor, B: int, T: int, H: int, dk: int = 128, dv: int = 128, *,

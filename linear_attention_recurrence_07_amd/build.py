@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["api.cpp", "recurrent.hip", "gated_rmsnorm.hip", "prefill_valu.hip", "chunk_prep.hip", "chunk_scan.hip",
-           "short_conv.hip", "out_proj.hip"]
+           "chunk_states.hip", "short_conv.hip", "out_proj.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

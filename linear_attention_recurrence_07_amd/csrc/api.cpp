@@ -130,8 +130,16 @@ kda_status_t check_stage_kernel(const kda_params_t *p) {
   return KDA_OK;
 }
 
-kda_status_t check_workspace(const kda_params_t *p, const int32_t *cu, const void *ws, size_t bytes) {
-  const size_t need = prefill_workspace(p, cu != nullptr);
+// The per-token states also keep each chunk's U rows (16 KB per chunk and head).
+size_t prefill_states_workspace(const kda_params_t *p, bool packed) {
+  if (!use_mfma_prefill(p)) return 0;
+  const int N = packed ? p->num_seqs : p->B;
+  return prefill_workspace(p, packed) + kda::chunk_states_u_bytes(p->B, p->T, p->H, N, packed);
+}
+
+kda_status_t check_workspace(const kda_params_t *p, const int32_t *cu, const void *ws, size_t bytes,
+                             bool states = false) {
+  const size_t need = states ? prefill_states_workspace(p, cu != nullptr) : prefill_workspace(p, cu != nullptr);
   if (bytes < need || (need > 0 && ws == nullptr))
     return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, bytes,
                 ws == nullptr ? " (NULL)" : "");
@@ -166,19 +174,22 @@ void set_conv(kda::Args &a, const kda_conv_t *c) {
   a.conv.fin[0] = c->final_q; a.conv.fin[1] = c->final_k; a.conv.fin[2] = c->final_v;
 }
 
-// Shared body of kda_chunk_prefill (conv NULL) and kda_chunk_prefill_conv.
+// Shared body of kda_chunk_prefill (conv NULL), kda_chunk_prefill_conv and
+// kda_chunk_prefill_states (with_states).
 kda_status_t prefill_impl(const kda_params_t *p, const kda_conv_t *conv, bool with_conv, const void *q,
                           const void *k, const void *v, const float *g, const float *beta,
                           const float *initial_state, const int32_t *cu_seqlens, const uint8_t *mask, void *o,
                           float *final_state, const void *gate, const float *norm_weight, void *y,
-                          void *workspace, size_t workspace_bytes, void *stream) {
+                          void *workspace, size_t workspace_bytes, void *stream, bool with_states = false,
+                          float *states = nullptr) {
   KDA_TRY(check_params(p, true));
   KDA_TRY(check_ptr(q, "q", true));
   KDA_TRY(check_ptr(k, "k", true));
   KDA_TRY(check_ptr(v, "v", true));
   KDA_TRY(check_ptr(g, "g", true, p->decay_per_head ? 4u : 16u));
   KDA_TRY(check_ptr(beta, "beta", true, 4));
-  KDA_TRY(check_ptr(o, "o", y == nullptr));   // optional when y is wanted
+  KDA_TRY(check_ptr(o, "o", y == nullptr || with_states));   // optional when y is wanted (not with states)
+  if (with_states) KDA_TRY(check_ptr(states, "states", true));
   KDA_TRY(check_ptr(final_state, "final_state", true));
   KDA_TRY(check_ptr(initial_state, "initial_state", false));
   KDA_TRY(check_layout(p, cu_seqlens, mask));
@@ -198,6 +209,9 @@ kda_status_t prefill_impl(const kda_params_t *p, const kda_conv_t *conv, bool wi
                                        "(chunk 0, 32 or 64); for other shapes run kda_short_conv first");
     set_conv(a, conv);
   }
+  if (with_states && !mfma)
+    return fail(KDA_ERR_UNSUPPORTED, "the chunked per-token states need bf16 inputs, dk = dv = 128, chunk 0, 32 or "
+                                     "64 and T * H * 128 < 2^31; kda_recurrent_states covers other shapes");
   if (!mfma) {
     if (!kda::prefill_valu_supports(p->dk, p->dv))
       return fail(KDA_ERR_UNSUPPORTED, "no prefill kernel for dk=%d dv=%d", p->dk, p->dv);
@@ -211,11 +225,13 @@ kda_status_t prefill_impl(const kda_params_t *p, const kda_conv_t *conv, bool wi
     // more than a separate pass at full HBM bandwidth on every CU, and it needs waits
     // between work-groups.  With y alone, the head outputs are written into y and
     // normalised there, in place.
-    KDA_TRY(check_workspace(p, cu_seqlens, workspace, workspace_bytes));
+    KDA_TRY(check_workspace(p, cu_seqlens, workspace, workspace_bytes, with_states));
     KDA_TRY(hip_status(kda::launch_chunk_prep(a, workspace, st), "prefill (chunk preparation)"));
     void *out = o != nullptr ? o : y;
     a.o = out;
+    a.states_out = states;
     KDA_TRY(hip_status(kda::launch_chunk_scan(a, workspace, st), "prefill (state scan)"));
+    if (with_states) KDA_TRY(hip_status(kda::launch_chunk_states(a, workspace, st), "per-token states"));
     if (y != nullptr) {
       const int64_t rows = static_cast<int64_t>(p->B) * p->T * p->H;
       const int32_t *tok_end = cu_seqlens ? cu_seqlens + a.N : nullptr;   // tokens past it are not written
@@ -252,6 +268,21 @@ kda_status_t kda_chunk_prefill_conv(const kda_params_t *p, const kda_conv_t *con
                                     size_t workspace_bytes, void *stream) {
   return prefill_impl(p, conv, true, q, k, v, g, beta, initial_state, cu_seqlens, mask, o, final_state, gate,
                       norm_weight, y, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_prefill_states(const kda_params_t *p, const void *q, const void *k, const void *v,
+                                      const float *g, const float *beta, const float *initial_state,
+                                      const int32_t *cu_seqlens, const uint8_t *mask, void *o,
+                                      float *final_state, const void *gate, const float *norm_weight, void *y,
+                                      float *states, void *workspace, size_t workspace_bytes, void *stream) {
+  return prefill_impl(p, nullptr, false, q, k, v, g, beta, initial_state, cu_seqlens, mask, o, final_state, gate,
+                      norm_weight, y, workspace, workspace_bytes, stream, true, states);
+}
+
+size_t kda_chunk_prefill_states_workspace_size(const kda_params_t *p, int32_t packed) {
+  if (p == nullptr || check_params(p, true) != KDA_OK) return 0;
+  if (packed && p->num_seqs <= 0) return 0;
+  return prefill_states_workspace(p, packed != 0);
 }
 
 size_t kda_chunk_prefill_workspace_size(const kda_params_t *p, int32_t packed) {

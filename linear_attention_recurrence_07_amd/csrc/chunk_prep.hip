@@ -186,7 +186,7 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         if (c0 - j >= t_begin) push(c0 - j);
     }
     // the j-th newest carried input is entry W-1-j of the sequence's carried inputs
-    for (int j = 1; cnt < 3; ++j) push(xinit != nullptr && j <= W - 1 ? -1 - (W - 1 - j) : kNoInput);
+    for (int j = 1; j <= 3 && cnt < 3; ++j) push(xinit != nullptr && j <= W - 1 ? -1 - (W - 1 - j) : kNoInput);
     // this lane's window before token c0 + 8 tg: real tokens of the chunk before it, then p
     uint32_t below = vbits & ((1u << (8 * tg)) - 1u);
     auto pop_top = [&]() -> int {

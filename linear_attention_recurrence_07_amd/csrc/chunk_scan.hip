@@ -99,13 +99,16 @@ static_assert(sizeof(Hand<false>) % 16 == 0 && sizeof(Hand<true>) % 16 == 0 && (
 // NORM: also write y (gated norm over the head's 128 channels); xs holds the exchanged
 // partial sums of squares, 2 tiles x 32 tokens per (slot, head).  WRITE_O: store the head
 // outputs o (only NORM may leave them out: the caller then wants y alone).  CONV: v is
-// the raw projection; the helpers run its short convolution (cv).
-template <typename TOut, bool HAS_INIT, bool NORM, bool WRITE_O, bool CONV>
+// the raw projection; the helpers run its short convolution (cv).  STATES: for the
+// per-token states, also store each chunk's U rows (fp32 [slot, head, token, column] in
+// uws) and the state after the chunk's last position into states [.., T, H, DK, DV].
+template <typename TOut, bool HAS_INIT, bool NORM, bool WRITE_O, bool CONV, bool STATES>
 __global__ void __launch_bounds__(NT, 1)
 chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, const float *init,
                   float *fin, const int32_t *__restrict__ cu, TOut *__restrict__ o,
                   const uint16_t *__restrict__ gate, const float *__restrict__ norm_w, TOut *__restrict__ y,
-                  uint64_t *xs, uint32_t *status, float eps, int T, int H, int units, ConvIn cv) {
+                  uint64_t *xs, uint32_t *status, float eps, int T, int H, int units, ConvIn cv,
+                  float *states, float *uws) {
   constexpr int NOST = NORM ? kNormLag + 1 : 2;
   __shared__ Smem<NOST, CONV> sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -389,7 +392,7 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
   // One chunk's products.  The LDS reads of each phase are issued together ahead of their
   // first use (the empty asm statements keep them there), so their latency overlaps the
   // matrix-core work of the previous phase instead of stalling each product.
-  auto products = [&](const Hand<CONV> &hc, float *ost) {
+  auto products = [&](const Hand<CONV> &hc, float *ost, int cidx) {
     const u32x4 *KB = reinterpret_cast<const u32x4 *>(hc.rec.kb);
     const u32x4 *QT = reinterpret_cast<const u32x4 *>(hc.rec.qt);
     const u32x4 *KE = reinterpret_cast<const u32x4 *>(hc.rec.ket);
@@ -461,6 +464,24 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     for (int t = 0; t < DK / 16; ++t) {
       Sacc[t] = mfma_f16(kef[t], Ul, Sacc[t]);
       Sacc[t] = mfma_f16(kef[t], Uh, Sacc[t]);
+    }
+    if constexpr (STATES) {
+      // A wave-uniform base plus this lane's byte offset, made opaque here so that the 40
+      // store addresses are formed at the stores instead of being kept live across chunks.
+      uint32_t lo = static_cast<uint32_t>(4 * lg * DV + col0 + wcol) * 4u;
+      __asm__ volatile("" : "+v"(lo));
+      uint8_t *up = reinterpret_cast<uint8_t *>(uws + (static_cast<size_t>(slot0 + cidx) * H + h) * C * DV) + lo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<float *>(up + i * DV * 4) = U0[i];
+        *reinterpret_cast<float *>(up + (SB + i) * DV * 4) = U1[i];
+      }
+      const int pl = min(t_begin + C * cidx + C - 1, t_end - 1);
+      uint8_t *sp = reinterpret_cast<uint8_t *>(states + ((row0 + pl) * H + h) * DK * DV) + lo;
+#pragma unroll
+      for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<float *>(sp + (16 * t + i) * DV * 4) = Sacc[t][i];
     }
     // O = (q^ exp(G)) S0 + Bqk U
 #pragma unroll
@@ -596,7 +617,7 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
             if (s >= kNormLag - 2) xw = fetch(s - (kNormLag - 2), lane);
           }
         }
-        products(sm.hand[s & 1], sm.ost[oi]);
+        products(sm.hand[s & 1], sm.ost[oi], s);
         oi = (oi + 1 == NOST) ? 0 : oi + 1;
         sync_lds();
       }
@@ -616,19 +637,30 @@ hipError_t launch3(const Args &a, const void *ws, uint64_t *xs, uint32_t *status
   static_assert(WRITE_O || NORM, "without the norm the head outputs are the only output");
   const int units = a.N * a.H;
   const unsigned grid = static_cast<unsigned>((units + 7) / 8) * 8 * NTILE;
-  auto go = [&](auto conv_t) {
-    hipLaunchKernelGGL((chunk_scan_kernel<TOut, HAS_INIT, NORM, WRITE_O, decltype(conv_t)::value>), dim3(grid),
-                       dim3(NT), 0, st, static_cast<const uint16_t *>(a.v), static_cast<const Rec *>(ws), a.init,
-                       a.state, a.cu, static_cast<TOut *>(a.o), static_cast<const uint16_t *>(a.gate), a.norm_w,
-                       static_cast<TOut *>(a.y), xs, status, a.eps, a.T, a.H, units, a.conv);
+  float *uws = nullptr;
+  auto go = [&](auto conv_t, auto states_t) {
+    hipLaunchKernelGGL((chunk_scan_kernel<TOut, HAS_INIT, NORM, WRITE_O, decltype(conv_t)::value,
+                                          decltype(states_t)::value>),
+                       dim3(grid), dim3(NT), 0, st, static_cast<const uint16_t *>(a.v), static_cast<const Rec *>(ws),
+                       a.init, a.state, a.cu, static_cast<TOut *>(a.o), static_cast<const uint16_t *>(a.gate),
+                       a.norm_w, static_cast<TOut *>(a.y), xs, status, a.eps, a.T, a.H, units, a.conv, a.states_out,
+                       uws);
   };
-  if (a.conv.W > 0) go(std::true_type{});
-  else go(std::false_type{});
+  if constexpr (!NORM && WRITE_O) {
+    if (a.states_out) {
+      uws = chunk_states_u_area(ws, a.B, a.T, a.H, a.N, a.cu != nullptr);
+      go(std::false_type{}, std::true_type{});
+      return hipGetLastError();
+    }
+  }
+  if (a.conv.W > 0) go(std::true_type{}, std::false_type{});
+  else go(std::false_type{}, std::false_type{});
   return hipGetLastError();
 }
 
 template <typename TOut, bool HAS_INIT>
 hipError_t launch2(const Args &a, const void *ws, uint64_t *xs, uint32_t *status, hipStream_t st) {
+  if (a.states_out) return launch3<TOut, HAS_INIT, false, true>(a, ws, xs, status, st);
   if (!a.y) return launch3<TOut, HAS_INIT, false, true>(a, ws, xs, status, st);
   return a.o ? launch3<TOut, HAS_INIT, true, true>(a, ws, xs, status, st)
              : launch3<TOut, HAS_INIT, true, false>(a, ws, xs, status, st);

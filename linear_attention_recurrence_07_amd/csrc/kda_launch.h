@@ -75,8 +75,15 @@ size_t chunk_prep_workspace_bytes(long long B, long long T, long long H, long lo
 uint64_t *chunk_exchange_words(const void *ws, long long B, long long T, long long H, long long N, bool packed);
 uint32_t *chunk_status_word(const void *ws, long long B, long long T, long long H, long long N, bool packed);
 hipError_t launch_chunk_prep(const Args &a, void *ws, hipStream_t s);
-// With a.y set the scan also applies the gated norm (a.gate, a.norm_w, a.eps).
+// With a.y set the scan also applies the gated norm (a.gate, a.norm_w, a.eps).  With
+// a.states_out set (and no a.y, no convolution) it also stores each chunk's U rows in the
+// workspace area after the prefill's own (chunk_states_u_area) and the state after each
+// chunk's last position into a.states_out; launch_chunk_states then fills the others.
 hipError_t launch_chunk_scan(const Args &a, const void *ws, hipStream_t s);
+// The per-token states' workspace area: fp32 U rows, 32 x 128 per (slot, head).
+size_t chunk_states_u_bytes(long long B, long long T, long long H, long long N, bool packed);
+float *chunk_states_u_area(const void *ws, long long B, long long T, long long H, long long N, bool packed);
+hipError_t launch_chunk_states(const Args &a, const void *ws, hipStream_t s);
 // With tok_end (a device pointer to the end of the last packed sequence), rows of tokens
 // at or past it (row / heads >= *tok_end) are left untouched.
 hipError_t launch_gated_rmsnorm(const void *x, const void *gate, const float *w, void *y,

@@ -229,9 +229,10 @@ recurrent_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn
   // window advances when `live`.
   auto filt = [&](int x, int e, float xr, bool live) -> float {
     const float4 tap = (x == 0 ? s_tq : (x == 1 ? s_tk : s_tv))[e];
+    constexpr int J1 = CONV ? 1 : 0, J2 = CONV ? 2 : 0;   // (the windows exist only with CONV)
     TIn *w0 = x == 0 ? s_wq[0] : (x == 1 ? s_wk[0] : s_wv[0]);
-    TIn *w1 = x == 0 ? s_wq[1] : (x == 1 ? s_wk[1] : s_wv[1]);
-    TIn *w2 = x == 0 ? s_wq[2] : (x == 1 ? s_wk[2] : s_wv[2]);
+    TIn *w1 = x == 0 ? s_wq[J1] : (x == 1 ? s_wk[J1] : s_wv[J1]);
+    TIn *w2 = x == 0 ? s_wq[J2] : (x == 1 ? s_wk[J2] : s_wv[J2]);
     const TIn r0 = w0[e], r1 = w1[e], r2 = w2[e];
     float z = conv_z4(tap, f32_of(r0), f32_of(r1), f32_of(r2), xr);
     if (cv.silu) z = silu_act(z);

@@ -130,6 +130,39 @@ def test_prefill_workspace_size_and_checks():
     assert lib.kda_status_string(WS) == b"KDA_ERR_WORKSPACE"
 
 
+def test_chunk_states_workspace_size_and_checks():
+    """kda_chunk_prefill_states: the prefill's workspace plus 32 x 128 fp32 U rows per
+    chunk and head; host validation before anything is launched."""
+    lib = K.load_library()
+    size = lambda p, packed=0: lib.kda_chunk_prefill_states_workspace_size(ctypes.byref(p), packed)
+    per = 32272 + 512 + 32 * 128 * 4
+    assert size(_p(B=1, T=64, H=2)) == 1 * 2 * 2 * per + 256
+    assert size(_p(B=3, T=65, H=2)) == 3 * 3 * 2 * per + 256
+    assert size(_p(B=1, T=64, H=2, num_seqs=3), 1) == (3 + 2) * 2 * per + 256
+    assert size(_p(B=1, T=64, H=2), 1) == 0
+    assert size(_p(chunk=16)) == 0 and size(_p(dk=64, dv=64)) == 0 and size(_p(in_dtype=0)) == 0
+    assert lib.kda_chunk_prefill_states_workspace_size(None, 0) == 0
+    need = size(_p())
+
+    def call(p, ws=None, nbytes=0, **ptrs):
+        names = ["q", "k", "v", "g", "beta", "init", "cu", "mask", "o", "fs", "gate", "w", "y", "states"]
+        d = dict(q=A, k=A, v=A, g=A, beta=A, init=None, cu=None, mask=None, o=A, fs=A, gate=None, w=None, y=None,
+                 states=A)
+        d.update(ptrs)
+        return lib.kda_chunk_prefill_states(ctypes.byref(p), *[d[n] for n in names], ws, nbytes, None)
+
+    assert call(_p()) == WS                                          # a valid call stops at the missing workspace
+    assert call(_p(), ws=A, nbytes=need - 1) == WS
+    assert call(_p(), ws=A, nbytes=lib.kda_chunk_prefill_workspace_size(ctypes.byref(_p()), 0)) == WS
+    assert call(_p(), states=None) == 1
+    assert call(_p(), states=MIS) == 4
+    assert call(_p(), o=None, gate=A, w=A, y=A) == 1                 # o is required here
+    assert call(_p(dk=64, dv=64)) == UNSUP                          # only the matrix-core prefill
+    assert call(_p(in_dtype=0)) == UNSUP
+    assert call(_p(chunk=16)) == UNSUP
+    assert call(_p(), q=None) == 1
+
+
 def test_stage_validation_codes():
     lib = K.load_library()
     need = lib.kda_chunk_prefill_workspace_size(ctypes.byref(_p()), 0)
