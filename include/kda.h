@@ -254,7 +254,9 @@ kda_status_t kda_recurrent_states(const kda_params_t *p,
  * (nnterp Kimi-Linear page, Notes, "Loading": the prompt kernel carries the state from
  * chunk to chunk).  The scan stores U of every chunk in the workspace and the state after
  * each chunk's last position into `states`; one more launch writes every other position
- * from the state before its chunk, 16 KB per store stream, independent across chunks.
+ * from the state before its chunk (one work-group per chunk and head, independent of the
+ * other chunks), so the call runs at the HBM write rate rather than at the token-by-token
+ * kernel's per-token latency.
  *   states [B, T, H, dk, dv] fp32, 16-byte aligned: states[b, t, h] is S after token t
  *          (a padding token repeats the carried state; tokens of a packed batch at or past
  *          cu_seqlens[N] are not written).  64 KB per token and head.
