@@ -17,10 +17,10 @@
 //     128 x 16 slice of the fp32 state in registers for the whole sequence.  Each chunk's
 //     products run on MFMA with the record's operands read from LDS in fragment order
 //     (16-byte reads, no bank conflicts).
-//   helper waves 4-7: stage the record and value tile of chunk c+1 (loaded two steps
-//     earlier into registers) into the other half of a double-buffered LDS hand-over
-//     area, issue the loads of chunk c+3, and write chunk c-1's output rows from a ring
-//     of output tiles, while the compute waves work on chunk c.
+//   helper waves 4-7: stage the record and value tile of chunk c+1 (loaded two or three
+//     steps earlier into registers) into the other half of a double-buffered LDS
+//     hand-over area, issue the loads of chunk c+3 (or c+4), and write chunk c-1's output
+//     rows from a ring of output tiles, while the compute waves work on chunk c.
 // One work-group barrier per step.  The two tiles of a head get work-group ids 8 apart,
 // so they land on the same XCD and share its L2 for the record reads.
 //
@@ -498,8 +498,8 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     to_f16();                                    // S0 of the next chunk
   };
 
-  // Step s: helpers stage chunk s+1 (loaded at step s-2), load chunk s+3 into the freed
-  // register set and write chunk s-1's rows; compute waves run chunk s.  Chunks past the
+  // Step s: helpers stage chunk s+1 (loaded at step s-AHEAD+1), load chunk s+1+AHEAD into
+  // the freed register set and write chunk s-1's rows; compute waves run chunk s.  Chunks past the
   // end repeat the last.  The two sides run separate loops with one work-group barrier
   // per step each (nchunks + 1 in all), so their loop-carried registers never overlap.
   // CONV: the value loads run one chunk ahead of the record loads; step s also filters
@@ -508,9 +508,17 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
   // the loops puts chunk 0's raw rows in place.
   if (nchunks > 0) {
     if (helper) {
-      Pre pre0, pre1;                            // two sets: loads run two steps ahead
+      // Register sets of loaded chunks: two (loads run two steps ahead), or three without the
+      // convolution and the in-scan norm.  The helpers' streaming of records and values
+      // bounds the scan (alone it takes 270 us at T = 8192 against 225 us for the compute
+      // waves alone); three steps ahead took the scan from 321 to 302-305 us (median), four
+      // gained nothing more.
+      constexpr bool DEEP = !CONV && !NORM;
+      constexpr int AHEAD = DEEP ? 3 : 2;
+      Pre pre0, pre1, pre2;
       load(pre0, 0);
       load(pre1, min(1, last));
+      if constexpr (DEEP) load(pre2, min(2, last));
       if constexpr (CONV) {
         const uint32_t tv = static_cast<uint32_t>(min(t_begin + hr, t_end - 1));
         put_raw(0, *reinterpret_cast<const u32x4 *>(vrow + (piece + tv * tok_bytes)));
@@ -530,7 +538,7 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
         put_raw(1, pre0.v);                      // chunk 1's raw rows
       }
       stage(sm.hand[0], pre0);
-      load(pre0, min(2, last));
+      load(pre0, min(AHEAD, last));
       // NORM: the gate pieces and flags of chunk s-5 in the set of step s's parity
       // (loaded at step s-2); at the start of step s, this tile's sums of squares of
       // chunks s-5 .. s-2
@@ -553,7 +561,7 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
           put_raw(s & 1, fv);                    // chunk s+2's raw rows
         } else {
           stage(sm.hand[(s + 1) & 1], from);
-          load(from, min(s + 3, last));
+          load(from, min(s + 1 + AHEAD, last));
         }
         float ss = 0.f;
         if (s >= 1) {
@@ -573,11 +581,21 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
         sync_lds();
       };
       int s = 0;
-      for (; s + 1 < nchunks; s += 2) {
-        hstep(s, pre1, gA, fA);                  // chunk s+1 is in pre1, s+2 in pre0
-        hstep(s + 1, pre0, gB, fB);
+      if constexpr (DEEP) {
+        for (; s + 2 < nchunks; s += 3) {
+          hstep(s, pre1, gA, fA);                // chunk s+1 is in pre1, s+2 in pre2, s+3 in pre0
+          hstep(s + 1, pre2, gA, fA);
+          hstep(s + 2, pre0, gA, fA);
+        }
+        if (s < nchunks) hstep(s, pre1, gA, fA);
+        if (s + 1 < nchunks) hstep(s + 1, pre2, gA, fA);
+      } else {
+        for (; s + 1 < nchunks; s += 2) {
+          hstep(s, pre1, gA, fA);                // chunk s+1 is in pre1, s+2 in pre0
+          hstep(s + 1, pre0, gB, fB);
+        }
+        if (s < nchunks) hstep(s, pre1, gA, fA);
       }
-      if (s < nchunks) hstep(s, pre1, gA, fA);
       const float ssl = emit(last, sm.ost[last % NOST]);
       if constexpr (NORM) {
         // y of chunks last-4 .. last.  The partner's sums of chunk last-4 are in LDS
