@@ -15,14 +15,18 @@
 //
 // Work-group: NT threads own an RB x 128 band of the state (F4 float4 each, rows
 // tid / 32 + RPS i, columns 4 (tid % 32) ..), so each token's band is one contiguous
-// store of RB x 512 bytes.  The whole state per work-group (RB = 128, 512 threads, 768
-// work-groups at T = 256 and 96 heads, all resident at once) measured 318 us for the call
-// against 339 us with 32-row bands and 256 threads (3,072 work-groups); 64-row bands and
-// 16-row bands were slower still, ordinary stores slower than non-temporal ones, and
-// splitting a chunk's positions over several work-groups (each replaying the earlier
-// updates) slower too.  Before the token loop the band's decays exp(g), the normalised keys (the L2
-// norm over all 128 channels, as the preparation forms it) and the chunk's U rows are
-// staged in LDS; a padding token gets decay 1 and key 0 (its state is the carried one).
+// store of RB x 512 bytes.  Before the token loop the band's decays exp(g), the
+// normalised keys (the L2 norm over all 128 channels, as the preparation forms it) and the
+// chunk's U rows are staged in LDS; a padding token gets decay 1 and key 0 (its state is
+// the carried one).
+//
+// Measured at T = 256 and 96 heads (the whole call): the whole state per work-group
+// (RB = 128, 512 threads, 768 work-groups, all resident at once) 318 us; 32-row bands
+// with 256 threads (3,072 work-groups) 339 us; 64- and 16-row bands slower; ordinary
+// stores instead of non-temporal ones slower; splitting a chunk's positions over several
+// work-groups that replay the earlier updates 329-386 us; one work-group per (sequence,
+// head, 16-row band) walking every chunk in order, so that the stores sweep the tensor
+// from start to end, 354 us.
 #include "kda_chunk.h"
 #include "kda_launch.h"
 
