@@ -510,9 +510,9 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     if (helper) {
       // Register sets of loaded chunks: two (loads run two steps ahead), or three without the
       // convolution and the in-scan norm.  The helpers' streaming of records and values
-      // bounds the scan (alone it takes 270 us at T = 8192 against 225 us for the compute
-      // waves alone); three steps ahead took the scan from 321 to 302-305 us (median), four
-      // gained nothing more.
+      // bounds the scan (alone it takes 262-270 us at T = 8192 against about 225 us for the
+      // compute waves alone), but mostly by the paired reads of each record, not by the
+      // bytes in flight: three steps ahead gives at most a few per cent, four nothing more.
       constexpr bool DEEP = !CONV && !NORM;
       constexpr int AHEAD = DEEP ? 3 : 2;
       Pre pre0, pre1, pre2;
