@@ -237,7 +237,10 @@ chunk_scan_kernel(const uint16_t *__restrict__ v, const Rec *__restrict__ ws, co
     for (int i = 0; i < 8; ++i) {
       const int w = i >> 1;
       auto el = [&](u32x4 x) { return (i & 1) ? hi_bf16(x[w]) : lo_bf16(x[w]); };
-      z[i] = conv_z(ctap[i], el(cr.r0), el(cr.r1), el(cr.r2), el(cr.x), cv.W);
+      // all four taps (a narrower filter's older taps are zero; its window rows are real
+      // inputs, carried inputs or zeros, so finite): no per-element selects on the width
+      z[i] = conv_z4(make_float4(ctap[i][0], ctap[i][1], ctap[i][2], ctap[i][3]), el(cr.r0), el(cr.r1), el(cr.r2),
+                     el(cr.x));
       if (cv.silu) z[i] = silu_act(z[i]);
     }
     const bool keep = (valid >> hr) & 1u;
