@@ -245,7 +245,9 @@ chunk_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
         unpack(rows[i], x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          z[e] = conv_z(tap[e], h0[e], h1[e], h2[e], x[e], W);
+          // all four taps (a narrower filter's older taps are zero and its window rows
+          // finite): no per-element selects on the width
+          z[e] = conv_z4(make_float4(tap[e][0], tap[e][1], tap[e][2], tap[e][3]), h0[e], h1[e], h2[e], x[e]);
           if (cv.silu) z[e] = silu_act(z[e]);
           z[e] = ok ? z[e] : 0.f;
           h0[e] = ok ? h1[e] : h0[e];
