@@ -137,7 +137,9 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __ex
 // taps are right-aligned: tap[3] is the filter's last weight (the one that meets x) and
 // tap[4-W .. 2] its first W-1, oldest first; window entries older than W-1 inputs are not
 // read.  Every kernel that filters goes through these two functions in the same order of
-// operations, so the separate and the fused convolutions give the same bits.
+// operations: at W = 4 they are the same operations, so the separate and the fused
+// convolutions give the same bits; the fused kernels use conv_z4 for every width, and for
+// a narrower filter its extra zero-tap products can only change the sign of a zero.
 __device__ __forceinline__ float conv_z(const float (&tap)[4], float h0, float h1, float h2, float x, int W) {
   float z = tap[3] * x;
   if (W >= 4) z = __builtin_fmaf(tap[0], h0, z);
