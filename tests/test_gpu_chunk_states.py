@@ -92,7 +92,8 @@ def _check(x, states, o, fs, *, use_l2=True, scale=None, heads=None):
             assert torch.equal(states[b, t], fs[n]), f"state at the last token of sequence {n} != final_state"
 
 
-@pytest.mark.parametrize("case", ["plain", "masked", "packed", "per_head_chunk64", "one_chunk", "short"])
+@pytest.mark.parametrize("case", ["plain", "masked", "packed", "per_head_chunk64", "one_chunk", "short",
+                                  "padded_chunk", "packed_chunk64_per_head"])
 def test_chunk_states(case):
     if case == "plain":
         x = gi.make_inputs("cs_plain", B=2, T=100, H=3, dk=128, dv=128, seed=71, initial_state_std=0.05)
@@ -118,9 +119,23 @@ def test_chunk_states(case):
     elif case == "one_chunk":
         x = gi.make_inputs("cs_one", B=3, T=32, H=2, dk=128, dv=128, seed=75)
         chunk = 0
-    else:
+    elif case == "short":
         x = gi.make_inputs("cs_short", B=2, T=2, H=2, dk=128, dv=128, seed=76, initial_state_std=0.05)
         chunk = 0
+    elif case == "padded_chunk":
+        # a whole chunk of padding in row 1 (its positions repeat the carried state) and
+        # a ragged, padded tail in row 0
+        m = np.ones((2, 80), np.uint8)
+        m[1, 32:64] = 0
+        m[0, 70:] = 0
+        x = gi.make_inputs("cs_padchunk", B=2, T=80, H=2, dk=128, dv=128, seed=80, initial_state_std=0.05, mask=m)
+        chunk = 0
+    else:
+        lens = [70, 5, 64, 31]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        x = gi.make_inputs("cs_packed64", B=1, T=int(cu[-1]), H=2, dk=128, dv=128, seed=81,
+                           initial_state_std=0.05, cu_seqlens=cu, decay_per_head=True)
+        chunk = 64
     states, o, fs = _run(x, chunk=chunk)
     _check(x, states, o, fs)
 
