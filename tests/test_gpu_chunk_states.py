@@ -196,3 +196,21 @@ def test_chunk_states_zero_tokens():
     torch.cuda.synchronize()
     assert torch.equal(fs, init)
     assert torch.all(buf == 3.0)
+
+
+def test_chunk_states_with_gated_norm_and_bf16_outputs():
+    """bf16 o and the gated norm's y through kda_chunk_prefill_states: o, y and the final
+    state bit-identical to kda_chunk_prefill's, the states against the oracle."""
+    import linear_attention_recurrence_07_amd as kda
+    x = gi.make_inputs("cs_norm", B=2, T=67, H=2, dk=128, dv=128, seed=82, initial_state_std=0.05, norm=True)
+    d = U.device_inputs(x, DEV)
+    states = torch.full((x.B, x.T, x.H, x.dk, x.dv), SENTINEL, device=DEV)
+    kw = dict(gate=d["gate"], norm_weight=d["norm_weight"], norm_eps=x.norm_eps, output_dtype=torch.bfloat16)
+    U.log("chunk states with the gated norm, bf16 outputs")
+    o, fs, y = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], states=states, **kw)
+    o2, fs2, y2 = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], **kw)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16 and y.dtype == torch.bfloat16
+    assert torch.equal(o, o2) and torch.equal(y, y2) and torch.equal(fs, fs2)
+    _, _, rst = _oracle_states(x)
+    U.assert_close("chunk states cs_norm", U.to_numpy64(states), rst, U.BF16_TOL)
